@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs for attention, shared by the tests, smoke() and bench.py.
+
+This module holds no attention arithmetic: it only draws i.i.d. N(0, 1) tensors
+from seeded CPU generators, rounds them to the working dtype, and names the
+workloads.  Both the HIP path and the CPU oracle consume what it returns (the
+oracle upcasts the same rounded values to float64).
+
+Seeds: tensor t of workload k uses seed 1000*k + t with t = 0 (Q), 1 (K), 2 (V),
+3 (dO).  Point p of the throughput sweep uses 5000 + 10*p + t.  The GQA workload
+additionally scales ceil(1%) of all key rows by 8 (exact in bf16), rows picked by
+a seed-4100 permutation over the flattened (batch, kv-head, position) rows, before
+the dtype cast: those rows produce scores far above the rest and move the running
+max late in the key loop.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import torch
+
+DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str
+    B: int
+    H: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    backward: bool
+    seed_base: int
+    k_outlier_frac: float = 0.0
+    k_outlier_scale: float = 8.0
+    k_outlier_seed: int = 0
+    notes: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def shape_q(self):
+        return (self.B, self.H, self.N, self.d)
+
+    @property
+    def shape_kv(self):
+        return (self.B, self.Hkv, self.N, self.d)
+
+    def fwd_flop(self) -> float:
+        """4*B*H*N^2*d for the two forward matmuls, halved under a causal mask."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def bwd_flop(self) -> float:
+        """Five N^2*d matmuls (S recompute, dV, dP, dK, dQ): 2.5x the forward."""
+        return 2.5 * self.fwd_flop()
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "dtype": self.dtype, "B": self.B, "H": self.H,
+                "Hkv": self.Hkv, "N": self.N, "d": self.d, "causal": self.causal}
+
+
+SWEEP_N = (1024, 2048, 4096, 8192, 16384)
+SWEEP_D = (64, 128)
+
+
+def sweep_points():
+    """Throughput sweep points, ordered by N ascending then d ascending."""
+    pts = []
+    for n in SWEEP_N:
+        for d in SWEEP_D:
+            p = len(pts)
+            pts.append(Workload(f"sweep_bf16_B4_H16_N{n}_d{d}", "bf16", 4, 16, 16, n, d,
+                                False, True, 5000 + 10 * p))
+    return pts
+
+
+WORKLOADS = {
+    "fp32_single_head": Workload("fp32_single_head_B1_H1_N256_d64", "fp32", 1, 1, 1, 256, 64,
+                                 False, True, 1000),
+    "bf16_fwd": Workload("bf16_fwd_B4_H16_N2048_d128", "bf16", 4, 16, 16, 2048, 128,
+                         False, False, 2000),
+    "fp16_causal": Workload("fp16_causal_B2_H32_N8192_d64", "fp16", 2, 32, 32, 8192, 64,
+                            True, True, 3000),
+    "bf16_gqa_causal": Workload("bf16_gqa_causal_B1_H32_Hkv8_N16384_d128", "bf16", 1, 32, 8,
+                                16384, 128, True, True, 4000, k_outlier_frac=0.01,
+                                k_outlier_seed=4100),
+}
+for _w in sweep_points():
+    WORKLOADS[_w.name] = _w
+
+# The throughput headline: bf16, non-causal, B*H = 64, N = 8192, d = 128.
+HEADLINE = WORKLOADS["sweep_bf16_B4_H16_N8192_d128"]
+
+
+def randn(shape, seed: int) -> torch.Tensor:
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32)
+
+
+def make_inputs(w: Workload, with_grad: bool | None = None) -> dict:
+    """CPU tensors q, k, v (and do) in the workload's dtype, contiguous."""
+    dt = DTYPES[w.dtype]
+    q = randn(w.shape_q, w.seed_base + 0)
+    k = randn(w.shape_kv, w.seed_base + 1)
+    v = randn(w.shape_kv, w.seed_base + 2)
+    if w.k_outlier_frac > 0:
+        rows = w.B * w.Hkv * w.N
+        n_sel = math.ceil(w.k_outlier_frac * rows)
+        g = torch.Generator(device="cpu").manual_seed(w.k_outlier_seed)
+        sel = torch.randperm(rows, generator=g)[:n_sel]
+        k = k.reshape(rows, w.d)
+        k[sel] *= w.k_outlier_scale
+        k = k.reshape(w.shape_kv)
+    out = {"q": q.to(dt).contiguous(), "k": k.to(dt).contiguous(), "v": v.to(dt).contiguous()}
+    if with_grad if with_grad is not None else w.backward:
+        out["do"] = randn(w.shape_q, w.seed_base + 3).to(dt).contiguous()
+    return out
+
+
+def custom(dtype: str, B: int, H: int, Hkv: int, N: int, d: int, causal: bool,
+           seed_base: int, **kw) -> Workload:
+    """A small ad-hoc workload (edge cases in tests)."""
+    return Workload(f"case_{dtype}_B{B}_H{H}_Hkv{Hkv}_N{N}_d{d}_{'c' if causal else 'nc'}",
+                    dtype, B, H, Hkv, N, d, causal, True, seed_base, **kw)
+
+
+def with_dtype(w: Workload, dtype: str) -> Workload:
+    return replace(w, dtype=dtype, name=w.name + "_as_" + dtype)

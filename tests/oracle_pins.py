@@ -1,0 +1,322 @@
+"""Pins for the fp64 oracle: each returns an error figure, tests compare it to a bound.
+
+Kept as plain functions so that ``test_oracle_mutations.py`` can re-run them on an
+oracle with a planted mistake and show that at least one pin catches it.  None of
+these retypes the oracle's formulas: each checks the oracle against something
+else the pages or the mathematics fix (printed values, closed forms, invariants,
+finite differences, brute-force loops, a library routine).
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle.attention as A
+import oracle.brute as BR
+import oracle.online_walk as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fa2_worked_example.json")
+
+
+def rng_case(seed, B=1, H=2, Hkv=1, N=7, d=4, scale=None):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((B, H, N, d))
+    k = r.standard_normal((B, Hkv, N, d))
+    v = r.standard_normal((B, Hkv, N, d))
+    do = r.standard_normal((B, H, N, d))
+    return q, k, v, do, (1.0 / math.sqrt(d) if scale is None else scale)
+
+
+def closed_form(terms):
+    return sum(c * math.exp(e) for c, e in terms)
+
+
+def load_golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def worked_example_arrays(g):
+    q = np.array(g["Q"], dtype=np.float64)
+    k = np.array(g["K_T"], dtype=np.float64).T.copy()
+    v = np.array(g["V"], dtype=np.float64)
+    return q, k, v
+
+
+# --- p1: the worked example -------------------------------------------------------
+
+def pin_worked_example_walk():
+    """Max error of the tiled walk's (m, l, Ot) after each step vs the page's closed forms."""
+    g = load_golden()
+    q, k, v = worked_example_arrays(g)
+    _, _, steps = W.tiled_forward(q, k, v, g["block_rows"], g["block_cols"], g["scale"],
+                                  trace=True)
+    err = 0.0
+    for st in g["steps"]:
+        got = steps[st["j"] - 1]          # query tile 1 is i = 0, key tile j is index j-1
+        assert got["i"] == 0
+        err = max(err, np.max(np.abs(got["m"] - np.array(st["m"], dtype=float))))
+        err = max(err, max(abs(got["l"][r] - closed_form(st["l"][r])) for r in range(2)))
+        for r in range(2):
+            for c in range(2):
+                err = max(err, abs(got["Ot"][r, c] - closed_form(st["Ot"][r][c])))
+    return err
+
+
+def pin_worked_example_scores():
+    """S_1j = Q_1 K_j^T from the oracle's score function vs the page's printed tiles."""
+    g = load_golden()
+    q, k, v = worked_example_arrays(g)
+    s = A.scores(q[:2], k, g["scale"], False)
+    err = 0.0
+    for st in g["steps"]:
+        j = st["j"] - 1
+        err = max(err, np.max(np.abs(s[:, 2 * j:2 * j + 2] - np.array(st["S"], dtype=float))))
+    return err
+
+
+def pin_worked_example_naive():
+    """The plain-definition oracle's O, LSE of rows 1-2 vs Ot/l and m + ln l of the last step."""
+    g = load_golden()
+    q, k, v = worked_example_arrays(g)
+    o, lse = A.attention_forward(q[None, None], k[None, None], v[None, None], g["scale"])
+    last = g["steps"][-1]
+    err = 0.0
+    for r in range(2):
+        l = closed_form(last["l"][r])
+        err = max(err, abs(lse[0, 0, r] - (last["m"][r] + math.log(l))))
+        for c in range(2):
+            err = max(err, abs(o[0, 0, r, c] - closed_form(last["Ot"][r][c]) / l))
+    return err
+
+
+def pin_tiled_equals_naive(seed=0, N=13, d=5, br=4, bc=3, causal=False):
+    q, k, v, _, scale = rng_case(seed, 1, 1, 1, N, d)
+    o_t, lse_t = W.tiled_forward(q[0, 0], k[0, 0], v[0, 0], br, bc, scale, causal)
+    o_n, lse_n = A.attention_forward(q, k, v, scale, causal)
+    return max(np.max(np.abs(o_t - o_n[0, 0])), np.max(np.abs(lse_t - lse_n[0, 0])))
+
+
+# --- p2..p9: invariants and closed forms ------------------------------------------
+
+def pin_rows_sum_to_one(seed=1, causal=True):
+    q, k, _, _, scale = rng_case(seed, 1, 1, 1, 9, 3)
+    p = A.softmax_rows(A.scores(q[0, 0], k[0, 0], scale, causal))
+    return np.max(np.abs(p.sum(axis=1) - 1.0))
+
+
+def pin_shift_invariance(seed=2, causal=False):
+    """Adding u to every key row shifts each score row by scale*q_i.u: O and all
+    gradients are unchanged and LSE_i moves by exactly scale*q_i.u."""
+    q, k, v, do, scale = rng_case(seed, 1, 2, 1, 8, 4)
+    u = np.random.default_rng(seed + 100).standard_normal(4) * 3.0
+    a = A.attention_backward(q, k, v, do, scale, causal)
+    b = A.attention_backward(q, k + u, v, do, scale, causal)
+    err = 0.0
+    for name in ("o", "dq", "dk", "dv"):
+        err = max(err, np.max(np.abs(a[name] - b[name])))
+    shift = scale * np.einsum("bhnd,d->bhn", q, u)
+    err = max(err, np.max(np.abs(b["lse"] - a["lse"] - shift)))
+    return err
+
+
+def pin_softmax_jvp(seed=3, n=6):
+    """s*(g - <s,g>) equals the full Jacobian product with J = diag(s) - s s^T; J is
+    symmetric; each result row sums to zero."""
+    r = np.random.default_rng(seed)
+    z = r.standard_normal((4, n)) * 2
+    gr = r.standard_normal((4, n))
+    s = A.softmax_rows(z)
+    got = A.softmax_backward_rows(s, gr)
+    err = 0.0
+    for i in range(4):
+        jac = np.diag(s[i]) - np.outer(s[i], s[i])
+        err = max(err, np.max(np.abs(jac - jac.T)))
+        err = max(err, np.max(np.abs(jac @ gr[i] - got[i])))
+    err = max(err, np.max(np.abs(got.sum(axis=1))))
+    return err
+
+
+def pin_softmax_jvp_fd(seed=4, n=7, h=1e-6):
+    """The softmax JVP against central differences of <g, softmax(z)> in z."""
+    r = np.random.default_rng(seed)
+    z = r.standard_normal(n)
+    gr = r.standard_normal(n)
+    got = A.softmax_backward_rows(A.softmax_rows(z[None])[0], gr)
+    fd = np.empty(n)
+    for j in range(n):
+        zp, zm = z.copy(), z.copy()
+        zp[j] += h
+        zm[j] -= h
+        fd[j] = (gr @ A.softmax_rows(zp[None])[0] - gr @ A.softmax_rows(zm[None])[0]) / (2 * h)
+    return np.max(np.abs(fd - got))
+
+
+def pin_d_identity(seed=5, causal=True):
+    """rowsum(dO * O) equals rowsum(P * dP), the row dot of the softmax JVP."""
+    q, k, v, do, scale = rng_case(seed, 2, 2, 2, 10, 4)
+    out = A.attention_backward(q, k, v, do, scale, causal)
+    return np.max(np.abs(np.sum(do * out["o"], axis=-1) - out["D"]))
+
+
+def pin_equal_value_rows(seed=6, causal=False):
+    """All value rows equal to one vector w: O is w for every row and dQ = dK = 0."""
+    q, k, _, do, scale = rng_case(seed, 1, 2, 1, 9, 4)
+    w = np.array([0.5, -1.25, 2.0, 3.0])
+    v = np.broadcast_to(w, k.shape).copy()
+    out = A.attention_backward(q, k, v, do, scale, causal)
+    return max(np.max(np.abs(out["o"] - w)), np.max(np.abs(out["dq"])),
+               np.max(np.abs(out["dk"])))
+
+
+def pin_zero_query(seed=7, causal=False):
+    """Q = 0: every score is 0, P is uniform over the visible keys, O is the mean
+    (causal: prefix mean) of V and LSE is ln(number of visible keys)."""
+    _, k, v, _, scale = rng_case(seed, 1, 1, 1, 8, 3)
+    q = np.zeros((1, 1, 8, 3))
+    o, lse = A.attention_forward(q, k, v, scale, causal)
+    n = np.arange(1, 9) if causal else np.full(8, 8)
+    if causal:
+        mean = np.cumsum(v[0, 0], axis=0) / n[:, None]
+    else:
+        mean = np.broadcast_to(v[0, 0].mean(axis=0), (8, 3))
+    return max(np.max(np.abs(o[0, 0] - mean)), np.max(np.abs(lse[0, 0] - np.log(n))))
+
+
+def pin_causal_row0_and_single_key(seed=8):
+    """Causal row 0 sees only key 0: O_0 = v_0, LSE_0 = scale q_0.k_0.  N = 1 likewise."""
+    q, k, v, _, scale = rng_case(seed, 1, 1, 1, 6, 4)
+    o, lse = A.attention_forward(q, k, v, scale, True)
+    err = max(np.max(np.abs(o[0, 0, 0] - v[0, 0, 0])),
+              abs(lse[0, 0, 0] - scale * q[0, 0, 0] @ k[0, 0, 0]))
+    o1, lse1 = A.attention_forward(q[:, :, :1], k[:, :, :1], v[:, :, :1], scale, False)
+    err = max(err, np.max(np.abs(o1[0, 0, 0] - v[0, 0, 0])),
+              abs(lse1[0, 0, 0] - scale * q[0, 0, 0] @ k[0, 0, 0]))
+    return err
+
+
+def pin_gqa_is_repeated_mha(seed=9, causal=True):
+    """GQA equals MHA on K, V repeated n_rep times per head; dK, dV are the group sums."""
+    q, k, v, do, scale = rng_case(seed, 2, 6, 2, 7, 3)
+    n_rep = 3
+    kr = np.repeat(k, n_rep, axis=1)
+    vr = np.repeat(v, n_rep, axis=1)
+    g = A.attention_backward(q, k, v, do, scale, causal)
+    m = A.attention_backward(q, kr, vr, do, scale, causal)
+    err = max(np.max(np.abs(g[n] - m[n])) for n in ("o", "lse", "dq"))
+    for name in ("dk", "dv"):
+        summed = m[name].reshape(2, 2, n_rep, 7, 3).sum(axis=2)
+        err = max(err, np.max(np.abs(g[name] - summed)))
+    return err
+
+
+# --- p7, p10, p11: independent computations --------------------------------------
+
+def pin_finite_differences(seed=10, N=12, d=5, causal=False, gqa=False, h=1e-6):
+    """dQ, dK, dV vs central differences of L = sum(dO * O) (relative to max |grad|)."""
+    H, Hkv = (4, 2) if gqa else (2, 2)
+    q, k, v, do, scale = rng_case(seed, 1, H, Hkv, N, d)
+    out = A.attention_backward(q, k, v, do, scale, causal)
+
+    def loss(qq, kk, vv):
+        o, _ = A.attention_forward(qq, kk, vv, scale, causal)
+        return float(np.sum(do * o))
+
+    worst = 0.0
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        fd = np.empty_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"dq": (xp, k, v), "dk": (q, xp, v), "dv": (q, k, xp)}[name]
+            args_m = {"dq": (xm, k, v), "dk": (q, xm, v), "dv": (q, k, xm)}[name]
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        worst = max(worst, np.max(np.abs(fd - out[name])) / np.max(np.abs(fd)))
+    return worst
+
+
+def pin_brute_force(seed=11, N=6, d=3, causal=False):
+    q, k, v, do, scale = rng_case(seed, 1, 1, 1, N, d)
+    out = A.attention_backward(q, k, v, do, scale, causal)
+    ql, kl, vl, dol = (x[0, 0].tolist() for x in (q, k, v, do))
+    o_b, lse_b = BR.forward(ql, kl, vl, scale, causal)
+    dq_b, dk_b, dv_b = BR.backward(ql, kl, vl, dol, scale, causal)
+    err = max(np.max(np.abs(out["o"][0, 0] - np.array(o_b))),
+              np.max(np.abs(out["lse"][0, 0] - np.array(lse_b))))
+    for name, ref in (("dq", dq_b), ("dk", dk_b), ("dv", dv_b)):
+        err = max(err, np.max(np.abs(out[name][0, 0] - np.array(ref))))
+    return err
+
+
+def pin_torch_library(seed=12, causal=False, gqa=False):
+    """Second opinion: torch CPU scaled_dot_product_attention in float64 plus autograd."""
+    import torch
+    H, Hkv = (4, 2) if gqa else (2, 2)
+    q, k, v, do, scale = rng_case(seed, 2, H, Hkv, 11, 6)
+    out = A.attention_backward(q, k, v, do, scale, causal)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    rep = H // Hkv
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(rep, dim=1), tv.repeat_interleave(rep, dim=1),
+        is_causal=causal, scale=scale)
+    o.backward(torch.tensor(do))
+    err = np.max(np.abs(o.detach().numpy() - out["o"]))
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        err = max(err, np.max(np.abs(t.grad.numpy() - out[name])))
+    return err
+
+
+def pin_row_sampling(seed=13, causal=True):
+    """Row-by-row evaluation equals the full forward (the large-shape parity path)."""
+    q, k, v, _, scale = rng_case(seed, 2, 4, 2, 9, 3)
+    o, lse = A.attention_forward(q, k, v, scale, causal, row_block=4)
+    picks = [(1, 3, 0), (0, 1, 8), (1, 0, 4), (0, 2, 5)]
+    o_r, lse_r = A.attention_forward_rows(q, k, v, scale, causal, picks)
+    err = 0.0
+    for n, (b, h, i) in enumerate(picks):
+        err = max(err, np.max(np.abs(o_r[n] - o[b, h, i])), abs(lse_r[n] - lse[b, h, i]))
+    return err
+
+
+def pin_row_blocking(seed=14, causal=True):
+    """Row blocks of complete rows (size 3) equal a single block."""
+    q, k, v, do, scale = rng_case(seed, 1, 2, 1, 10, 4)
+    a = A.attention_backward(q, k, v, do, scale, causal, row_block=3)
+    b = A.attention_backward(q, k, v, do, scale, causal, row_block=1024)
+    return max(np.max(np.abs(a[n] - b[n])) for n in ("o", "lse", "dq", "dk", "dv", "D"))
+
+
+ALL_PINS = {
+    "worked_example_walk": (pin_worked_example_walk, 1e-12),
+    "worked_example_scores": (pin_worked_example_scores, 0.0),
+    "worked_example_naive": (pin_worked_example_naive, 1e-12),
+    "tiled_equals_naive": (pin_tiled_equals_naive, 1e-13),
+    "tiled_equals_naive_causal": (lambda: pin_tiled_equals_naive(causal=True, br=3, bc=4), 1e-13),
+    "rows_sum_to_one": (pin_rows_sum_to_one, 1e-14),
+    "shift_invariance": (pin_shift_invariance, 1e-12),
+    "shift_invariance_causal": (lambda: pin_shift_invariance(causal=True), 1e-12),
+    "softmax_jvp": (pin_softmax_jvp, 1e-14),
+    "softmax_jvp_fd": (pin_softmax_jvp_fd, 1e-8),
+    "d_identity": (pin_d_identity, 1e-13),
+    "equal_value_rows": (pin_equal_value_rows, 1e-13),
+    "equal_value_rows_causal": (lambda: pin_equal_value_rows(causal=True), 1e-13),
+    "zero_query": (pin_zero_query, 1e-14),
+    "zero_query_causal": (lambda: pin_zero_query(causal=True), 1e-14),
+    "causal_row0_single_key": (pin_causal_row0_and_single_key, 1e-14),
+    "gqa_is_repeated_mha": (pin_gqa_is_repeated_mha, 1e-13),
+    "finite_differences": (pin_finite_differences, 1e-7),
+    "finite_differences_causal_gqa": (lambda: pin_finite_differences(causal=True, gqa=True, N=9), 1e-7),
+    "brute_force": (pin_brute_force, 1e-13),
+    "brute_force_causal": (lambda: pin_brute_force(causal=True, N=7), 1e-13),
+    "torch_library": (pin_torch_library, 1e-12),
+    "torch_library_causal_gqa": (lambda: pin_torch_library(causal=True, gqa=True), 1e-12),
+    "row_sampling": (pin_row_sampling, 1e-13),
+    "row_blocking": (pin_row_blocking, 1e-13),
+}

@@ -1,0 +1,104 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each.
+
+This is the evidence that the pins in ``oracle_pins.py`` constrain every step of
+the oracle: a dropped term, a wrong sign, a missing scale, a transposed operand or
+a wrong head map each make at least one pin fail.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.attention as A
+import oracle_pins as P
+
+
+def _mutant_head(variant):
+    orig = A.attention_head
+
+    def head(q, k, v, scale, causal, do=None, row_block=1024):
+        if do is None or variant is None:
+            return orig(q, k, v, scale, causal, do, row_block)
+        n = q.shape[0]
+        s = A.scores(q, k, scale, causal, np.arange(n))
+        p = A.softmax_rows(s)
+        o = p @ v
+        lse = A.logsumexp_rows(s)
+        dp = do @ v.T
+        ds = A.softmax_backward_rows(p, dp)
+        dvec = np.sum(p * dp, axis=-1)
+        dq = scale * (ds @ k)
+        dk = scale * (ds.T @ q)
+        dv = p.T @ do
+        if variant == "dk_no_scale":
+            dk = ds.T @ q
+        elif variant == "dk_transposed":
+            dk = scale * (ds @ q)
+        elif variant == "dv_transposed":
+            dv = p @ do
+        elif variant == "dq_uses_v":
+            dq = scale * (ds @ v)
+        elif variant == "dp_transposed":
+            ds = A.softmax_backward_rows(p, (do @ v.T).T)
+            dq = scale * (ds @ k)
+            dk = scale * (ds.T @ q)
+        return o, lse, dq, dk, dv, dvec
+
+    return head
+
+
+MUTANTS = {
+    "jvp_drops_dot": ("softmax_backward_rows", lambda p, g: p * g),
+    "jvp_sign_flip": ("softmax_backward_rows",
+                      lambda p, g: p * (np.sum(p * g, axis=-1, keepdims=True) - g)),
+    "scores_no_scale": ("scores", lambda q, k, scale, causal, row_ids=None:
+                        P_orig_scores(q, k, 1.0, causal, row_ids)),
+    "causal_off_by_one": ("scores", lambda q, k, scale, causal, row_ids=None:
+                          _shifted_mask(q, k, scale, causal, row_ids)),
+    "lse_drops_max": ("logsumexp_rows",
+                      lambda s: np.log(np.sum(np.exp(s - np.max(s, axis=-1, keepdims=True)), axis=-1))),
+    "gqa_modulo_map": ("kv_head_of", lambda h, H, Hkv: h % Hkv),
+    "dk_no_scale": ("attention_head", "dk_no_scale"),
+    "dk_transposed": ("attention_head", "dk_transposed"),
+    "dv_transposed": ("attention_head", "dv_transposed"),
+    "dq_uses_v": ("attention_head", "dq_uses_v"),
+    "dp_transposed": ("attention_head", "dp_transposed"),
+}
+
+P_orig_scores = A.scores
+
+
+def _shifted_mask(q, k, scale, causal, row_ids):
+    s = scale * (q @ k.T)
+    if causal:
+        if row_ids is None:
+            row_ids = np.arange(q.shape[0])
+        s = np.where(np.arange(k.shape[0])[None, :] > row_ids[:, None] + 1, -np.inf, s)
+    return s
+
+
+def _failing_pins():
+    failed = []
+    for name, (fn, bound) in P.ALL_PINS.items():
+        try:
+            with np.errstate(all="ignore"):
+                err = fn()
+            if not np.isfinite(err) or err > bound:
+                failed.append(name)
+        except Exception:  # a shape error or NaN assertion also counts as caught
+            failed.append(name)
+    return failed
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _failing_pins() == []
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_mutant_is_caught(mutant, monkeypatch):
+    target, repl = MUTANTS[mutant]
+    if target == "attention_head":
+        monkeypatch.setattr(A, "attention_head", _mutant_head(repl))
+    else:
+        monkeypatch.setattr(A, target, repl)
+    failed = _failing_pins()
+    assert failed, f"no pin caught mutant {mutant}"
