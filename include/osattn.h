@@ -1,0 +1,102 @@
+/*
+ * osattn — fused online-softmax scaled-dot-product attention for AMD MI355X (gfx950).
+ *
+ * C ABI.  Plain device pointers and integer sizes; no C++ or framework types.
+ * Every entry point only enqueues work on the given HIP stream and returns; it
+ * never synchronises, never allocates device memory and keeps no global state,
+ * so calls are re-entrant.  Faults inside a kernel surface at the caller's next
+ * synchronisation on that stream.
+ *
+ * Operation (FlashAttention-2 page, "Standard Attention" and the FA2 inner loop;
+ * ml-notes page, why scores are divided by sqrt(d)):
+ *
+ *     S   = scale * Q K^T,        S_ij = -inf for j > i when causal
+ *     O   = softmax_rows(S) V
+ *     LSE = ln sum_j exp(S_ij)    per query row
+ *
+ * computed tile by tile with a running row max and running denominator so that
+ * no N x N matrix is ever written to memory.  The backward pass (softmax-backward
+ * page, "Backpropagating Through Softmax": the row JVP P*(dP - <P, dP>)) rebuilds
+ * P from LSE and forms
+ *
+ *     D  = rowsum(dO * O),  dS = P * (dO V^T - D),
+ *     dV = P^T dO,  dQ = scale * dS K,  dK = scale * dS^T Q.
+ *
+ * Layouts (all row-major and contiguous, element type given by `dtype`):
+ *     q, o, dO, dq : [B][H][N][d]
+ *     k, v, dk, dv : [B][Hkv][N][d]
+ *     lse          : [B][H][N]  float32, natural-log units
+ * Query head h reads key/value head h / (H / Hkv) (grouped-query attention,
+ * contiguous groups); dk and dv of a key/value head sum over its query heads.
+ * The causal mask is square and top-left aligned: query i sees keys 0..i.
+ *
+ * Supported: dtype in {ATTN_F32, ATTN_F16, ATTN_BF16}; d in {64, 128}; any
+ * N >= 1; H a multiple of Hkv.  Inputs and outputs use `dtype`; arithmetic
+ * accumulates in float32; softmax statistics are float32.  Outputs are rounded
+ * to nearest even.
+ */
+#ifndef OSATTN_H
+#define OSATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,      /* a required pointer is NULL                                */
+  ATTN_ERR_SHAPE = -2,     /* B, H, Hkv or N < 1, or a tensor exceeds 2^31 rows         */
+  ATTN_ERR_HEAD_DIM = -3,  /* d not in {64, 128}                                         */
+  ATTN_ERR_GQA = -4,       /* H not a multiple of Hkv                                    */
+  ATTN_ERR_DTYPE = -5,     /* dtype not an attn_dtype_t value                            */
+  ATTN_ERR_SCALE = -6,     /* scale not finite or not > 0                                */
+  ATTN_ERR_ALIGN = -7,     /* a tensor base address is not 16-byte aligned               */
+  ATTN_ERR_WORKSPACE = -8, /* workspace NULL or smaller than attn_bwd_workspace_bytes()  */
+  ATTN_ERR_LAUNCH = -9     /* the HIP runtime rejected a kernel launch                   */
+} attn_status_t;
+
+/*
+ * Forward pass.  Reads q, k, v; writes o (fully overwritten) and lse.
+ *   scale  : multiplies Q K^T before masking and softmax (usually 1/sqrt(d)).
+ *   causal : 0 or 1.
+ *   stream : a hipStream_t (NULL = the default stream).
+ * Returns ATTN_OK or a negative attn_status_t; on a validation error nothing
+ * is launched and no output is touched.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Hkv, int N, int d, float scale, int causal,
+             int dtype, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for these sizes: the per-row
+ * D = rowsum(dO * O) in float32 (B*H*N values), rounded up to 256 bytes.
+ * Returns 0 for invalid sizes.  Callers should always ask this function rather
+ * than assume the formula.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int dtype);
+
+/*
+ * Backward pass.  Reads q, k, v, o, lse (as written by attn_fwd with the same
+ * arguments) and dO; writes dq, dk, dv (fully overwritten).  `workspace` is
+ * caller-owned device memory of at least attn_bwd_workspace_bytes() bytes; its
+ * contents on entry do not matter and on return are unspecified.  Two calls that
+ * may overlap in time need distinct workspaces.
+ * Same validation and return codes as attn_fwd, plus ATTN_ERR_WORKSPACE.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dO, void* dq, void* dk, void* dv,
+             int B, int H, int Hkv, int N, int d, float scale, int causal,
+             int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* A static, human-readable name for a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSATTN_H */

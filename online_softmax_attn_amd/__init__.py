@@ -1,0 +1,182 @@
+"""osattn: fused online-softmax attention for AMD MI355X (gfx950), Python binding.
+
+A thin ctypes layer over the C ABI in ``include/osattn.h`` (``libosattn.so`` next
+to this file).  It only checks tensors and marshals pointers, sizes and the
+current HIP stream: every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+
+    o, lse = attn_fwd(q, k, v, causal=False)          # q [B,H,N,d], k/v [B,Hkv,N,d]
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=False)
+
+Tensors must be contiguous ROCm-device tensors of one dtype (float32, float16 or
+bfloat16); ``lse`` is float32 [B,H,N].  ``scale`` defaults to 1/sqrt(d).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "attn_fwd",
+    "attn_bwd",
+    "attn_bwd_workspace_bytes",
+    "status_string",
+    "library",
+    "library_path",
+    "AttnError",
+    "DTYPE_CODES",
+    "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libosattn.so")
+
+STATUS = {
+    "ATTN_OK": 0,
+    "ATTN_ERR_NULL": -1,
+    "ATTN_ERR_SHAPE": -2,
+    "ATTN_ERR_HEAD_DIM": -3,
+    "ATTN_ERR_GQA": -4,
+    "ATTN_ERR_DTYPE": -5,
+    "ATTN_ERR_SCALE": -6,
+    "ATTN_ERR_ALIGN": -7,
+    "ATTN_ERR_WORKSPACE": -8,
+    "ATTN_ERR_LAUNCH": -9,
+}
+DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library() -> ctypes.CDLL:
+    """Load libosattn.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m online_softmax_attn_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp,
+                             ctypes.c_size_t, vp]
+    lib.attn_bwd.restype = i
+    lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().attn_status_string(int(status)).decode()
+
+
+def _check_dev(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the ROCm device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _dims(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B,H,N,d] and k, v [B,Hkv,N,d]")
+    B, H, N, d = q.shape
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    return B, H, k.shape[1], N, d
+
+
+def _stream_handle(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def attn_bwd_workspace_bytes(B, H, Hkv, N, d, dtype) -> int:
+    code = DTYPE_CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(library().attn_bwd_workspace_bytes(B, H, Hkv, N, d, code))
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """O and LSE for q [B,H,N,d], k/v [B,Hkv,N,d]; enqueued on the current stream."""
+    lib = library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    if q.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, Hkv, N, d = _dims(q, k)
+    if v.shape != k.shape:
+        raise ValueError("v must have the shape of k")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    _check_dev("out", out, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    if out.shape != q.shape or lse.shape != (B, H, N):
+        raise ValueError("out / lse have the wrong shape")
+    st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      B, H, Hkv, N, d, float(scale), int(bool(causal)), DTYPE_CODES[q.dtype],
+                      _stream_handle(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def attn_bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV from the forward's O and LSE; enqueued on the current stream."""
+    lib = library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    B, H, Hkv, N, d = _dims(q, k)
+    if v.shape != k.shape or o.shape != q.shape or do.shape != q.shape or lse.shape != (B, H, N):
+        raise ValueError("inconsistent shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_dev(name, t, q.dtype)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} has the wrong shape")
+    need = attn_bwd_workspace_bytes(B, H, Hkv, N, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    _check_dev("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      B, H, Hkv, N, d, float(scale), int(bool(causal)), DTYPE_CODES[q.dtype],
+                      workspace.data_ptr(), ws_bytes, _stream_handle(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

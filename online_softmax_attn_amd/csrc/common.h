@@ -1,0 +1,112 @@
+// Device-side building blocks shared by the osattn kernels (gfx950 / CDNA4 only).
+//
+// MFMA operand layouts used throughout (wave64, confirmed on gfx950):
+//   v_mfma_f32_32x32x16_{bf16,f16}:  D[32x32] += A[32x16] * B[16x32]
+//     lane l supplies A[m = l%32][k = 8*(l/32) + j] and B[k = 8*(l/32) + j][n = l%32]
+//     for j = 0..7 (one 128-bit register quad each);
+//     result register r of lane l is D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32].
+//   ds_read_b64_tr_b16 (LDS transpose read): inside each group of 16 lanes, lane i
+//     receives element i%4 of the 4-element (64-bit) chunk addressed by lane
+//     4*e + i/4, as its element e.  Pointing lane 4*a + b at row a, columns 4b..4b+3
+//     of a row-major tile therefore hands lane i the column i of rows 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace osattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element traits: storage is 16-bit for bf16/fp16.
+template <typename T> struct Mfma;
+
+template <> struct Mfma<__bf16> {
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ f32x16 mma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<_Float16> {
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ f32x16 mma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// fp32 -> 16-bit with round-to-nearest-even, returned as raw bits.
+template <typename T> __device__ __forceinline__ uint16_t to_bits(float x);
+template <> __device__ __forceinline__ uint16_t to_bits<__bf16>(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+template <> __device__ __forceinline__ uint16_t to_bits<_Float16>(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+template <typename T> __device__ __forceinline__ float from_bits(uint16_t b);
+template <> __device__ __forceinline__ float from_bits<__bf16>(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+template <> __device__ __forceinline__ float from_bits<_Float16>(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Pack 8 floats into an MFMA operand (round to nearest even).
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::vec8 pack8(const float* x) {
+  typename Mfma<T>::vec8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (T)x[j];
+  return r;
+}
+
+// LDS pointer helpers (address space 3).
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// `p` must point into a __shared__ array; the cast is an address-space cast.
+__device__ __forceinline__ i16x4 lds_read_tr4(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(void*)p);
+}
+
+// Combine two transposed 4-element reads into one 8-element MFMA operand.
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::vec8 join8(i16x4 lo, i16x4 hi) {
+  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(typename Mfma<T>::vec8, v);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::vec8 as_vec8(u32x4 x) {
+  return __builtin_bit_cast(typename Mfma<T>::vec8, x);
+}
+
+__device__ __forceinline__ float wave_xor32_max(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float wave_xor32_sum(float x) {
+  return x + __shfl_xor(x, 32);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maps a linear workgroup index to a logical one so that the workgroups the
+// hardware places on one XCD (dispatch is round-robin over the 8 XCDs) get a
+// contiguous range of logical tiles, i.e. the same heads, sharing that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int per = nblocks >> 3;
+  if (bid >= (per << 3)) return bid;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+}  // namespace osattn

@@ -1,0 +1,265 @@
+// float32 forward and backward kernels (vector FMA, no reduced-precision inputs).
+//
+// Same method as the MFMA path (FlashAttention-2 page: per query tile, a loop
+// over key/value tiles with running max, running denominator and unnormalised
+// output; the backward rebuilds P from the saved logsumexp), written for exact
+// float32 products: every dot product is a chain of fp32 FMAs.  One wave owns 32
+// rows; lane l handles row l % 32 and the column half l / 32 of the head
+// dimension, and the two halves of each dot product meet with one lane exchange.
+// Tiles of 32 key (or query) rows are staged in LDS and read as broadcasts.
+#include "common.h"
+#include "launch.h"
+
+namespace osattn {
+
+namespace {
+
+constexpr int kRows = 32;  // rows per workgroup (one wave of 64 lanes)
+
+template <int D>
+__device__ __forceinline__ float half_dot(const float* a, const float* lds_row) {
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) s = fmaf(a[c], lds_row[c], s);
+  return s;
+}
+
+// Cooperative copy of `rows` rows of D floats (row-major, global) into LDS,
+// zero-filling rows at or beyond `limit`.
+template <int D>
+__device__ __forceinline__ void stage_rows(float* lds, const float* g, int first, int limit) {
+  for (int e = threadIdx.x; e < kRows * D; e += 64) {
+    const int r = e / D;
+    lds[e] = (first + r < limit) ? g[(size_t)(first + r) * D + (e % D)] : 0.f;
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q,
+                                                     const float* __restrict__ K,
+                                                     const float* __restrict__ V,
+                                                     float* __restrict__ O,
+                                                     float* __restrict__ LSE, int H, int Hkv,
+                                                     int N, float scale) {
+  __shared__ float ks[kRows * D];
+  __shared__ float vs[kRows * D];
+  const int lane = threadIdx.x;
+  const int half = lane >> 5;
+  const int bh = blockIdx.y;
+  const int h = bh % H, b = bh / H;
+  const int kvh = h / (H / Hkv);
+  const int row = blockIdx.x * kRows + (lane & 31);
+  const float* Qp = Q + (size_t)bh * N * D;
+  const float* Kp = K + (size_t)(b * Hkv + kvh) * N * D;
+  const float* Vp = V + (size_t)(b * Hkv + kvh) * N * D;
+
+  float q[D / 2], o[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) {
+    q[c] = row < N ? Qp[(size_t)row * D + half * (D / 2) + c] : 0.f;
+    o[c] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  int n_keys = N;
+  if (CAUSAL) n_keys = min(N, blockIdx.x * kRows + kRows);
+  for (int k0 = 0; k0 < n_keys; k0 += kRows) {
+    __syncthreads();
+    stage_rows<D>(ks, Kp, k0, N);
+    stage_rows<D>(vs, Vp, k0, N);
+    __syncthreads();
+    float s[kRows];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+      float x = half_dot<D>(q, ks + j * D + half * (D / 2));
+      x = (x + __shfl_xor(x, 32)) * scale;
+      const int key = k0 + j;
+      if (key >= N || (CAUSAL && key > row)) x = -INFINITY;
+      s[j] = x;
+      mt = fmaxf(mt, x);
+    }
+    const float mn = fmaxf(m, mt);
+    // A row with every key masked so far keeps m = -inf; its weights stay zero.
+    const float alpha = (mn == -INFINITY) ? 1.f : expf(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c) o[c] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+      const float p = (s[j] == -INFINITY) ? 0.f : expf(s[j] - mn);
+      l += p;
+      const float* vr = vs + j * D + half * (D / 2);
+#pragma unroll
+      for (int c = 0; c < D / 2; ++c) o[c] = fmaf(p, vr[c], o[c]);
+    }
+    m = mn;
+  }
+  if (row < N) {
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c) O[((size_t)bh * N + row) * D + half * (D / 2) + c] = o[c] * inv;
+    if (half == 0) LSE[(size_t)bh * N + row] = m + logf(l);
+  }
+}
+
+// dK, dV for 32 key rows of one key/value head, looping over every query row of
+// every query head in its group (single writer per key row).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    float* __restrict__ dK, float* __restrict__ dV, int H, int Hkv, int N, float scale) {
+  __shared__ float qs[kRows * D];
+  __shared__ float dos[kRows * D];
+  __shared__ float lse_s[kRows];
+  __shared__ float d_s[kRows];
+  const int lane = threadIdx.x;
+  const int half = lane >> 5;
+  const int bg = blockIdx.y;  // b * Hkv + kvh
+  const int kvh = bg % Hkv, b = bg / Hkv;
+  const int n_rep = H / Hkv;
+  const int key = blockIdx.x * kRows + (lane & 31);
+  const float* Kp = K + (size_t)bg * N * D;
+  const float* Vp = V + (size_t)bg * N * D;
+
+  float kr[D / 2], vr[D / 2], dk[D / 2], dv[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) {
+    kr[c] = key < N ? Kp[(size_t)key * D + half * (D / 2) + c] : 0.f;
+    vr[c] = key < N ? Vp[(size_t)key * D + half * (D / 2) + c] : 0.f;
+    dk[c] = 0.f;
+    dv[c] = 0.f;
+  }
+  const int first_q = CAUSAL ? blockIdx.x * kRows : 0;
+  for (int r = 0; r < n_rep; ++r) {
+    const int bh = b * H + kvh * n_rep + r;
+    const float* Qp = Q + (size_t)bh * N * D;
+    const float* dOp = dO + (size_t)bh * N * D;
+    for (int i0 = first_q; i0 < N; i0 += kRows) {
+      __syncthreads();
+      stage_rows<D>(qs, Qp, i0, N);
+      stage_rows<D>(dos, dOp, i0, N);
+      if (lane < kRows) {
+        const int i = i0 + lane;
+        lse_s[lane] = i < N ? LSE[(size_t)bh * N + i] : INFINITY;
+        d_s[lane] = i < N ? Dv[(size_t)bh * N + i] : 0.f;
+      }
+      __syncthreads();
+      for (int ii = 0; ii < kRows; ++ii) {
+        const int i = i0 + ii;
+        float s = half_dot<D>(kr, qs + ii * D + half * (D / 2));
+        s = (s + __shfl_xor(s, 32)) * scale;
+        float dp = half_dot<D>(vr, dos + ii * D + half * (D / 2));
+        dp = dp + __shfl_xor(dp, 32);
+        const bool masked = (i >= N) || (CAUSAL && key > i);
+        const float p = masked ? 0.f : expf(s - lse_s[ii]);
+        const float ds = p * (dp - d_s[ii]);
+        const float* qrow = qs + ii * D + half * (D / 2);
+        const float* dorow = dos + ii * D + half * (D / 2);
+#pragma unroll
+        for (int c = 0; c < D / 2; ++c) {
+          dv[c] = fmaf(p, dorow[c], dv[c]);
+          dk[c] = fmaf(ds, qrow[c], dk[c]);
+        }
+      }
+    }
+  }
+  if (key < N) {
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c) {
+      dK[(size_t)bg * N * D + (size_t)key * D + half * (D / 2) + c] = dk[c] * scale;
+      dV[(size_t)bg * N * D + (size_t)key * D + half * (D / 2) + c] = dv[c];
+    }
+  }
+}
+
+// dQ for 32 query rows, looping over the key/value tiles they see.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    float* __restrict__ dQ, int H, int Hkv, int N, float scale) {
+  __shared__ float ks[kRows * D];
+  __shared__ float vs[kRows * D];
+  const int lane = threadIdx.x;
+  const int half = lane >> 5;
+  const int bh = blockIdx.y;
+  const int h = bh % H, b = bh / H;
+  const int kvh = h / (H / Hkv);
+  const int row = blockIdx.x * kRows + (lane & 31);
+  const float* Kp = K + (size_t)(b * Hkv + kvh) * N * D;
+  const float* Vp = V + (size_t)(b * Hkv + kvh) * N * D;
+
+  float q[D / 2], dor[D / 2], dq[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) {
+    q[c] = row < N ? Q[((size_t)bh * N + row) * D + half * (D / 2) + c] : 0.f;
+    dor[c] = row < N ? dO[((size_t)bh * N + row) * D + half * (D / 2) + c] : 0.f;
+    dq[c] = 0.f;
+  }
+  const float lse = row < N ? LSE[(size_t)bh * N + row] : INFINITY;
+  const float dd = row < N ? Dv[(size_t)bh * N + row] : 0.f;
+  int n_keys = N;
+  if (CAUSAL) n_keys = min(N, blockIdx.x * kRows + kRows);
+  for (int k0 = 0; k0 < n_keys; k0 += kRows) {
+    __syncthreads();
+    stage_rows<D>(ks, Kp, k0, N);
+    stage_rows<D>(vs, Vp, k0, N);
+    __syncthreads();
+    for (int j = 0; j < kRows; ++j) {
+      const int key = k0 + j;
+      float s = half_dot<D>(q, ks + j * D + half * (D / 2));
+      s = (s + __shfl_xor(s, 32)) * scale;
+      float dp = half_dot<D>(dor, vs + j * D + half * (D / 2));
+      dp = dp + __shfl_xor(dp, 32);
+      const bool masked = (key >= N) || (row >= N) || (CAUSAL && key > row);
+      const float p = masked ? 0.f : expf(s - lse);
+      const float ds = p * (dp - dd);
+      const float* krow = ks + j * D + half * (D / 2);
+#pragma unroll
+      for (int c = 0; c < D / 2; ++c) dq[c] = fmaf(ds, krow[c], dq[c]);
+    }
+  }
+  if (row < N) {
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c) dQ[((size_t)bh * N + row) * D + half * (D / 2) + c] = dq[c] * scale;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t fwd_f32_t(const FwdArgs& a) {
+  dim3 grid((a.N + kRows - 1) / kRows, a.B * a.H);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, (hipStream_t)a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
+                     a.H, a.Hkv, a.N, a.scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t bwd_f32_t(const BwdArgs& a) {
+  dim3 gk((a.N + kRows - 1) / kRows, a.B * a.Hkv);
+  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), gk, dim3(64), 0, (hipStream_t)a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dO,
+                     a.lse, a.dvec, (float*)a.dk, (float*)a.dv, a.H, a.Hkv, a.N, a.scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 gq((a.N + kRows - 1) / kRows, a.B * a.H);
+  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), gq, dim3(64), 0, (hipStream_t)a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dO,
+                     a.lse, a.dvec, (float*)a.dq, a.H, a.Hkv, a.N, a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdArgs& a) {
+  if (a.d == 64) return a.causal ? fwd_f32_t<64, true>(a) : fwd_f32_t<64, false>(a);
+  return a.causal ? fwd_f32_t<128, true>(a) : fwd_f32_t<128, false>(a);
+}
+
+hipError_t launch_bwd_f32(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? bwd_f32_t<64, true>(a) : bwd_f32_t<64, false>(a);
+  return a.causal ? bwd_f32_t<128, true>(a) : bwd_f32_t<128, false>(a);
+}
+
+}  // namespace osattn

@@ -1,0 +1,47 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernel files.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace osattn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Hkv, N, d;
+  float scale;
+  int causal;
+  int dtype;  // 0 fp32, 1 fp16, 2 bf16
+  void* stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dO;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;  // workspace: D = rowsum(dO * O), [B][H][N] float32
+  int B, H, Hkv, N, d;
+  float scale;
+  int causal;
+  int dtype;
+  void* stream;
+};
+
+hipError_t launch_fwd_mfma(const FwdArgs& a);
+hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_bwd_preprocess(const BwdArgs& a);
+hipError_t launch_bwd_mfma(const BwdArgs& a);
+hipError_t launch_bwd_f32(const BwdArgs& a);
+
+}  // namespace osattn

@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+rejects every invalid argument with its status code before any launch.
+
+Only validation failures are exercised here (they return before the first HIP
+call), plus the pure host function attn_bwd_workspace_bytes.  The fake device
+pointers are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import online_softmax_attn_amd as osa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "osattn.h")
+
+P = 0x10000  # a 16-byte aligned fake address, never dereferenced
+S = osa.STATUS
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\**(attn_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def header_enum(name_prefix):
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(ATTN_[A-Z0-9_]+)\s*=\s*(-?\d+)", text)
+            if m.group(1).startswith(name_prefix)}
+
+
+def test_library_exports_every_header_symbol():
+    lib = osa.library()
+    names = header_functions()
+    assert set(names) == set(osa.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_codes_match_header():
+    enum = header_enum("ATTN_ERR")
+    enum["ATTN_OK"] = header_enum("ATTN_OK")["ATTN_OK"]
+    assert enum == S
+    for name, code in S.items():
+        assert osa.status_string(code) and osa.status_string(code) != "unknown status"
+    assert osa.status_string(-99) == "unknown status"
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Hkv=1, N=8, d=64, scale=0.125, causal=0,
+             dtype=2, stream=None)
+    a.update(kw)
+    return osa.library().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                  a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
+                                  a["stream"])
+
+
+def bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, Hkv=1, N=8, d=64,
+             scale=0.125, causal=0, dtype=2, ws=P, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return osa.library().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                                  a["dk"], a["dv"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                                  a["scale"], a["causal"], a["dtype"], a["ws"], a["ws_bytes"],
+                                  a["stream"])
+
+
+INVALID = [
+    ({"q": None}, "ATTN_ERR_NULL"),
+    ({"lse": None}, "ATTN_ERR_NULL"),
+    ({"B": 0}, "ATTN_ERR_SHAPE"),
+    ({"H": 0}, "ATTN_ERR_SHAPE"),
+    ({"Hkv": 0}, "ATTN_ERR_SHAPE"),
+    ({"N": 0}, "ATTN_ERR_SHAPE"),
+    ({"N": -5}, "ATTN_ERR_SHAPE"),
+    ({"B": 1 << 16, "H": 1 << 10, "Hkv": 1 << 10, "N": 1 << 10}, "ATTN_ERR_SHAPE"),
+    ({"causal": 2}, "ATTN_ERR_SHAPE"),
+    ({"d": 32}, "ATTN_ERR_HEAD_DIM"),
+    ({"d": 256}, "ATTN_ERR_HEAD_DIM"),
+    ({"d": 96}, "ATTN_ERR_HEAD_DIM"),
+    ({"H": 3, "Hkv": 2}, "ATTN_ERR_GQA"),
+    ({"dtype": 3}, "ATTN_ERR_DTYPE"),
+    ({"dtype": -1}, "ATTN_ERR_DTYPE"),
+    ({"scale": 0.0}, "ATTN_ERR_SCALE"),
+    ({"scale": -1.0}, "ATTN_ERR_SCALE"),
+    ({"scale": float("inf")}, "ATTN_ERR_SCALE"),
+    ({"scale": float("nan")}, "ATTN_ERR_SCALE"),
+    ({"q": P + 8}, "ATTN_ERR_ALIGN"),
+    ({"lse": P + 4}, "ATTN_ERR_ALIGN"),
+]
+
+
+@pytest.mark.parametrize("kw,code", INVALID, ids=[f"{k}->{c}" for k, c in INVALID])
+def test_fwd_rejects(kw, code):
+    assert fwd(**kw) == S[code]
+
+
+@pytest.mark.parametrize("kw,code", INVALID + [
+    ({"do": None}, "ATTN_ERR_NULL"),
+    ({"dv": None}, "ATTN_ERR_NULL"),
+    ({"ws": None}, "ATTN_ERR_WORKSPACE"),
+    ({"ws_bytes": 16}, "ATTN_ERR_WORKSPACE"),
+    ({"dk": P + 2}, "ATTN_ERR_ALIGN"),
+    ({"ws": P + 8}, "ATTN_ERR_ALIGN"),
+], ids=lambda x: str(x))
+def test_bwd_rejects(kw, code):
+    assert bwd(**kw) == S[code]
+
+
+def test_workspace_bytes():
+    f = osa.library().attn_bwd_workspace_bytes
+    assert f(1, 1, 1, 1, 64, 0) == 256
+    n = 4 * 16 * 8192
+    assert f(4, 16, 16, 8192, 128, 2) == n * 4
+    assert f(1, 32, 8, 16384, 128, 2) == 32 * 16384 * 4
+    assert f(1, 3, 2, 8, 64, 2) == 0          # H not a multiple of Hkv
+    assert f(1, 1, 1, 8, 80, 2) == 0          # unsupported d
+    assert f(0, 1, 1, 8, 64, 2) == 0
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        osa.attn_fwd(q, q, q)
