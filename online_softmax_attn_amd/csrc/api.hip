@@ -16,6 +16,8 @@ int validate_sizes(int B, int H, int Hkv, int N, int d, int dtype) {
   // Row indices (b * H + h) * N + i must fit comfortably in 32-bit arithmetic.
   if ((long long)B * H * N >= (1LL << 31) || (long long)B * Hkv * N >= (1LL << 31))
     return ATTN_ERR_SHAPE;
+  // One head's rows are addressed with 32-bit byte offsets.
+  if ((long long)N * d * 4 >= (1LL << 31)) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (H % Hkv != 0) return ATTN_ERR_GQA;
   if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;

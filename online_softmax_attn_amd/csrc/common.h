@@ -100,6 +100,62 @@ __device__ __forceinline__ float wave_xor32_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum of the eight 16-bit values of an MFMA operand, accumulated in fp32 with
+// v_dot2_f32_{bf16,f16} against (1, 1): two elements per instruction, and the
+// sum is of exactly the rounded values the matrix core consumes.
+template <typename T> __device__ __forceinline__ float sum8(typename Mfma<T>::vec8 v, float acc);
+template <> __device__ __forceinline__ float sum8<__bf16>(bf16x8 v, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+  return acc;
+}
+template <> __device__ __forceinline__ float sum8<_Float16>(f16x8 v, float acc) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+  return acc;
+}
+
+// ---- buffer resources -------------------------------------------------------------
+// A raw buffer over [base, base + bytes): loads at offsets >= bytes return zero,
+// which is how rows past the end of a sequence are read without branches.
+// Word 3 (0x00020000) is the raw-buffer configuration used for gfx9-family parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave
+// writes lds_chunk + 16*i (lds_chunk is wave-uniform and 16-byte aligned).
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_chunk,
+                                                  uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_chunk, 16, off, 0, 0, 0);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence would
+// wait for every outstanding global load, including prefetches still in flight.
+// Callers order their own memory traffic (LDS reads are consumed before the
+// barrier is reached; DMA writes are waited for with wait_vmcnt).
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // Maps a linear workgroup index to a logical one so that the workgroups the
 // hardware places on one XCD (dispatch is round-robin over the 8 XCDs) get a
 // contiguous range of logical tiles, i.e. the same heads, sharing that XCD's L2.

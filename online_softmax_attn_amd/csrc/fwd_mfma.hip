@@ -7,7 +7,9 @@
 // and writes O = Ot / l and the row logsumexp once.
 //
 // Mapping onto CDNA4:
-//  * 4 waves per workgroup; each wave owns QB blocks of 32 query rows.
+//  * NW waves per workgroup (8: two per SIMD, so one wave's softmax arithmetic
+//    overlaps another wave's matrix-core work); each wave owns QB blocks of 32
+//    query rows.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: the
 //    result layout then gives every lane one query row (lane % 32) and 16 keys per
 //    32-key block, so the row max and row sum are in-lane, plus one exchange with
@@ -15,46 +17,65 @@
 //  * O^T = V^T P^T uses the probabilities straight from registers as the B operand
 //    (the key order inside a 16-key chunk is permuted identically on both operands).
 //    V stays row-major in LDS and is read transposed with ds_read_b64_tr_b16.
-//  * K/V tiles of 64 keys are double-buffered in LDS: the next tile's global loads
-//    are issued before the current tile's math and stored to LDS after it.
-//  * exp2 with log2(e) * scale folded into one FMA per score.
+//  * K/V tiles of 64 keys go from HBM/L2 straight into LDS (buffer_load ... lds,
+//    16 bytes per lane, rows past the end read as zero), NBUF tiles in flight.
+//    LDS rows are unpadded; 16-byte granules are XOR-swizzled by row so that the
+//    128-bit K reads and the transposed V reads are free of bank conflicts.
+//  * exp2 with log2(e) * scale folded into one FMA per score; row sums with
+//    v_dot2 over the rounded probabilities the matrix core consumes.
 //  * Rescaling of Ot and l is lazy: the reference max is only moved when a row's
 //    new max exceeds it by more than 8 (log2 units), so exp2 arguments stay <= 8.
 //    The result is exact for any reference value (the correction the pages
 //    describe cancels in Ot / l); it only avoids rescaling work.
-//  * Causal: key tiles wholly after a wave's last row are skipped (loop bound per
-//    workgroup, skip per wave); only tiles that cross the diagonal are masked.
+//  * Causal: key tiles wholly after the workgroup's last row are not loaded, tiles
+//    wholly after a wave's last row are skipped by that wave, and only tiles that
+//    cross the diagonal are masked.  Workgroups with the longest rows start first.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace osattn {
 
-template <int D, int QB>
-struct FwdCfg {
-  static constexpr int kWaves = 4;
-  static constexpr int kBR = kWaves * 32 * QB;  // query rows per workgroup
-  static constexpr int kBC = 64;                // keys per tile
-  static constexpr int kKStride = D + 8;        // K row stride in LDS (elements): +16 B
-  static constexpr int kVStride = D + 32;       // V row stride in LDS (elements): +64 B
-  static constexpr int kKTile = kBC * kKStride;
-  static constexpr int kVTile = kBC * kVStride;
-  static constexpr int kChunksPerRow = D / 8;   // 16-byte chunks per row
-  static constexpr int kRowsPerPass = 256 / kChunksPerRow;
-  static constexpr int kPasses = kBC / kRowsPerPass;
+template <int D>
+struct FwdSwizzle {
+  // 16-byte granule index XOR applied to row `row` of a K tile / a V tile.
+  static __device__ __forceinline__ int k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  static __device__ __forceinline__ int v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 };
 
-template <typename T, int D, int QB, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
-__attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
+template <int D, int NW, int QB, int NBUF>
+struct FwdCfg {
+  static constexpr int kBR = NW * 32 * QB;     // query rows per workgroup
+  static constexpr int kBC = 64;               // keys per tile
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileElems = kBC * D;   // one K or V tile (16-bit elements)
+  static constexpr int kChunks = kBC * kRowBytes / 1024;  // 1 KB LDS-DMA chunks per tile
+  static constexpr int kCPW = kChunks / NW;    // chunks per wave per tensor
+  static_assert(kCPW >= 1 && kChunks % NW == 0, "tile must split evenly over the waves");
+};
+
+template <typename T, int D, int NW, int QB, int NBUF, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
+__attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                      float* __restrict__ LSE, int H, int Hkv, int N, int n_qtiles,
                      float scale_log2) {
-  using C = FwdCfg<D, QB>;
+  using C = FwdCfg<D, NW, QB, NBUF>;
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][C::kKTile];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][C::kVTile];
+  using Swz = FwdSwizzle<D>;
+  // One array per pipeline stage: with the stage known at compile time, the
+  // compiler can tell that reads of one stage do not alias the DMA writes still in
+  // flight into the others, and inserts no wait for them.
+  static_assert(NBUF == 2 || NBUF == 3, "two or three stages");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k2[NBUF > 2 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v2[NBUF > 2 ? C::kTileElems : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -72,52 +93,62 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int q0 = qt * C::kBR;
   const int wrow0 = q0 + wave * 32 * QB;
 
-  const uint16_t* Qp = Q + (size_t)bh * N * D;
-  const uint16_t* Kp = K + (size_t)(b * Hkv + kvh) * N * D;
-  const uint16_t* Vp = V + (size_t)(b * Hkv + kvh) * N * D;
+  const uint32_t head_bytes = (uint32_t)N * C::kRowBytes;
+  const auto rq = make_rsrc(Q + (size_t)bh * N * D, head_bytes);
+  const auto rk = make_rsrc(K + (size_t)(b * Hkv + kvh) * N * D, head_bytes);
+  const auto rv = make_rsrc(V + (size_t)(b * Hkv + kvh) * N * D, head_bytes);
 
   // Query fragments (B operand of S^T = K Q^T): lane holds row l32 of each block,
-  // columns 16c + 8*hi .. +7 for every 16-column chunk c.
+  // columns 16c + 8*hi .. +7 for every 16-column chunk c.  Rows >= N read zero.
   vec8 qf[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int row = wrow0 + 32 * qb + l32;
+    const uint32_t rowoff = (uint32_t)(wrow0 + 32 * qb + l32) * C::kRowBytes;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < N) x = *(const u32x4*)(Qp + (size_t)row * D + 16 * c + 8 * hi);
-      qf[qb][c] = as_vec8<T>(x);
-    }
+    for (int c = 0; c < D / 16; ++c) qf[qb][c] = as_vec8<T>(buffer_load16(rq, rowoff + (16 * c + 8 * hi) * 2));
   }
 
   int n_kt = (N + C::kBC - 1) / C::kBC;
   if (CAUSAL) n_kt = min(n_kt, (q0 + C::kBR + C::kBC - 1) / C::kBC);
 
-  // Global -> register staging of one K/V tile, then register -> LDS.
-  const int ld_row = tid / C::kChunksPerRow;
-  const int ld_col = (tid % C::kChunksPerRow) * 8;
-  u32x4 kst[C::kPasses], vst[C::kPasses];
-  auto gload = [&](int kt) {
+  // Global offsets of this lane's 16 bytes in each of its LDS-DMA chunks: chunk ch
+  // covers LDS bytes [ch*1024, +1024) of the tile, i.e. tile row off / kRowBytes,
+  // physical granule pg; the data there is logical granule pg ^ swizzle(row).
+  uint32_t goff_k[C::kCPW], goff_v[C::kCPW];
 #pragma unroll
-    for (int p = 0; p < C::kPasses; ++p) {
-      const int r = kt * C::kBC + p * C::kRowsPerPass + ld_row;
-      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-      if (r < N) {
-        zk = *(const u32x4*)(Kp + (size_t)r * D + ld_col);
-        zv = *(const u32x4*)(Vp + (size_t)r * D + ld_col);
-      }
-      kst[p] = zk;
-      vst[p] = zv;
+  for (int i = 0; i < C::kCPW; ++i) {
+    const int off = (wave * C::kCPW + i) * 1024 + lane * 16;
+    const int row = off / C::kRowBytes;
+    const int pg = (off % C::kRowBytes) / 16;
+    goff_k[i] = row * C::kRowBytes + ((pg ^ Swz::k(row)) * 16);
+    goff_v[i] = row * C::kRowBytes + ((pg ^ Swz::v(row)) * 16);
+  }
+  auto issue = [&](int kt, uint16_t* lk, uint16_t* lv) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)kt * C::kBC * C::kRowBytes;
+#pragma unroll
+    for (int i = 0; i < C::kCPW; ++i) {
+      const int ch = wave * C::kCPW + i;
+      buffer_load16_lds(rk, lk + ch * 512, base + goff_k[i]);
+      buffer_load16_lds(rv, lv + ch * 512, base + goff_v[i]);
     }
   };
-  auto lstore = [&](int buf) {
+
+  // LDS read offsets (bytes within a tile), loop-invariant per lane.
+  //  K (A operand of S^T): row kb*32 + l32, logical granule 2c + hi.
+  uint32_t koff[D / 16];
 #pragma unroll
-    for (int p = 0; p < C::kPasses; ++p) {
-      const int r = p * C::kRowsPerPass + ld_row;
-      *(u32x4*)&lds_k[buf][r * C::kKStride + ld_col] = kst[p];
-      *(u32x4*)&lds_v[buf][r * C::kVStride + ld_col] = vst[p];
-    }
-  };
+  for (int c = 0; c < D / 16; ++c) koff[c] = l32 * C::kRowBytes + (((2 * c + hi) ^ Swz::k(l32)) * 16);
+  //  V (transposed reads, see common.h): group g = lane / 16 and index i = lane % 16
+  //  read row 4*hi + i/4 (+8 for the upper half) of a 16-key chunk and columns
+  //  32t + 16*(g%2) + 4*(i%4) .. +3.
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  uint32_t voff[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    const int col = 32 * t + tr_col;
+    voff[t] = tr_row * C::kRowBytes + (((col >> 3) ^ Swz::v(tr_row)) * 16) + (col & 7) * 2;
+  }
 
   f32x16 acc[QB][D / 32];
 #pragma unroll
@@ -135,117 +166,124 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     l_run[qb] = 0.f;
   }
 
-  // Transposed-read addressing of V (see common.h): lane group g = lane / 16,
-  // index i = lane % 16 points at row 4*hi + i/4 (+8 for the second half) of the
-  // 16-key chunk and columns 16*(g%2) + 4*(i%4) .. +3 of the 32-column tile.
-  const int tr_row = 4 * hi + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) gload(kt + 1);
+  auto compute = [&](int kt, const char* kbase, const char* vbase) __attribute__((always_inline)) {
     const int k0 = kt * C::kBC;
     const bool active = !CAUSAL || (k0 <= wrow0 + 32 * QB - 1);
-    if (active) {
-      // ---- step 1: S^T = K_j Q_i^T ---------------------------------------------
-      f32x16 s[QB][2];
+    if (!active) return;
+
+    // ---- step 1: S^T = K_j Q_i^T -------------------------------------------------
+    f32x16 s[QB][2];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
+    for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 a =
-              *(const u32x4*)&lds_k[buf][(kb * 32 + l32) * C::kKStride + 16 * c + 8 * hi];
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 a = *(const u32x4*)(kbase + kb * 32 * C::kRowBytes + koff[c]);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = M::mma32(as_vec8<T>(a), qf[qb][c], s[qb][kb]);
-        }
-      }
-      // ---- causal / ragged-tail mask ------------------------------------------
-      const bool need_mask = (k0 + C::kBC > N) || (CAUSAL && k0 + C::kBC - 1 > wrow0);
-      if (need_mask) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int row = wrow0 + 32 * qb + l32;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-              if (key >= N || (CAUSAL && key > row)) s[qb][kb][r] = -INFINITY;
-            }
-        }
-      }
-      // ---- step 2/4: row max, lazy move of the reference max ---------------------
-      float mt[QB];
-      bool grow = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = s[qb][0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-        mt[qb] = wave_xor32_max(mx) * scale_log2;
-        grow |= mt[qb] > m_run[qb] + 8.0f;
-      }
-      if (__any(grow)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float mn = fmaxf(m_run[qb], mt[qb]);
-          const float alpha = fast_exp2(m_run[qb] - mn);
-          m_run[qb] = mn;
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[qb][t][r] *= alpha;
-        }
-      }
-      // ---- step 2/3: P = exp2(S*c - m), row sums of the rounded P ---------------
-      vec8 pf[QB][4];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float part = 0.f;
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          float pv[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            pv[j] = fast_exp2(fmaf(s[qb][c4 >> 1][8 * (c4 & 1) + j], scale_log2, -m_run[qb]));
-          pf[qb][c4] = pack8<T>(pv);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) part += (float)pf[qb][c4][j];
-        }
-        l_run[qb] += part;
-      }
-      // ---- step 5: O^T += V_j^T P^T ---------------------------------------------
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          const uint16_t* vb = &lds_v[buf][(16 * c4 + tr_row) * C::kVStride + 32 * t + tr_col];
-          const i16x4 lo = lds_read_tr4(vb);
-          const i16x4 up = lds_read_tr4(vb + 8 * C::kVStride);
-          const vec8 a = join8<T>(lo, up);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc[qb][t] = M::mma32(a, pf[qb][c4], acc[qb][t]);
-        }
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = M::mma32(as_vec8<T>(a), qf[qb][c], s[qb][kb]);
       }
     }
-    if (kt + 1 < n_kt) lstore(buf ^ 1);
-    __syncthreads();
+    // ---- causal / ragged-tail mask (only on tiles that need it) ------------------------
+    const bool need_mask = (k0 + C::kBC > N) || (CAUSAL && k0 + C::kBC - 1 > wrow0);
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int row = wrow0 + 32 * qb + l32;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key >= N || (CAUSAL && key > row)) s[qb][kb][r] = -INFINITY;
+          }
+      }
+    }
+    // ---- step 2/4: row max, lazy move of the reference max --------------------------
+    float mt[QB];
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
+      mt[qb] = wave_xor32_max(mx) * scale_log2;
+      grow |= mt[qb] > m_run[qb] + 8.0f;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float mn = fmaxf(m_run[qb], mt[qb]);
+        const float alpha = fast_exp2(m_run[qb] - mn);
+        m_run[qb] = mn;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[qb][t][r] *= alpha;
+      }
+    }
+    // ---- step 2/3: P = exp2(S*c - m), row sums of the rounded P -----------------------
+    vec8 pf[QB][4];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float neg_m = -m_run[qb];
+      float part = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(s[qb][c4 >> 1][8 * (c4 & 1) + j], scale_log2, neg_m));
+        pf[qb][c4] = pack8<T>(pv);
+        part = sum8<T>(pf[qb][c4], part);
+      }
+      l_run[qb] += part;
+    }
+    // ---- step 5: O^T += V_j^T P^T ---------------------------------------------------
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const char* vb = vbase + 16 * c4 * C::kRowBytes + voff[t];
+        const vec8 a = join8<T>(lds_read_tr4(vb), lds_read_tr4(vb + 8 * C::kRowBytes));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][t] = M::mma32(a, pf[qb][c4], acc[qb][t]);
+      }
+    }
+  };
+
+  if (0 < n_kt) issue(0, lds_k0, lds_v0);
+  if (NBUF > 2 && 1 < n_kt) issue(1, lds_k1, lds_v1);
+
+  // One pipeline step for tile kt held in stage S (compile-time).
+  auto step = [&](auto stage_c, int kt) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_c)::value;
+    uint16_t* lk = S == 0 ? lds_k0 : (S == 1 ? lds_k1 : lds_k2);
+    uint16_t* lv = S == 0 ? lds_v0 : (S == 1 ? lds_v1 : lds_v2);
+    constexpr int SN = (S + NBUF - 1) % NBUF;  // stage that receives tile kt + NBUF - 1
+    uint16_t* nk = SN == 0 ? lds_k0 : (SN == 1 ? lds_k1 : lds_k2);
+    uint16_t* nv = SN == 0 ? lds_v0 : (SN == 1 ? lds_v1 : lds_v2);
+    // Tile kt has landed once at most the later tiles' loads are outstanding.
+    if (NBUF > 2 && kt + 1 < n_kt) wait_vmcnt<(NBUF > 2 ? (NBUF - 2) * 2 * C::kCPW : 0)>();
+    else wait_vmcnt<0>();
+    block_barrier();  // every wave's share of tile kt is in LDS; tile kt-1 is free
+    if (kt + NBUF - 1 < n_kt) issue(kt + NBUF - 1, nk, nv);
+    compute(kt, (const char*)lk, (const char*)lv);
+  };
+  for (int kt = 0; kt < n_kt; kt += NBUF) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < n_kt) step(std::integral_constant<int, 1>{}, kt + 1);
+    if constexpr (NBUF > 2)
+      if (kt + 2 < n_kt) step(std::integral_constant<int, 2>{}, kt + 2);
   }
 
-  // ---- final normalisation: O = Ot / l, LSE = ln(2) * (m + log2 l) -------------
+  // ---- final normalisation: O = Ot / l, LSE = ln(2) * (m + log2 l) ---------------
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wrow0 + 32 * qb + l32;
@@ -269,27 +307,23 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 }
 
-template <typename T, int D, int QB, bool CAUSAL>
+template <typename T, int D, int NW, int QB, int NBUF, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
-  using C = FwdCfg<D, QB>;
+  using C = FwdCfg<D, NW, QB, NBUF>;
   const int n_qtiles = (a.N + C::kBR - 1) / C::kBR;
   const long long blocks = (long long)n_qtiles * a.B * a.H;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, QB, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0,
-                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H, a.Hkv, a.N, n_qtiles,
-                     a.scale * kLog2e);
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW, QB, NBUF, CAUSAL>), dim3((unsigned)blocks),
+                     dim3(NW * 64), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H, a.Hkv,
+                     a.N, n_qtiles, a.scale * kLog2e);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_fwd_d(const FwdArgs& a) {
-  // Two query blocks per wave double the reuse of every K/V operand read from LDS;
-  // short problems keep one block per wave so that more workgroups fill the chip.
-  const long long rows = (long long)a.B * a.H * a.N;
-  const bool big = rows >= 256LL * 256 * 2;
-  if (a.causal)
-    return big ? launch_fwd_t<T, D, 2, true>(a) : launch_fwd_t<T, D, 1, true>(a);
-  return big ? launch_fwd_t<T, D, 2, false>(a) : launch_fwd_t<T, D, 1, false>(a);
+  // 8 waves x 32 rows (256-row tiles), 2 waves per SIMD; three K/V tiles in flight.
+  if (a.causal) return launch_fwd_t<T, D, 8, 1, 3, true>(a);
+  return launch_fwd_t<T, D, 8, 1, 3, false>(a);
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a) {
