@@ -38,9 +38,9 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False, extra_flags=None, out: str = LIB) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    fd, tmp = tempfile.mkstemp(prefix=".libosattn.", suffix=".so.tmp", dir=HERE)
+def build(verbose: bool = False, extra_flags=None, out: str = LIB, csrc: str = CSRC) -> str:
+    srcs = [os.path.join(csrc, s) for s in SOURCES]
+    fd, tmp = tempfile.mkstemp(prefix=".libosattn.", suffix=".so.tmp", dir=os.path.dirname(os.path.abspath(out)))
     os.close(fd)
     cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags or []) + ["-o", tmp] + srcs
     if verbose:
@@ -60,8 +60,10 @@ def build(verbose: bool = False, extra_flags=None, out: str = LIB) -> str:
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")
-    ap.add_argument("--extra", nargs="*", default=[])
+    ap.add_argument("--extra", action="append", default=[])
+    ap.add_argument("--out", default=LIB)
+    ap.add_argument("--csrc", default=CSRC)
     args = ap.parse_args()
-    path = build(args.verbose, args.extra)
+    path = build(args.verbose, args.extra, args.out, args.csrc)
     print(path)
     sys.exit(0)

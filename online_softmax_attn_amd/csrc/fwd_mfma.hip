@@ -69,13 +69,15 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // One array per pipeline stage: with the stage known at compile time, the
   // compiler can tell that reads of one stage do not alias the DMA writes still in
   // flight into the others, and inserts no wait for them.
-  static_assert(NBUF == 2 || NBUF == 3, "two or three stages");
+  static_assert(NBUF == 3 || NBUF == 4, "three or four stages");
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[C::kTileElems];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_k2[NBUF > 2 ? C::kTileElems : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_v2[NBUF > 2 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k2[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v2[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k3[NBUF > 3 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v3[NBUF > 3 ? C::kTileElems : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -133,6 +135,22 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
   };
 
+  // Compile-time stage -> LDS buffers.
+  auto stage_k = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return lds_k0;
+    else if constexpr (S == 1) return lds_k1;
+    else if constexpr (S == 2) return lds_k2;
+    else return lds_k3;
+  };
+  auto stage_v = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return lds_v0;
+    else if constexpr (S == 1) return lds_v1;
+    else if constexpr (S == 2) return lds_v2;
+    else return lds_v3;
+  };
+
   // LDS read offsets (bytes within a tile), loop-invariant per lane.
   //  K (A operand of S^T): row kb*32 + l32, logical granule 2c + hi.
   uint32_t koff[D / 16];
@@ -166,56 +184,87 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     l_run[qb] = 0.f;
   }
 
-  auto compute = [&](int kt, const char* kbase, const char* vbase) __attribute__((always_inline)) {
-    const int k0 = kt * C::kBC;
-    const bool active = !CAUSAL || (k0 <= wrow0 + 32 * QB - 1);
-    if (!active) return;
-
-    // ---- step 1: S^T = K_j Q_i^T -------------------------------------------------
-    f32x16 s[QB][2];
+  // ---- building blocks of one tile ------------------------------------------------
+  // step 1: S^T = K_j Q_i^T from the K tile at kbase (16 MFMAs per query block).
+  auto scores = [&](const char* kbase, f32x16 (&sc)[QB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) sc[qb][kb][r] = 0.f;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const u32x4 a = *(const u32x4*)(kbase + kb * 32 * C::kRowBytes + koff[c]);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = M::mma32(as_vec8<T>(a), qf[qb][c], s[qb][kb]);
+        for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = M::mma32(as_vec8<T>(a), qf[qb][c], sc[qb][kb]);
       }
     }
-    // ---- causal / ragged-tail mask (only on tiles that need it) ------------------------
-    const bool need_mask = (k0 + C::kBC > N) || (CAUSAL && k0 + C::kBC - 1 > wrow0);
-    if (need_mask) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int row = wrow0 + 32 * qb + l32;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= N || (CAUSAL && key > row)) s[qb][kb][r] = -INFINITY;
-          }
-      }
-    }
-    // ---- step 2/4: row max, lazy move of the reference max --------------------------
-    float mt[QB];
-    bool grow = false;
+  };
+  // Causal / ragged-tail mask of the tile starting at key k0.
+  auto mask = [&](f32x16 (&sc)[QB][2], int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
+      const int row = wrow0 + 32 * qb + l32;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
-      mt[qb] = wave_xor32_max(mx) * scale_log2;
-      grow |= mt[qb] > m_run[qb] + 8.0f;
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= N || (CAUSAL && key > row)) sc[qb][kb][r] = -INFINITY;
+        }
     }
+  };
+  // step 2: row max of a tile (in log2 units of the scaled scores).
+  auto tile_max = [&](f32x16 (&sc)[QB][2], float (&mt)[QB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = fmaxf(sc[qb][0][0], sc[qb][0][1]);
+#pragma unroll
+      for (int i = 2; i < 32; i += 2)
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(sc[qb][i >> 4][i & 15], sc[qb][i >> 4][(i & 15) + 1]));
+      mt[qb] = wave_xor32_max(mx) * scale_log2;
+    }
+  };
+  // steps 2-3: P = exp2(S*c - m) rounded to the MFMA type; l += rowsum(rounded P).
+  auto probs = [&](f32x16 (&sc)[QB][2], vec8 (&pf)[QB][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float neg_m = -m_run[qb];
+      float part = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(sc[qb][c4 >> 1][8 * (c4 & 1) + j], scale_log2, neg_m));
+        pf[qb][c4] = pack8<T>(pv);
+        part = sum8<T>(pf[qb][c4], part);
+      }
+      l_run[qb] += part;
+    }
+  };
+  // step 5: O^T += V_j^T P^T from the V tile at vbase (16 MFMAs per query block);
+  // consecutive MFMAs go to different accumulators.
+  auto pv = [&](const char* vbase, vec8 (&pf)[QB][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        const char* vb = vbase + 16 * c4 * C::kRowBytes + voff[t];
+        const vec8 a = join8<T>(lds_read_tr4(vb), lds_read_tr4(vb + 8 * C::kRowBytes));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][t] = M::mma32(a, pf[qb][c4], acc[qb][t]);
+      }
+    }
+  };
+  // Lazy move of the reference max (step 4): only when some row's tile max exceeds
+  // it by more than 8; Ot and l are rescaled by exp2(m_old - m_new).
+  auto update_max = [&](float (&mt)[QB]) __attribute__((always_inline)) {
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) grow |= mt[qb] > m_run[qb] + 8.0f;
     if (__any(grow)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -229,58 +278,78 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           for (int r = 0; r < 16; ++r) acc[qb][t][r] *= alpha;
       }
     }
-    // ---- step 2/3: P = exp2(S*c - m), row sums of the rounded P -----------------------
-    vec8 pf[QB][4];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float neg_m = -m_run[qb];
-      float part = 0.f;
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        float pv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(s[qb][c4 >> 1][8 * (c4 & 1) + j], scale_log2, neg_m));
-        pf[qb][c4] = pack8<T>(pv);
-        part = sum8<T>(pf[qb][c4], part);
-      }
-      l_run[qb] += part;
-    }
-    // ---- step 5: O^T += V_j^T P^T ---------------------------------------------------
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const char* vb = vbase + 16 * c4 * C::kRowBytes + voff[t];
-        const vec8 a = join8<T>(lds_read_tr4(vb), lds_read_tr4(vb + 8 * C::kRowBytes));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb][t] = M::mma32(a, pf[qb][c4], acc[qb][t]);
-      }
-    }
+  };
+  auto active = [&](int kt) __attribute__((always_inline)) {
+    return !CAUSAL || (kt * C::kBC <= wrow0 + 32 * QB - 1);
+  };
+  auto needs_mask = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * C::kBC;
+    return (k0 + C::kBC > N) || (CAUSAL && k0 + C::kBC - 1 > wrow0);
   };
 
-  if (0 < n_kt) issue(0, lds_k0, lds_v0);
-  if (NBUF > 2 && 1 < n_kt) issue(1, lds_k1, lds_v1);
+  // ---- software pipeline ----------------------------------------------------------
+  // Iteration kt holds tile kt (its scores s_cur already computed) and tile kt+1 in
+  // LDS; it computes S(kt+1) on the matrix cores while the vector units turn S(kt)
+  // into probabilities, then O += V(kt)^T P(kt) and the row max of S(kt+1).  All of
+  // that is one basic block, so the instruction scheduler interleaves MFMA and VALU
+  // work of the same wave.  Loads run NBUF-2 tiles ahead of S.
+  auto wait_tiles_after = [&](int later) __attribute__((always_inline)) {
+    // wait until at most `later` tiles' loads are still in flight
+    if (NBUF > 3 && later >= 2) wait_vmcnt<(NBUF > 3 ? 4 * C::kCPW : 0)>();
+    else if (later >= 1) wait_vmcnt<2 * C::kCPW>();
+    else wait_vmcnt<0>();
+  };
 
-  // One pipeline step for tile kt held in stage S (compile-time).
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if (0 < n_kt) issue(0, stage_k(I0{}), stage_v(I0{}));
+  if (1 < n_kt) issue(1, stage_k(I1{}), stage_v(I1{}));
+  if (NBUF > 3 && 2 < n_kt) issue(2, stage_k(I2{}), stage_v(I2{}));
+  wait_tiles_after(min(NBUF - 2, n_kt - 1));
+  block_barrier();
+
+  f32x16 s_cur[QB][2];
+  float mt_cur[QB];
+  if (active(0)) {
+    scores((const char*)lds_k0, s_cur);
+    tile_max(s_cur, mt_cur);
+  }
+
   auto step = [&](auto stage_c, int kt) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_c)::value;
-    uint16_t* lk = S == 0 ? lds_k0 : (S == 1 ? lds_k1 : lds_k2);
-    uint16_t* lv = S == 0 ? lds_v0 : (S == 1 ? lds_v1 : lds_v2);
-    constexpr int SN = (S + NBUF - 1) % NBUF;  // stage that receives tile kt + NBUF - 1
-    uint16_t* nk = SN == 0 ? lds_k0 : (SN == 1 ? lds_k1 : lds_k2);
-    uint16_t* nv = SN == 0 ? lds_v0 : (SN == 1 ? lds_v1 : lds_v2);
-    // Tile kt has landed once at most the later tiles' loads are outstanding.
-    if (NBUF > 2 && kt + 1 < n_kt) wait_vmcnt<(NBUF > 2 ? (NBUF - 2) * 2 * C::kCPW : 0)>();
-    else wait_vmcnt<0>();
-    block_barrier();  // every wave's share of tile kt is in LDS; tile kt-1 is free
-    if (kt + NBUF - 1 < n_kt) issue(kt + NBUF - 1, nk, nv);
-    compute(kt, (const char*)lk, (const char*)lv);
+    constexpr int S1 = (S + 1) % NBUF;            // holds tile kt + 1
+    constexpr int SN = (S + NBUF - 1) % NBUF;     // receives tile kt + NBUF - 1
+    if (kt + 1 < n_kt) {
+      wait_tiles_after(min(NBUF - 3, n_kt - 2 - kt));
+      block_barrier();  // tile kt+1 visible to all waves; tile kt-1's buffers are free
+      if (kt + NBUF - 1 < n_kt) issue(kt + NBUF - 1, stage_k(std::integral_constant<int, SN>{}), stage_v(std::integral_constant<int, SN>{}));
+    }
+    if (!active(kt)) return;
+    if (needs_mask(kt)) {
+      mask(s_cur, kt * C::kBC);
+      tile_max(s_cur, mt_cur);
+    }
+    update_max(mt_cur);
+    // Scores of tile kt+1 (on the last tile this re-reads a resident buffer and the
+    // result is discarded).
+    f32x16 s_nxt[QB][2];
+    vec8 pf[QB][4];
+    scores((const char*)stage_k(std::integral_constant<int, S1>{}), s_nxt);
+    probs(s_cur, pf);
+    pv((const char*)stage_v(stage_c), pf);
+    tile_max(s_nxt, mt_cur);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s_cur[qb][kb] = s_nxt[qb][kb];
   };
   for (int kt = 0; kt < n_kt; kt += NBUF) {
     step(std::integral_constant<int, 0>{}, kt);
     if (kt + 1 < n_kt) step(std::integral_constant<int, 1>{}, kt + 1);
-    if constexpr (NBUF > 2)
-      if (kt + 2 < n_kt) step(std::integral_constant<int, 2>{}, kt + 2);
+    if (kt + 2 < n_kt) step(std::integral_constant<int, 2 % NBUF>{}, kt + 2);
+    if constexpr (NBUF > 3)
+      if (kt + 3 < n_kt) step(std::integral_constant<int, 3 % NBUF>{}, kt + 3);
   }
 
   // ---- final normalisation: O = Ot / l, LSE = ln(2) * (m + log2 l) ---------------
@@ -319,11 +388,24 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   return hipGetLastError();
 }
 
+// Tile configuration (waves per workgroup, 32-row query blocks per wave, K/V
+// buffers); the defaults are the measured best on MI355X and can be overridden
+// at build time for tuning sweeps.
+#ifndef OSATTN_FWD_NW
+#define OSATTN_FWD_NW 8
+#endif
+#ifndef OSATTN_FWD_QB
+#define OSATTN_FWD_QB 1
+#endif
+#ifndef OSATTN_FWD_NBUF
+#define OSATTN_FWD_NBUF 4
+#endif
+
 template <typename T, int D>
 static hipError_t launch_fwd_d(const FwdArgs& a) {
-  // 8 waves x 32 rows (256-row tiles), 2 waves per SIMD; three K/V tiles in flight.
-  if (a.causal) return launch_fwd_t<T, D, 8, 1, 3, true>(a);
-  return launch_fwd_t<T, D, 8, 1, 3, false>(a);
+  constexpr int NW = OSATTN_FWD_NW, QB = OSATTN_FWD_QB, NB = OSATTN_FWD_NBUF;
+  if (a.causal) return launch_fwd_t<T, D, NW, QB, NB, true>(a);
+  return launch_fwd_t<T, D, NW, QB, NB, false>(a);
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a) {
