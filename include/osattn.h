@@ -72,10 +72,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for these sizes: the per-row
- * D = rowsum(dO * O) in float32 (B*H*N values), rounded up to 256 bytes.
- * Returns 0 for invalid sizes.  Callers should always ask this function rather
- * than assume the formula.
+ * Bytes of device workspace attn_bwd needs for these sizes: two float32 values
+ * per query row (D = rowsum(dO * O) and LSE * log2(e)), each array rounded up to
+ * 256 bytes.  Returns 0 for invalid sizes.  Callers should always ask this
+ * function rather than assume the formula.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int dtype);
 

@@ -52,7 +52,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 size_t attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int dtype) {
   if (validate_sizes(B, H, Hkv, N, d, dtype) != ATTN_OK) return 0;
-  return round256((size_t)B * H * N * sizeof(float));
+  // D and LSE * log2(e), one float32 per query row each.
+  return 2 * round256((size_t)B * H * N * sizeof(float));
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -71,8 +72,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
       !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       !aligned16(workspace))
     return ATTN_ERR_ALIGN;
-  osattn::BwdArgs a{q,  k,  v,  o,  lse, dO,    dq,     dk,    dv,     (float*)workspace,
-                    B,  H,  Hkv, N, d,   scale, causal, dtype, stream};
+  float* dvec = (float*)workspace;
+  float* lse2 = (float*)((char*)workspace + round256((size_t)B * H * N * sizeof(float)));
+  osattn::BwdArgs a{q, k,   v, o, lse,   dO,     dq,    dk,    dv, dvec, lse2,
+                    B, H, Hkv, N, d, scale, causal, dtype, stream};
   hipError_t e = osattn::launch_bwd_preprocess(a);
   if (e == hipSuccess) e = dtype == ATTN_F32 ? osattn::launch_bwd_f32(a) : osattn::launch_bwd_mfma(a);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;

@@ -1,5 +1,5 @@
 // Backward pass of fused attention on bf16/fp16 MFMA (gfx950), plus the
-// D = rowsum(dO * O) preprocess shared with the float32 path.
+// per-row preprocess shared with the float32 path.
 //
 // The backward rebuilds P tile by tile from the saved logsumexp instead of
 // storing it (FlashAttention-2 page, "Recomputation in backward pass"), and uses
@@ -9,27 +9,49 @@
 // dQ = scale * dS K.
 //
 // Kernels:
-//  1. preprocess: D (float32, into the caller's workspace).
-//  2. dK/dV: one workgroup owns 128 keys of one key/value head (32 per wave, K and
-//     V rows resident in registers) and loops over every query head of its GQA
-//     group and every query tile that sees those keys; dK and dV have a single
-//     writer.  S = Q K^T and dP = dO V^T put one key per lane, so P and dS feed
-//     dV^T += dO^T P and dK^T += Q^T dS directly from registers; dO^T and Q^T are
-//     read from LDS with the transpose read.
-//  3. dQ: one workgroup owns 128 query rows and loops over key tiles, recomputing
-//     S and dP (transposed, one query row per lane as in the forward) and forming
-//     dQ^T += K^T dS^T.  No atomics; every output element has one writer.
+//  1. preprocess: D = rowsum(dO * O) and LSE * log2(e), float32, into the
+//     caller's workspace.
+//  2. dK/dV: one workgroup (4 waves, one per SIMD) owns 128 (d = 128) or 256
+//     (d = 64) keys of one key/value head; each wave keeps its 32 or 64 keys of K
+//     and V in registers next to the dK, dV accumulators, and loops over every
+//     query head of its GQA group and every query tile that sees those keys
+//     (single writer).  S = Q K^T and dP = dO V^T put one key per lane, so P and
+//     dS feed dV^T += dO^T P and dK^T += Q^T dS straight from registers.  With 64
+//     keys per wave each Q or dO operand read from LDS feeds two MFMAs.
+//  3. dQ: one workgroup (8 waves, two per SIMD) owns 256 query rows and loops over
+//     key tiles, recomputing S and dP transposed (one query row per lane, as in
+//     the forward) and forming dQ^T += K^T dS^T.  No atomics.
+//
+// Query/dO tiles (dK/dV kernel) and K/V tiles (dQ kernel) go from memory straight
+// into LDS (buffer_load ... lds; rows past N read as zero) in compile-time
+// pipeline stages.  Each tile is read both row-wise (128-bit reads) and
+// transposed (ds_read_b64_tr_b16); one 16-byte-granule XOR swizzle keeps both
+// access patterns free of bank conflicts.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace osattn {
 
+// Granule XOR for row `row` of a [rows][D] 16-bit tile in LDS.  Row-wise reads
+// touch one logical granule in 16 consecutive rows; transposed reads touch 4
+// consecutive rows x 4 consecutive granules.  Bits 2-3 of the XOR separate the 4
+// rows of a transposed read into different 64-byte bank groups, bits 0-1 make the
+// XOR distinct over 16 consecutive rows.
+template <int D>
+__device__ __forceinline__ int bwd_swz(int row) {
+  return D == 128 ? (4 * (row & 3) + ((row >> 2) & 3)) : (4 * ((row >> 1) & 1) + ((row >> 2) & 3));
+}
+
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O) in float32.
+// 1. D = rowsum(dO * O) and LSE * log2(e), float32.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const E* __restrict__ O,
                                                              const E* __restrict__ dO,
+                                                             const float* __restrict__ LSE,
                                                              float* __restrict__ Dv,
+                                                             float* __restrict__ lse2,
                                                              long long rows) {
   constexpr int kEPT = 16 / sizeof(E);   // elements per 16-byte load
   constexpr int kTPR = D / kEPT;          // threads per row (8, 16 or 32)
@@ -56,37 +78,51 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const E* __restrict
   }
 #pragma unroll
   for (int off = kTPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && (threadIdx.x % kTPR) == 0) Dv[row] = acc;
+  if (row < rows && (threadIdx.x % kTPR) == 0) {
+    Dv[row] = acc;
+    if (lse2) lse2[row] = LSE[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // 2. dK / dV.
-template <int D>
+template <int D, int NBUF>
 struct DkdvCfg {
-  static constexpr int kKeys = 128;  // keys per workgroup (32 per wave)
-  static constexpr int kQT = 64;     // query rows per staged tile
-  static constexpr int kStride = D + 8;
-  static constexpr int kTile = kQT * kStride;
-  static constexpr int kChunksPerRow = D / 8;
-  static constexpr int kRowsPerPass = 256 / kChunksPerRow;
-  static constexpr int kPasses = kQT / kRowsPerPass;
+  static constexpr int kNW = 4;                 // waves (one per SIMD)
+  // 32-key blocks per wave: two at d = 64; at d = 128 the K/V fragments and the
+  // dK/dV accumulators of two blocks would not fit in one wave's registers.
+  static constexpr int kKB = D == 64 ? 2 : 1;
+  static constexpr int kKeys = kNW * 32 * kKB;  // keys per workgroup
+  static constexpr int kQT = 64;                // query rows per staged tile
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileElems = kQT * D;
+  static constexpr int kChunks = kQT * kRowBytes / 1024;
+  static constexpr int kCPW = kChunks / kNW;
+  static_assert(kCPW >= 1 && kChunks % kNW == 0, "tile must split evenly over the waves");
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, int NBUF, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                     const float* __restrict__ LSE, const float* __restrict__ Dv,
+                     const float* __restrict__ LSE2, const float* __restrict__ Dv,
                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int H, int Hkv,
                      int N, int n_ktiles, float scale, float scale_log2) {
-  using C = DkdvCfg<D>;
+  using C = DkdvCfg<D, NBUF>;
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_q[2][C::kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_do[2][C::kTile];
-  __shared__ __attribute__((aligned(16))) float lds_lse[2][C::kQT];
-  __shared__ __attribute__((aligned(16))) float lds_d[2][C::kQT];
+  constexpr int KB = C::kKB;
+  static_assert(NBUF == 2 || NBUF == 3, "two or three stages");
+  __shared__ __attribute__((aligned(1024))) uint16_t lq0[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t ld0[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lq1[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t ld1[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lq2[NBUF > 2 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t ld2[NBUF > 2 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(256))) float ll0[C::kQT], lD0[C::kQT];
+  __shared__ __attribute__((aligned(256))) float ll1[C::kQT], lD1[C::kQT];
+  __shared__ __attribute__((aligned(256))) float ll2[C::kQT], lD2[C::kQT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -101,35 +137,34 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int b = bg / Hkv;
   const int n_rep = H / Hkv;
   const int k0 = kt * C::kKeys;
-  const int kw = k0 + 32 * wave;  // first key of this wave
+  const int kw = k0 + 32 * KB * wave;  // first key of this wave
 
-  const uint16_t* Kp = K + (size_t)bg * N * D;
-  const uint16_t* Vp = V + (size_t)bg * N * D;
+  const uint32_t head_bytes = (uint32_t)N * C::kRowBytes;
+  const auto rk = make_rsrc(K + (size_t)bg * N * D, head_bytes);
+  const auto rv = make_rsrc(V + (size_t)bg * N * D, head_bytes);
 
   // K and V rows of this wave (B operands of S = Q K^T and dP = dO V^T).
-  vec8 kf[D / 16], vf[D / 16];
-  {
-    const int key = kw + l32;
+  vec8 kf[KB][D / 16], vf[KB][D / 16];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const uint32_t rowoff = (uint32_t)(kw + 32 * kb + l32) * C::kRowBytes;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-      if (key < N) {
-        xk = *(const u32x4*)(Kp + (size_t)key * D + 16 * c + 8 * hi);
-        xv = *(const u32x4*)(Vp + (size_t)key * D + 16 * c + 8 * hi);
-      }
-      kf[c] = as_vec8<T>(xk);
-      vf[c] = as_vec8<T>(xv);
+      kf[kb][c] = as_vec8<T>(buffer_load16(rk, rowoff + (16 * c + 8 * hi) * 2));
+      vf[kb][c] = as_vec8<T>(buffer_load16(rv, rowoff + (16 * c + 8 * hi) * 2));
     }
   }
 
-  f32x16 dk_acc[D / 32], dv_acc[D / 32];
+  f32x16 dk_acc[KB][D / 32], dv_acc[KB][D / 32];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk_acc[t][r] = 0.f;
-      dv_acc[t][r] = 0.f;
-    }
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk_acc[kb][t][r] = 0.f;
+        dv_acc[kb][t][r] = 0.f;
+      }
 
   // Query tiles that see these keys: all of them, or (causal) from the diagonal on.
   const int qt_first = CAUSAL ? (k0 / C::kQT) : 0;
@@ -137,165 +172,227 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int per_head = n_qt - qt_first;
   const int n_iter = per_head * n_rep;
 
-  const int ld_row = tid / C::kChunksPerRow;
-  const int ld_col = (tid % C::kChunksPerRow) * 8;
-  u32x4 qst[C::kPasses], dst[C::kPasses];
-  float lse_st = 0.f, d_st = 0.f;
-  auto gload = [&](int it) {
+  // LDS-DMA offsets: chunk ch of a tile holds tile row off / kRowBytes, physical
+  // granule pg, i.e. logical granule pg ^ swizzle(row).
+  uint32_t goff[C::kCPW];
+#pragma unroll
+  for (int i = 0; i < C::kCPW; ++i) {
+    const int off = (wave * C::kCPW + i) * 1024 + lane * 16;
+    const int row = off / C::kRowBytes;
+    const int pg = (off % C::kRowBytes) / 16;
+    goff[i] = row * C::kRowBytes + ((pg ^ bwd_swz<D>(row)) * 16);
+  }
+  auto issue = [&](int it, uint16_t* lq, uint16_t* ld, float* ll, float* lD)
+      __attribute__((always_inline)) {
     const int r = it / per_head;
-    const int i0 = (qt_first + it % per_head) * C::kQT;
+    const uint32_t i0 = (uint32_t)(qt_first + it % per_head) * C::kQT;
     const size_t bh = (size_t)b * H + kvh * n_rep + r;
-    const uint16_t* Qp = Q + bh * N * D;
-    const uint16_t* dOp = dO + bh * N * D;
+    const auto rq = make_rsrc(Q + bh * N * D, head_bytes);
+    const auto rd = make_rsrc(dO + bh * N * D, head_bytes);
 #pragma unroll
-    for (int p = 0; p < C::kPasses; ++p) {
-      const int row = i0 + p * C::kRowsPerPass + ld_row;
-      u32x4 zq = {0u, 0u, 0u, 0u}, zd = {0u, 0u, 0u, 0u};
-      if (row < N) {
-        zq = *(const u32x4*)(Qp + (size_t)row * D + ld_col);
-        zd = *(const u32x4*)(dOp + (size_t)row * D + ld_col);
-      }
-      qst[p] = zq;
-      dst[p] = zd;
+    for (int i = 0; i < C::kCPW; ++i) {
+      const int ch = wave * C::kCPW + i;
+      buffer_load16_lds(rq, lq + ch * 512, i0 * C::kRowBytes + goff[i]);
+      buffer_load16_lds(rd, ld + ch * 512, i0 * C::kRowBytes + goff[i]);
     }
-    if (tid < C::kQT) {
-      const int row = i0 + tid;
-      // Rows past the end get P = exp2(-inf) = 0 and D = 0.
-      lse_st = row < N ? LSE[bh * N + row] * kLog2e : INFINITY;
-      d_st = row < N ? Dv[bh * N + row] : 0.f;
+    if (wave == 0) {  // 64 rows x 4 bytes of LSE*log2(e) and D; rows >= N read zero
+      const auto rl = make_rsrc(LSE2 + bh * N, (uint32_t)N * 4);
+      const auto rD = make_rsrc(Dv + bh * N, (uint32_t)N * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)ll, 4,
+                                               (i0 + lane) * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (__attribute__((address_space(3))) void*)lD, 4,
+                                               (i0 + lane) * 4, 0, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < C::kPasses; ++p) {
-      const int row = p * C::kRowsPerPass + ld_row;
-      *(u32x4*)&lds_q[buf][row * C::kStride + ld_col] = qst[p];
-      *(u32x4*)&lds_do[buf][row * C::kStride + ld_col] = dst[p];
-    }
-    if (tid < C::kQT) {
-      lds_lse[buf][tid] = lse_st;
-      lds_d[buf][tid] = d_st;
-    }
-  };
+  // Per-wave outstanding loads of one tile (wave 0 also loads LSE and D).
+  const int loads_per_tile = 2 * C::kCPW + (wave == 0 ? 2 : 0);
+  (void)loads_per_tile;
 
+  // LDS read offsets (bytes in a tile), loop-invariant per lane.
+  //  row-wise (A operand of S and dP): row 32qb + l32, logical granule 2c + hi
+  uint32_t roff[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) roff[c] = l32 * C::kRowBytes + (((2 * c + hi) ^ bwd_swz<D>(l32)) * 16);
+  //  transposed (A operands of dV^T and dK^T): rows 16cq + tr_row (+8), columns
+  //  32t + tr_col .. +3 (see common.h for the lane pattern of the transpose read)
   const int tr_row = 4 * hi + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  if (n_iter > 0) {
-    gload(0);
-    lstore(0);
+  //  The upper half (rows +8) has swizzle bwd_swz(row) ^ 2: granule bit 1, i.e. byte
+  //  bit 5 of the in-row offset, flips.
+  uint32_t toff[D / 32], toff8[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    const int col = 32 * t + tr_col;
+    toff[t] = tr_row * C::kRowBytes + (((col >> 3) ^ bwd_swz<D>(tr_row)) * 16) + (col & 7) * 2;
+    toff8[t] = (tr_row + 8) * C::kRowBytes + (((col >> 3) ^ bwd_swz<D>(tr_row + 8)) * 16) + (col & 7) * 2;
   }
-  __syncthreads();
 
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < n_iter) gload(it + 1);
+  auto compute = [&](int it, const char* qb_, const char* db_, const float* ll, const float* lD)
+      __attribute__((always_inline)) {
     const int i0 = (qt_first + it % per_head) * C::kQT;
 #pragma unroll
     for (int qb = 0; qb < C::kQT / 32; ++qb) {
       const int qs = i0 + 32 * qb;
       if (CAUSAL && qs + 31 < kw) continue;  // every key of this wave is after every row
-      // S = Q K^T and dP = dO V^T (result: lane = key, register = query row).
-      f32x16 s, dp;
+      // S = Q K^T, dP = dO V^T (lane = key, register r = query row 8(r/4)+4hi+r%4)
+      f32x16 s[KB], dp[KB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[kb][r] = 0.f;
+          dp[kb][r] = 0.f;
+        }
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        const u32x4 aq = *(const u32x4*)&lds_q[buf][(32 * qb + l32) * C::kStride + 16 * c + 8 * hi];
-        const u32x4 ad = *(const u32x4*)&lds_do[buf][(32 * qb + l32) * C::kStride + 16 * c + 8 * hi];
-        s = M::mma32(as_vec8<T>(aq), kf[c], s);
-        dp = M::mma32(as_vec8<T>(ad), vf[c], dp);
-      }
-      const int key = kw + l32;
-      float p[16], ds[16];
+        const u32x4 aq = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
+        const u32x4 ad = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ql = 32 * qb + 8 * g + 4 * hi;  // local query row of register 4g
-        const f32x4 lse4 = *(const f32x4*)&lds_lse[buf][ql];
-        const f32x4 d4 = *(const f32x4*)&lds_d[buf][ql];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pv = fast_exp2(fmaf(s[r], scale_log2, -lse4[e]));
-          if (CAUSAL && key > i0 + ql + e) pv = 0.f;
-          p[r] = pv;
-          ds[r] = pv * (dp[r] - d4[e]);
+        for (int kb = 0; kb < KB; ++kb) {
+          s[kb] = M::mma32(as_vec8<T>(aq), kf[kb][c], s[kb]);
+          dp[kb] = M::mma32(as_vec8<T>(ad), vf[kb][c], dp[kb]);
         }
       }
-      // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over the 32 query rows)
+      // P = exp2(S*c - LSE*log2e) (0 where masked), dS = P * (dP - D)
 #pragma unroll
       for (int cq = 0; cq < 2; ++cq) {
-        const vec8 pp = pack8<T>(p + 8 * cq);
-        const vec8 ps = pack8<T>(ds + 8 * cq);
-        const int row = 32 * qb + 16 * cq + tr_row;
+        vec8 pp[KB], ps[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int key = kw + 32 * kb + l32;
+          float p8[8], d8[8];
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const int ql = 32 * qb + 16 * cq + 8 * g2 + 4 * hi;  // local row of register 8cq+4g2
+            const f32x4 lse4 = *(const f32x4*)&ll[ql];
+            const f32x4 d4 = *(const f32x4*)&lD[ql];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * cq + 4 * g2 + e;
+              float pv = fast_exp2(fmaf(s[kb][r], scale_log2, -lse4[e]));
+              if (CAUSAL && key > i0 + ql + e) pv = 0.f;
+              p8[4 * g2 + e] = pv;
+              d8[4 * g2 + e] = pv * (dp[kb][r] - d4[e]);
+            }
+          }
+          pp[kb] = pack8<T>(p8);
+          ps[kb] = pack8<T>(d8);
+        }
+        // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over these 16 query rows)
+        const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
-          const uint16_t* db = &lds_do[buf][row * C::kStride + 32 * t + tr_col];
-          const uint16_t* qb_ = &lds_q[buf][row * C::kStride + 32 * t + tr_col];
-          const vec8 adt = join8<T>(lds_read_tr4(db), lds_read_tr4(db + 8 * C::kStride));
-          const vec8 aqt = join8<T>(lds_read_tr4(qb_), lds_read_tr4(qb_ + 8 * C::kStride));
-          dv_acc[t] = M::mma32(adt, pp, dv_acc[t]);
-          dk_acc[t] = M::mma32(aqt, ps, dk_acc[t]);
+          const char* dt = db_ + rowb + toff[t];
+          const char* qt = qb_ + rowb + toff[t];
+          const vec8 adt = join8<T>(lds_read_tr4(dt), lds_read_tr4(db_ + rowb + toff8[t]));
+          const vec8 aqt = join8<T>(lds_read_tr4(qt), lds_read_tr4(qb_ + rowb + toff8[t]));
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            dv_acc[kb][t] = M::mma32(adt, pp[kb], dv_acc[kb][t]);
+            dk_acc[kb][t] = M::mma32(aqt, ps[kb], dk_acc[kb][t]);
+          }
         }
       }
     }
-    if (it + 1 < n_iter) lstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  auto stage = [&](auto sc, auto fn) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) fn(lq0, ld0, ll0, lD0);
+    else if constexpr (S == 1) fn(lq1, ld1, ll1, lD1);
+    else fn(lq2, ld2, ll2, lD2);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if (0 < n_iter) stage(I0{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd) { issue(0, a, d, l, dd); });
+  if (NBUF > 2 && 1 < n_iter)
+    stage(I1{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd) { issue(1, a, d, l, dd); });
+
+  auto step = [&](auto sc, int it) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
+    constexpr int SN = (S + NBUF - 1) % NBUF;  // receives tile it + NBUF - 1
+    // Tile `it` has landed once at most the next tile's loads are outstanding.
+    if (NBUF > 2 && it + 1 < n_iter) {
+      if (wave == 0) wait_vmcnt<2 * C::kCPW + 2>();
+      else wait_vmcnt<2 * C::kCPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_barrier();
+    if (it + NBUF - 1 < n_iter)
+      stage(std::integral_constant<int, SN>{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd) {
+        issue(it + NBUF - 1, a, d, l, dd);
+      });
+    stage(sc, [&](uint16_t* a, uint16_t* d, float* l, float* dd) {
+      compute(it, (const char*)a, (const char*)d, l, dd);
+    });
+  };
+  for (int it = 0; it < n_iter; it += NBUF) {
+    step(I0{}, it);
+    if (it + 1 < n_iter) step(I1{}, it + 1);
+    if constexpr (NBUF > 2)
+      if (it + 2 < n_iter) step(std::integral_constant<int, 2>{}, it + 2);
   }
 
   // Store: lane = key, register r of tile t = column 32t + 8(r/4) + 4hi + r%4.
-  const int key = kw + l32;
-  if (key < N) {
-    uint16_t* dkp = dK + ((size_t)bg * N + key) * D;
-    uint16_t* dvp = dV + ((size_t)bg * N + key) * D;
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t)
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = kw + 32 * kb + l32;
+    if (key < N) {
+      uint16_t* dkp = dK + ((size_t)bg * N + key) * D;
+      uint16_t* dvp = dV + ((size_t)bg * N + key) * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 wk, wv;
-        wk[0] = (uint32_t)to_bits<T>(dk_acc[t][4 * g + 0] * scale) |
-                ((uint32_t)to_bits<T>(dk_acc[t][4 * g + 1] * scale) << 16);
-        wk[1] = (uint32_t)to_bits<T>(dk_acc[t][4 * g + 2] * scale) |
-                ((uint32_t)to_bits<T>(dk_acc[t][4 * g + 3] * scale) << 16);
-        wv[0] = (uint32_t)to_bits<T>(dv_acc[t][4 * g + 0]) |
-                ((uint32_t)to_bits<T>(dv_acc[t][4 * g + 1]) << 16);
-        wv[1] = (uint32_t)to_bits<T>(dv_acc[t][4 * g + 2]) |
-                ((uint32_t)to_bits<T>(dv_acc[t][4 * g + 3]) << 16);
-        *(u32x2*)(dkp + 32 * t + 8 * g + 4 * hi) = wk;
-        *(u32x2*)(dvp + 32 * t + 8 * g + 4 * hi) = wv;
-      }
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 wk, wv;
+          wk[0] = (uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 0] * scale) |
+                  ((uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 1] * scale) << 16);
+          wk[1] = (uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 2] * scale) |
+                  ((uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 3] * scale) << 16);
+          wv[0] = (uint32_t)to_bits<T>(dv_acc[kb][t][4 * g + 0]) |
+                  ((uint32_t)to_bits<T>(dv_acc[kb][t][4 * g + 1]) << 16);
+          wv[1] = (uint32_t)to_bits<T>(dv_acc[kb][t][4 * g + 2]) |
+                  ((uint32_t)to_bits<T>(dv_acc[kb][t][4 * g + 3]) << 16);
+          *(u32x2*)(dkp + 32 * t + 8 * g + 4 * hi) = wk;
+          *(u32x2*)(dvp + 32 * t + 8 * g + 4 * hi) = wv;
+        }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // 3. dQ.
-template <int D>
+template <int D, int NBUF>
 struct DqCfg {
-  static constexpr int kRows = 128;  // query rows per workgroup (32 per wave)
-  static constexpr int kBC = 64;     // keys per staged tile
-  static constexpr int kStride = D + 8;
-  static constexpr int kTile = kBC * kStride;
-  static constexpr int kChunksPerRow = D / 8;
-  static constexpr int kRowsPerPass = 256 / kChunksPerRow;
-  static constexpr int kPasses = kBC / kRowsPerPass;
+  static constexpr int kNW = 8;              // waves (two per SIMD)
+  static constexpr int kRows = kNW * 32;     // query rows per workgroup
+  static constexpr int kBC = 64;             // keys per staged tile
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileElems = kBC * D;
+  static constexpr int kChunks = kBC * kRowBytes / 1024;
+  static constexpr int kCPW = kChunks / kNW;
+  static_assert(kCPW >= 1 && kChunks % kNW == 0, "tile must split evenly over the waves");
 };
 
-template <typename T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+template <typename T, int D, int NBUF, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                   const float* __restrict__ LSE, const float* __restrict__ Dv,
+                   const float* __restrict__ LSE2, const float* __restrict__ Dv,
                    uint16_t* __restrict__ dQ, int H, int Hkv, int N, int n_qtiles, float scale,
                    float scale_log2) {
-  using C = DqCfg<D>;
+  using C = DqCfg<D, NBUF>;
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][C::kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][C::kTile];
+  static_assert(NBUF == 2 || NBUF == 3, "two or three stages");
+  __shared__ __attribute__((aligned(1024))) uint16_t lk0[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv0[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lk1[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv1[C::kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lk2[NBUF > 2 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv2[NBUF > 2 ? C::kTileElems : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -306,7 +403,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int qt = L % n_qtiles;
   const int bh = L / n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
   const int h = bh % H;
   const int b = bh / H;
   const int kvh = h / (H / Hkv);
@@ -314,21 +411,23 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int wrow0 = q0 + 32 * wave;
   const int row = wrow0 + l32;
 
-  const uint16_t* Kp = K + (size_t)(b * Hkv + kvh) * N * D;
-  const uint16_t* Vp = V + (size_t)(b * Hkv + kvh) * N * D;
+  const uint32_t head_bytes = (uint32_t)N * C::kRowBytes;
+  const auto rq = make_rsrc(Q + (size_t)bh * N * D, head_bytes);
+  const auto rdo = make_rsrc(dO + (size_t)bh * N * D, head_bytes);
+  const auto rk = make_rsrc(K + (size_t)(b * Hkv + kvh) * N * D, head_bytes);
+  const auto rv = make_rsrc(V + (size_t)(b * Hkv + kvh) * N * D, head_bytes);
 
+  // Q and dO rows of this lane (B operands of S^T = K Q^T and dP^T = V dO^T).
   vec8 qf[D / 16], df[D / 16];
+  {
+    const uint32_t rowoff = (uint32_t)row * C::kRowBytes;
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    u32x4 xq = {0u, 0u, 0u, 0u}, xd = {0u, 0u, 0u, 0u};
-    if (row < N) {
-      xq = *(const u32x4*)(Q + ((size_t)bh * N + row) * D + 16 * c + 8 * hi);
-      xd = *(const u32x4*)(dO + ((size_t)bh * N + row) * D + 16 * c + 8 * hi);
+    for (int c = 0; c < D / 16; ++c) {
+      qf[c] = as_vec8<T>(buffer_load16(rq, rowoff + (16 * c + 8 * hi) * 2));
+      df[c] = as_vec8<T>(buffer_load16(rdo, rowoff + (16 * c + 8 * hi) * 2));
     }
-    qf[c] = as_vec8<T>(xq);
-    df[c] = as_vec8<T>(xd);
   }
-  const float lse2 = row < N ? LSE[(size_t)bh * N + row] * kLog2e : INFINITY;
+  const float lse2 = row < N ? LSE2[(size_t)bh * N + row] : 0.f;
   const float drow = row < N ? Dv[(size_t)bh * N + row] : 0.f;
 
   f32x16 acc[D / 32];
@@ -340,90 +439,115 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   int n_kt = (N + C::kBC - 1) / C::kBC;
   if (CAUSAL) n_kt = min(n_kt, (q0 + C::kRows + C::kBC - 1) / C::kBC);
 
-  const int ld_row = tid / C::kChunksPerRow;
-  const int ld_col = (tid % C::kChunksPerRow) * 8;
-  u32x4 kst[C::kPasses], vst[C::kPasses];
-  auto gload = [&](int kt) {
+  uint32_t goff[C::kCPW];
 #pragma unroll
-    for (int p = 0; p < C::kPasses; ++p) {
-      const int r = kt * C::kBC + p * C::kRowsPerPass + ld_row;
-      u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
-      if (r < N) {
-        zk = *(const u32x4*)(Kp + (size_t)r * D + ld_col);
-        zv = *(const u32x4*)(Vp + (size_t)r * D + ld_col);
-      }
-      kst[p] = zk;
-      vst[p] = zv;
-    }
-  };
-  auto lstore = [&](int buf) {
+  for (int i = 0; i < C::kCPW; ++i) {
+    const int off = (wave * C::kCPW + i) * 1024 + lane * 16;
+    const int r = off / C::kRowBytes;
+    const int pg = (off % C::kRowBytes) / 16;
+    goff[i] = r * C::kRowBytes + ((pg ^ bwd_swz<D>(r)) * 16);
+  }
+  auto issue = [&](int kt, uint16_t* lk, uint16_t* lv) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)kt * C::kBC * C::kRowBytes;
 #pragma unroll
-    for (int p = 0; p < C::kPasses; ++p) {
-      const int r = p * C::kRowsPerPass + ld_row;
-      *(u32x4*)&lds_k[buf][r * C::kStride + ld_col] = kst[p];
-      *(u32x4*)&lds_v[buf][r * C::kStride + ld_col] = vst[p];
+    for (int i = 0; i < C::kCPW; ++i) {
+      const int ch = wave * C::kCPW + i;
+      buffer_load16_lds(rk, lk + ch * 512, base + goff[i]);
+      buffer_load16_lds(rv, lv + ch * 512, base + goff[i]);
     }
   };
 
+  uint32_t roff[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) roff[c] = l32 * C::kRowBytes + (((2 * c + hi) ^ bwd_swz<D>(l32)) * 16);
   const int tr_row = 4 * hi + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  //  The upper half (rows +8) has swizzle bwd_swz(row) ^ 2: granule bit 1, i.e. byte
+  //  bit 5 of the in-row offset, flips.
+  uint32_t toff[D / 32], toff8[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    const int col = 32 * t + tr_col;
+    toff[t] = tr_row * C::kRowBytes + (((col >> 3) ^ bwd_swz<D>(tr_row)) * 16) + (col & 7) * 2;
+    toff8[t] = (tr_row + 8) * C::kRowBytes + (((col >> 3) ^ bwd_swz<D>(tr_row + 8)) * 16) + (col & 7) * 2;
+  }
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) gload(kt + 1);
+  auto compute = [&](int kt, const char* kbase, const char* vbase) __attribute__((always_inline)) {
     const int k0 = kt * C::kBC;
-    const bool active = !CAUSAL || (k0 <= wrow0 + 31);
-    if (active) {
+    if (CAUSAL && k0 > wrow0 + 31) return;  // every key of the tile is after every row
+    const bool need_mask = (k0 + C::kBC > N) || (CAUSAL && k0 + C::kBC - 1 > wrow0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
       // S^T = K Q^T, dP^T = V dO^T (lane = query row, register = key)
-      f32x16 s[2], dp[2];
+      f32x16 s, dp;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[kb][r] = 0.f;
-          dp[kb][r] = 0.f;
-        }
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 ak = *(const u32x4*)&lds_k[buf][(kb * 32 + l32) * C::kStride + 16 * c + 8 * hi];
-          const u32x4 av = *(const u32x4*)&lds_v[buf][(kb * 32 + l32) * C::kStride + 16 * c + 8 * hi];
-          s[kb] = M::mma32(as_vec8<T>(ak), qf[c], s[kb]);
-          dp[kb] = M::mma32(as_vec8<T>(av), df[c], dp[kb]);
-        }
+        const u32x4 ak = *(const u32x4*)(kbase + kb * 32 * C::kRowBytes + roff[c]);
+        const u32x4 av = *(const u32x4*)(vbase + kb * 32 * C::kRowBytes + roff[c]);
+        s = M::mma32(as_vec8<T>(ak), qf[c], s);
+        dp = M::mma32(as_vec8<T>(av), df[c], dp);
       }
-      const bool need_mask = (k0 + C::kBC > N) || (CAUSAL && k0 + C::kBC - 1 > wrow0);
-      float dsv[2][16];
+      float dsv[16];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = fast_exp2(fmaf(s[kb][r], scale_log2, -lse2));
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= N || (CAUSAL && key > row)) pv = 0.f;
-          }
-          dsv[kb][r] = pv * (dp[kb][r] - drow);
+      for (int r = 0; r < 16; ++r) {
+        float pv = fast_exp2(fmaf(s[r], scale_log2, -lse2));
+        if (need_mask) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= N || (CAUSAL && key > row)) pv = 0.f;
         }
-      // dQ^T += K^T dS^T
+        dsv[r] = pv * (dp[r] - drow);
+      }
+      // dQ^T += K^T dS^T (reduction over the 32 keys of this block, 16 at a time)
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const vec8 ps = pack8<T>(&dsv[c4 >> 1][8 * (c4 & 1)]);
+      for (int cc = 0; cc < 2; ++cc) {
+        const vec8 ps = pack8<T>(&dsv[8 * cc]);
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
-          const uint16_t* kb_ = &lds_k[buf][(16 * c4 + tr_row) * C::kStride + 32 * t + tr_col];
-          const vec8 a = join8<T>(lds_read_tr4(kb_), lds_read_tr4(kb_ + 8 * C::kStride));
+          const int rowb = (32 * kb + 16 * cc) * C::kRowBytes;
+          const vec8 a = join8<T>(lds_read_tr4(kbase + rowb + toff[t]), lds_read_tr4(kbase + rowb + toff8[t]));
           acc[t] = M::mma32(a, ps, acc[t]);
         }
       }
     }
-    if (kt + 1 < n_kt) lstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  auto stage_k = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return lk0;
+    else if constexpr (S == 1) return lk1;
+    else return lk2;
+  };
+  auto stage_v = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return lv0;
+    else if constexpr (S == 1) return lv1;
+    else return lv2;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if (0 < n_kt) issue(0, stage_k(I0{}), stage_v(I0{}));
+  if (NBUF > 2 && 1 < n_kt) issue(1, stage_k(I1{}), stage_v(I1{}));
+
+  auto step = [&](auto sc, int kt) __attribute__((always_inline)) {
+    constexpr int SN = (decltype(sc)::value + NBUF - 1) % NBUF;
+    if (NBUF > 2 && kt + 1 < n_kt) wait_vmcnt<2 * C::kCPW>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    if (kt + NBUF - 1 < n_kt)
+      issue(kt + NBUF - 1, stage_k(std::integral_constant<int, SN>{}),
+            stage_v(std::integral_constant<int, SN>{}));
+    compute(kt, (const char*)stage_k(sc), (const char*)stage_v(sc));
+  };
+  for (int kt = 0; kt < n_kt; kt += NBUF) {
+    step(I0{}, kt);
+    if (kt + 1 < n_kt) step(I1{}, kt + 1);
+    if constexpr (NBUF > 2)
+      if (kt + 2 < n_kt) step(std::integral_constant<int, 2>{}, kt + 2);
   }
 
   if (row < N) {
@@ -449,7 +573,8 @@ static hipError_t preprocess_t(const BwdArgs& a) {
   const long long rows = (long long)a.B * a.H * a.N;
   const long long blocks = (rows + (256 / kTPR) - 1) / (256 / kTPR);
   hipLaunchKernelGGL((bwd_preprocess_kernel<E, D>), dim3((unsigned)blocks), dim3(256), 0,
-                     (hipStream_t)a.stream, (const E*)a.o, (const E*)a.dO, a.dvec, rows);
+                     (hipStream_t)a.stream, (const E*)a.o, (const E*)a.dO, a.lse, a.dvec, a.lse2,
+                     rows);
   return hipGetLastError();
 }
 
@@ -459,27 +584,32 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a) {
   return a.d == 64 ? preprocess_t<__bf16, 64>(a) : preprocess_t<__bf16, 128>(a);
 }
 
+#ifndef OSATTN_BWD_NBUF
+#define OSATTN_BWD_NBUF 3
+#endif
+
 template <typename T, int D, bool CAUSAL>
 static hipError_t bwd_t(const BwdArgs& a) {
+  constexpr int NB = OSATTN_BWD_NBUF;
   const float sl2 = a.scale * kLog2e;
   {
-    using C = DkdvCfg<D>;
+    using C = DkdvCfg<D, NB>;
     const int n_kt = (a.N + C::kKeys - 1) / C::kKeys;
     const long long blocks = (long long)n_kt * a.B * a.Hkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NB, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0,
                        (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse, a.dvec,
+                       (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse2, a.dvec,
                        (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.Hkv, a.N, n_kt, a.scale, sl2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
-    using C = DqCfg<D>;
+    using C = DqCfg<D, NB>;
     const int n_qt = (a.N + C::kRows - 1) / C::kRows;
     const long long blocks = (long long)n_qt * a.B * a.H;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, NB, CAUSAL>), dim3((unsigned)blocks), dim3(512), 0,
                        (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse, a.dvec,
+                       (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse2, a.dvec,
                        (uint16_t*)a.dq, a.H, a.Hkv, a.N, n_qt, a.scale, sl2);
   }
   return hipGetLastError();

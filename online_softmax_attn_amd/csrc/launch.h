@@ -31,6 +31,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dvec;  // workspace: D = rowsum(dO * O), [B][H][N] float32
+  float* lse2;  // workspace: LSE * log2(e), [B][H][N] float32
   int B, H, Hkv, N, d;
   float scale;
   int causal;

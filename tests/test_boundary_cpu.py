@@ -114,10 +114,11 @@ def test_bwd_rejects(kw, code):
 
 def test_workspace_bytes():
     f = osa.library().attn_bwd_workspace_bytes
-    assert f(1, 1, 1, 1, 64, 0) == 256
+    assert f(1, 1, 1, 1, 64, 0) == 2 * 256
     n = 4 * 16 * 8192
-    assert f(4, 16, 16, 8192, 128, 2) == n * 4
-    assert f(1, 32, 8, 16384, 128, 2) == 32 * 16384 * 4
+    assert f(4, 16, 16, 8192, 128, 2) == 2 * n * 4
+    assert f(1, 32, 8, 16384, 128, 2) == 2 * 32 * 16384 * 4
+    assert f(1, 3, 3, 5, 64, 1) == 2 * 256
     assert f(1, 3, 2, 8, 64, 2) == 0          # H not a multiple of Hkv
     assert f(1, 1, 1, 8, 80, 2) == 0          # unsupported d
     assert f(0, 1, 1, 8, 64, 2) == 0
