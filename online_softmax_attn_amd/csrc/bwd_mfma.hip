@@ -227,32 +227,40 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     toff8[t] = (tr_row + 8) * C::kRowBytes + (((col >> 3) ^ bwd_swz<D>(tr_row + 8)) * 16) + (col & 7) * 2;
   }
 
-  auto compute = [&](int it, const char* qb_, const char* db_, const float* ll, const float* lD)
-      __attribute__((always_inline)) {
-    const int i0 = (qt_first + it % per_head) * C::kQT;
+  // One staged tile of 64 query rows = two 32-row blocks.  The scores and dP of
+  // both blocks are issued first; the softmax-JVP arithmetic of block 0 then
+  // overlaps the MFMAs of block 1 and the dV/dK MFMAs of block 0 overlap the
+  // arithmetic of block 1.  Everything is one basic block (masking is a
+  // compile-time variant chosen per tile) so the scheduler can interleave.
+  auto compute_tile = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
+                          const float* lD) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    constexpr int NQB = C::kQT / 32;
+    // S = Q K^T, dP = dO V^T (lane = key, register r = query row 8(r/4)+4hi+r%4)
+    f32x16 s[NQB][KB], dp[NQB][KB];
 #pragma unroll
-    for (int qb = 0; qb < C::kQT / 32; ++qb) {
-      const int qs = i0 + 32 * qb;
-      if (CAUSAL && qs + 31 < kw) continue;  // every key of this wave is after every row
-      // S = Q K^T, dP = dO V^T (lane = key, register r = query row 8(r/4)+4hi+r%4)
-      f32x16 s[KB], dp[KB];
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          s[kb][r] = 0.f;
-          dp[kb][r] = 0.f;
+          s[qb][kb][r] = 0.f;
+          dp[qb][kb][r] = 0.f;
         }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         const u32x4 aq = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
         const u32x4 ad = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          s[kb] = M::mma32(as_vec8<T>(aq), kf[kb][c], s[kb]);
-          dp[kb] = M::mma32(as_vec8<T>(ad), vf[kb][c], dp[kb]);
+          s[qb][kb] = M::mma32(as_vec8<T>(aq), kf[kb][c], s[qb][kb]);
+          dp[qb][kb] = M::mma32(as_vec8<T>(ad), vf[kb][c], dp[qb][kb]);
         }
       }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
       // P = exp2(S*c - LSE*log2e) (0 where masked), dS = P * (dP - D)
 #pragma unroll
       for (int cq = 0; cq < 2; ++cq) {
@@ -269,10 +277,10 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 8 * cq + 4 * g2 + e;
-              float pv = fast_exp2(fmaf(s[kb][r], scale_log2, -lse4[e]));
-              if (CAUSAL && key > i0 + ql + e) pv = 0.f;
+              float pv = fast_exp2(fmaf(s[qb][kb][r], scale_log2, -lse4[e]));
+              if (MASK && key > i0 + ql + e) pv = 0.f;
               p8[4 * g2 + e] = pv;
-              d8[4 * g2 + e] = pv * (dp[kb][r] - d4[e]);
+              d8[4 * g2 + e] = pv * (dp[qb][kb][r] - d4[e]);
             }
           }
           pp[kb] = pack8<T>(p8);
@@ -282,10 +290,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
-          const char* dt = db_ + rowb + toff[t];
-          const char* qt = qb_ + rowb + toff[t];
-          const vec8 adt = join8<T>(lds_read_tr4(dt), lds_read_tr4(db_ + rowb + toff8[t]));
-          const vec8 aqt = join8<T>(lds_read_tr4(qt), lds_read_tr4(qb_ + rowb + toff8[t]));
+          const vec8 adt = join8<T>(lds_read_tr4(db_ + rowb + toff[t]), lds_read_tr4(db_ + rowb + toff8[t]));
+          const vec8 aqt = join8<T>(lds_read_tr4(qb_ + rowb + toff[t]), lds_read_tr4(qb_ + rowb + toff8[t]));
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
             dv_acc[kb][t] = M::mma32(adt, pp[kb], dv_acc[kb][t]);
@@ -294,6 +300,16 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         }
       }
     }
+  };
+  auto compute = [&](int it, const char* qb_, const char* db_, const float* ll, const float* lD)
+      __attribute__((always_inline)) {
+    const int i0 = (qt_first + it % per_head) * C::kQT;
+    if (CAUSAL && i0 + C::kQT - 1 < kw) return;  // every key of this wave is after every row
+    // Causal: only tiles whose first row precedes this wave's last key need the mask.
+    if (CAUSAL && i0 < kw + 32 * KB - 1)
+      compute_tile(std::true_type{}, i0, qb_, db_, ll, lD);
+    else
+      compute_tile(std::false_type{}, i0, qb_, db_, ll, lD);
   };
 
   auto stage = [&](auto sc, auto fn) __attribute__((always_inline)) {

@@ -44,10 +44,10 @@ struct FwdSwizzle {
   static __device__ __forceinline__ int v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 };
 
-template <int D, int NW, int QB, int NBUF>
+template <int D, int NW, int QB, int NBUF, int BC>
 struct FwdCfg {
   static constexpr int kBR = NW * 32 * QB;     // query rows per workgroup
-  static constexpr int kBC = 64;               // keys per tile
+  static constexpr int kBC = BC;               // keys per tile (64 or 128)
   static constexpr int kRowBytes = D * 2;
   static constexpr int kTileElems = kBC * D;   // one K or V tile (16-bit elements)
   static constexpr int kChunks = kBC * kRowBytes / 1024;  // 1 KB LDS-DMA chunks per tile
@@ -55,29 +55,27 @@ struct FwdCfg {
   static_assert(kCPW >= 1 && kChunks % NW == 0, "tile must split evenly over the waves");
 };
 
-template <typename T, int D, int NW, int QB, int NBUF, bool CAUSAL>
+template <typename T, int D, int NW, int QB, int NBUF, int BC, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                      float* __restrict__ LSE, int H, int Hkv, int N, int n_qtiles,
                      float scale_log2) {
-  using C = FwdCfg<D, NW, QB, NBUF>;
+  using C = FwdCfg<D, NW, QB, NBUF, BC>;
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
   using Swz = FwdSwizzle<D>;
   // One array per pipeline stage: with the stage known at compile time, the
   // compiler can tell that reads of one stage do not alias the DMA writes still in
   // flight into the others, and inserts no wait for them.
-  static_assert(NBUF == 3 || NBUF == 4, "three or four stages");
+  static_assert(NBUF == 2 || NBUF == 3, "two or three stages");
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[C::kTileElems];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_k2[C::kTileElems];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_v2[C::kTileElems];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_k3[NBUF > 3 ? C::kTileElems : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_v3[NBUF > 3 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k2[NBUF > 2 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v2[NBUF > 2 ? C::kTileElems : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -135,22 +133,6 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
   };
 
-  // Compile-time stage -> LDS buffers.
-  auto stage_k = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
-    constexpr int S = decltype(sc)::value;
-    if constexpr (S == 0) return lds_k0;
-    else if constexpr (S == 1) return lds_k1;
-    else if constexpr (S == 2) return lds_k2;
-    else return lds_k3;
-  };
-  auto stage_v = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
-    constexpr int S = decltype(sc)::value;
-    if constexpr (S == 0) return lds_v0;
-    else if constexpr (S == 1) return lds_v1;
-    else if constexpr (S == 2) return lds_v2;
-    else return lds_v3;
-  };
-
   // LDS read offsets (bytes within a tile), loop-invariant per lane.
   //  K (A operand of S^T): row kb*32 + l32, logical granule 2c + hi.
   uint32_t koff[D / 16];
@@ -184,87 +166,57 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     l_run[qb] = 0.f;
   }
 
-  // ---- building blocks of one tile ------------------------------------------------
-  // step 1: S^T = K_j Q_i^T from the K tile at kbase (16 MFMAs per query block).
-  auto scores = [&](const char* kbase, f32x16 (&sc)[QB][2]) __attribute__((always_inline)) {
+  auto compute = [&](int kt, const char* kbase, const char* vbase) __attribute__((always_inline)) {
+    const int k0 = kt * C::kBC;
+    const bool active = !CAUSAL || (k0 <= wrow0 + 32 * QB - 1);
+    if (!active) return;
+
+    // ---- step 1: S^T = K_j Q_i^T -------------------------------------------------
+    constexpr int KB = BC / 32;  // 32-key blocks per tile
+    f32x16 s[QB][KB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[qb][kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         const u32x4 a = *(const u32x4*)(kbase + kb * 32 * C::kRowBytes + koff[c]);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = M::mma32(as_vec8<T>(a), qf[qb][c], sc[qb][kb]);
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = M::mma32(as_vec8<T>(a), qf[qb][c], s[qb][kb]);
       }
     }
-  };
-  // Causal / ragged-tail mask of the tile starting at key k0.
-  auto mask = [&](f32x16 (&sc)[QB][2], int k0) __attribute__((always_inline)) {
+    // ---- causal / ragged-tail mask (only on tiles that need it) ------------------------
+    const bool need_mask = (k0 + C::kBC > N) || (CAUSAL && k0 + C::kBC - 1 > wrow0);
+    if (need_mask) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int row = wrow0 + 32 * qb + l32;
+      for (int qb = 0; qb < QB; ++qb) {
+        const int row = wrow0 + 32 * qb + l32;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= N || (CAUSAL && key > row)) sc[qb][kb][r] = -INFINITY;
-        }
-    }
-  };
-  // step 2: row max of a tile (in log2 units of the scaled scores).
-  auto tile_max = [&](f32x16 (&sc)[QB][2], float (&mt)[QB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = fmaxf(sc[qb][0][0], sc[qb][0][1]);
-#pragma unroll
-      for (int i = 2; i < 32; i += 2)
-        mx = __builtin_fmaxf(mx, __builtin_fmaxf(sc[qb][i >> 4][i & 15], sc[qb][i >> 4][(i & 15) + 1]));
-      mt[qb] = wave_xor32_max(mx) * scale_log2;
-    }
-  };
-  // steps 2-3: P = exp2(S*c - m) rounded to the MFMA type; l += rowsum(rounded P).
-  auto probs = [&](f32x16 (&sc)[QB][2], vec8 (&pf)[QB][4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float neg_m = -m_run[qb];
-      float part = 0.f;
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        float pv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(sc[qb][c4 >> 1][8 * (c4 & 1) + j], scale_log2, neg_m));
-        pf[qb][c4] = pack8<T>(pv);
-        part = sum8<T>(pf[qb][c4], part);
-      }
-      l_run[qb] += part;
-    }
-  };
-  // step 5: O^T += V_j^T P^T from the V tile at vbase (16 MFMAs per query block);
-  // consecutive MFMAs go to different accumulators.
-  auto pv = [&](const char* vbase, vec8 (&pf)[QB][4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        const char* vb = vbase + 16 * c4 * C::kRowBytes + voff[t];
-        const vec8 a = join8<T>(lds_read_tr4(vb), lds_read_tr4(vb + 8 * C::kRowBytes));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb][t] = M::mma32(a, pf[qb][c4], acc[qb][t]);
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key >= N || (CAUSAL && key > row)) s[qb][kb][r] = -INFINITY;
+          }
       }
     }
-  };
-  // Lazy move of the reference max (step 4): only when some row's tile max exceeds
-  // it by more than 8; Ot and l are rescaled by exp2(m_old - m_new).
-  auto update_max = [&](float (&mt)[QB]) __attribute__((always_inline)) {
+    // ---- step 2/4: row max, lazy move of the reference max --------------------------
+    float mt[QB];
     bool grow = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) grow |= mt[qb] > m_run[qb] + 8.0f;
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
+      mt[qb] = wave_xor32_max(mx) * scale_log2;
+      grow |= mt[qb] > m_run[qb] + 8.0f;
+    }
     if (__any(grow)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -278,78 +230,58 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           for (int r = 0; r < 16; ++r) acc[qb][t][r] *= alpha;
       }
     }
-  };
-  auto active = [&](int kt) __attribute__((always_inline)) {
-    return !CAUSAL || (kt * C::kBC <= wrow0 + 32 * QB - 1);
-  };
-  auto needs_mask = [&](int kt) __attribute__((always_inline)) {
-    const int k0 = kt * C::kBC;
-    return (k0 + C::kBC > N) || (CAUSAL && k0 + C::kBC - 1 > wrow0);
+    // ---- step 2/3: P = exp2(S*c - m), row sums of the rounded P -----------------------
+    vec8 pf[QB][2 * KB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float neg_m = -m_run[qb];
+      float part = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < 2 * KB; ++c4) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(s[qb][c4 >> 1][8 * (c4 & 1) + j], scale_log2, neg_m));
+        pf[qb][c4] = pack8<T>(pv);
+        part = sum8<T>(pf[qb][c4], part);
+      }
+      l_run[qb] += part;
+    }
+    // ---- step 5: O^T += V_j^T P^T ---------------------------------------------------
+#pragma unroll
+    for (int c4 = 0; c4 < 2 * KB; ++c4) {
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        const char* vb = vbase + 16 * c4 * C::kRowBytes + voff[t];
+        const vec8 a = join8<T>(lds_read_tr4(vb), lds_read_tr4(vb + 8 * C::kRowBytes));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][t] = M::mma32(a, pf[qb][c4], acc[qb][t]);
+      }
+    }
   };
 
-  // ---- software pipeline ----------------------------------------------------------
-  // Iteration kt holds tile kt (its scores s_cur already computed) and tile kt+1 in
-  // LDS; it computes S(kt+1) on the matrix cores while the vector units turn S(kt)
-  // into probabilities, then O += V(kt)^T P(kt) and the row max of S(kt+1).  All of
-  // that is one basic block, so the instruction scheduler interleaves MFMA and VALU
-  // work of the same wave.  Loads run NBUF-2 tiles ahead of S.
-  auto wait_tiles_after = [&](int later) __attribute__((always_inline)) {
-    // wait until at most `later` tiles' loads are still in flight
-    if (NBUF > 3 && later >= 2) wait_vmcnt<(NBUF > 3 ? 4 * C::kCPW : 0)>();
-    else if (later >= 1) wait_vmcnt<2 * C::kCPW>();
-    else wait_vmcnt<0>();
-  };
+  if (0 < n_kt) issue(0, lds_k0, lds_v0);
+  if (NBUF > 2 && 1 < n_kt) issue(1, lds_k1, lds_v1);
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  if (0 < n_kt) issue(0, stage_k(I0{}), stage_v(I0{}));
-  if (1 < n_kt) issue(1, stage_k(I1{}), stage_v(I1{}));
-  if (NBUF > 3 && 2 < n_kt) issue(2, stage_k(I2{}), stage_v(I2{}));
-  wait_tiles_after(min(NBUF - 2, n_kt - 1));
-  block_barrier();
-
-  f32x16 s_cur[QB][2];
-  float mt_cur[QB];
-  if (active(0)) {
-    scores((const char*)lds_k0, s_cur);
-    tile_max(s_cur, mt_cur);
-  }
-
+  // One pipeline step for tile kt held in stage S (compile-time).
   auto step = [&](auto stage_c, int kt) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_c)::value;
-    constexpr int S1 = (S + 1) % NBUF;            // holds tile kt + 1
-    constexpr int SN = (S + NBUF - 1) % NBUF;     // receives tile kt + NBUF - 1
-    if (kt + 1 < n_kt) {
-      wait_tiles_after(min(NBUF - 3, n_kt - 2 - kt));
-      block_barrier();  // tile kt+1 visible to all waves; tile kt-1's buffers are free
-      if (kt + NBUF - 1 < n_kt) issue(kt + NBUF - 1, stage_k(std::integral_constant<int, SN>{}), stage_v(std::integral_constant<int, SN>{}));
-    }
-    if (!active(kt)) return;
-    if (needs_mask(kt)) {
-      mask(s_cur, kt * C::kBC);
-      tile_max(s_cur, mt_cur);
-    }
-    update_max(mt_cur);
-    // Scores of tile kt+1 (on the last tile this re-reads a resident buffer and the
-    // result is discarded).
-    f32x16 s_nxt[QB][2];
-    vec8 pf[QB][4];
-    scores((const char*)stage_k(std::integral_constant<int, S1>{}), s_nxt);
-    probs(s_cur, pf);
-    pv((const char*)stage_v(stage_c), pf);
-    tile_max(s_nxt, mt_cur);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s_cur[qb][kb] = s_nxt[qb][kb];
+    uint16_t* lk = S == 0 ? lds_k0 : (S == 1 ? lds_k1 : lds_k2);
+    uint16_t* lv = S == 0 ? lds_v0 : (S == 1 ? lds_v1 : lds_v2);
+    constexpr int SN = (S + NBUF - 1) % NBUF;  // stage that receives tile kt + NBUF - 1
+    uint16_t* nk = SN == 0 ? lds_k0 : (SN == 1 ? lds_k1 : lds_k2);
+    uint16_t* nv = SN == 0 ? lds_v0 : (SN == 1 ? lds_v1 : lds_v2);
+    // Tile kt has landed once at most the later tiles' loads are outstanding.
+    if (NBUF > 2 && kt + 1 < n_kt) wait_vmcnt<(NBUF > 2 ? (NBUF - 2) * 2 * C::kCPW : 0)>();
+    else wait_vmcnt<0>();
+    block_barrier();  // every wave's share of tile kt is in LDS; tile kt-1 is free
+    if (kt + NBUF - 1 < n_kt) issue(kt + NBUF - 1, nk, nv);
+    compute(kt, (const char*)lk, (const char*)lv);
   };
   for (int kt = 0; kt < n_kt; kt += NBUF) {
     step(std::integral_constant<int, 0>{}, kt);
     if (kt + 1 < n_kt) step(std::integral_constant<int, 1>{}, kt + 1);
-    if (kt + 2 < n_kt) step(std::integral_constant<int, 2 % NBUF>{}, kt + 2);
-    if constexpr (NBUF > 3)
-      if (kt + 3 < n_kt) step(std::integral_constant<int, 3 % NBUF>{}, kt + 3);
+    if constexpr (NBUF > 2)
+      if (kt + 2 < n_kt) step(std::integral_constant<int, 2>{}, kt + 2);
   }
 
   // ---- final normalisation: O = Ot / l, LSE = ln(2) * (m + log2 l) ---------------
@@ -376,12 +308,12 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 }
 
-template <typename T, int D, int NW, int QB, int NBUF, bool CAUSAL>
+template <typename T, int D, int NW, int QB, int NBUF, int BC, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
-  using C = FwdCfg<D, NW, QB, NBUF>;
+  using C = FwdCfg<D, NW, QB, NBUF, BC>;
   const int n_qtiles = (a.N + C::kBR - 1) / C::kBR;
   const long long blocks = (long long)n_qtiles * a.B * a.H;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW, QB, NBUF, CAUSAL>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW, QB, NBUF, BC, CAUSAL>), dim3((unsigned)blocks),
                      dim3(NW * 64), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H, a.Hkv,
                      a.N, n_qtiles, a.scale * kLog2e);
@@ -398,14 +330,17 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
 #define OSATTN_FWD_QB 1
 #endif
 #ifndef OSATTN_FWD_NBUF
-#define OSATTN_FWD_NBUF 4
+#define OSATTN_FWD_NBUF 2
+#endif
+#ifndef OSATTN_FWD_BC
+#define OSATTN_FWD_BC 128
 #endif
 
 template <typename T, int D>
 static hipError_t launch_fwd_d(const FwdArgs& a) {
-  constexpr int NW = OSATTN_FWD_NW, QB = OSATTN_FWD_QB, NB = OSATTN_FWD_NBUF;
-  if (a.causal) return launch_fwd_t<T, D, NW, QB, NB, true>(a);
-  return launch_fwd_t<T, D, NW, QB, NB, false>(a);
+  constexpr int NW = OSATTN_FWD_NW, QB = OSATTN_FWD_QB, NB = OSATTN_FWD_NBUF, BC = OSATTN_FWD_BC;
+  if (a.causal) return launch_fwd_t<T, D, NW, QB, NB, BC, true>(a);
+  return launch_fwd_t<T, D, NW, QB, NB, BC, false>(a);
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a) {
