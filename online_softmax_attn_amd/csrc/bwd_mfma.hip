@@ -232,7 +232,98 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // overlaps the MFMAs of block 1 and the dV/dK MFMAs of block 0 overlap the
   // arithmetic of block 1.  Everything is one basic block (masking is a
   // compile-time variant chosen per tile) so the scheduler can interleave.
-  auto compute_tile = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
+  // Variant for 32 keys per wave: one staged tile of 64 query rows, processed as
+  // two 32-row blocks.  For each block every LDS operand is requested before the
+  // instructions that consume it, with scheduling fences in between, so that LDS
+  // latency overlaps other work of the same wave (one wave per SIMD has nothing
+  // else to hide it):
+  //   row-wise Q/dO reads + LSE/D   | S, dP MFMAs
+  //   transposed Q/dO reads         | softmax-JVP arithmetic
+  //                                 | dV, dK MFMAs
+  auto compute_tile_fenced = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
+                          const float* lD) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+#pragma unroll
+    for (int qb = 0; qb < C::kQT / 32; ++qb) {
+      // -- operand requests for S and dP
+      u32x4 aq[D / 16], ad[D / 16];
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        aq[c] = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
+        ad[c] = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
+      }
+      f32x4 lse4[4], d4[4];  // rows 32qb + 8g + 4hi + 0..3 for register group g
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        lse4[g] = *(const f32x4*)&ll[32 * qb + 8 * g + 4 * hi];
+        d4[g] = *(const f32x4*)&lD[32 * qb + 8 * g + 4 * hi];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // -- S = Q K^T, dP = dO V^T (lane = key, register r = query row 8(r/4)+4hi+r%4)
+      f32x16 s[KB], dp[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[kb][r] = 0.f;
+          dp[kb][r] = 0.f;
+        }
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          s[kb] = M::mma32(as_vec8<T>(aq[c]), kf[kb][c], s[kb]);
+          dp[kb] = M::mma32(as_vec8<T>(ad[c]), vf[kb][c], dp[kb]);
+        }
+      // -- operand requests for dV^T and dK^T (transposed reads of the same tiles)
+      vec8 adt[2][D / 32], aqt[2][D / 32];
+#pragma unroll
+      for (int cq = 0; cq < 2; ++cq) {
+        const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          adt[cq][t] = join8<T>(lds_read_tr4(db_ + rowb + toff[t]), lds_read_tr4(db_ + rowb + toff8[t]));
+          aqt[cq][t] = join8<T>(lds_read_tr4(qb_ + rowb + toff[t]), lds_read_tr4(qb_ + rowb + toff8[t]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // -- P = exp2(S*c - LSE*log2e) (0 where masked), dS = P * (dP - D)
+      vec8 pp[2][KB], ps[2][KB];
+#pragma unroll
+      for (int cq = 0; cq < 2; ++cq)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int key = kw + 32 * kb + l32;
+          float p8[8], d8[8];
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const int g = 2 * cq + g2;
+            const int ql = 32 * qb + 8 * g + 4 * hi;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              float pv = fast_exp2(fmaf(s[kb][r], scale_log2, -lse4[g][e]));
+              if (MASK && key > i0 + ql + e) pv = 0.f;
+              p8[4 * g2 + e] = pv;
+              d8[4 * g2 + e] = pv * (dp[kb][r] - d4[g][e]);
+            }
+          }
+          pp[cq][kb] = pack8<T>(p8);
+          ps[cq][kb] = pack8<T>(d8);
+        }
+      // -- dV^T += dO^T P ; dK^T += Q^T dS  (reduction over the 32 query rows)
+#pragma unroll
+      for (int cq = 0; cq < 2; ++cq)
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            dv_acc[kb][t] = M::mma32(adt[cq][t], pp[cq][kb], dv_acc[kb][t]);
+            dk_acc[kb][t] = M::mma32(aqt[cq][t], ps[cq][kb], dk_acc[kb][t]);
+          }
+    }
+  };
+  auto compute_tile_wide = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
                           const float* lD) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_c)::value;
     constexpr int NQB = C::kQT / 32;
@@ -300,6 +391,11 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         }
       }
     }
+  };
+  auto compute_tile = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
+                          const float* lD) __attribute__((always_inline)) {
+    if constexpr (KB == 1) compute_tile_fenced(mask_c, i0, qb_, db_, ll, lD);
+    else compute_tile_wide(mask_c, i0, qb_, db_, ll, lD);
   };
   auto compute = [&](int it, const char* qb_, const char* db_, const float* ll, const float* lD)
       __attribute__((always_inline)) {
