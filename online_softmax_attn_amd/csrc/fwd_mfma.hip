@@ -23,10 +23,11 @@
 //    128-bit K reads and the transposed V reads are free of bank conflicts.
 //  * exp2 with log2(e) * scale folded into one FMA per score; row sums with
 //    v_dot2 over the rounded probabilities the matrix core consumes.
-//  * Rescaling of Ot and l is lazy: the reference max is only moved when a row's
-//    new max exceeds it by more than 8 (log2 units), so exp2 arguments stay <= 8.
-//    The result is exact for any reference value (the correction the pages
-//    describe cancels in Ot / l); it only avoids rescaling work.
+//  * The reference max is lazy: P is formed against the current reference and the
+//    exact tile max is taken (with the rescale of Ot and l) only on the first tile
+//    and when a row's tile sum of P leaves [0, 2^30].  The result is exact for any
+//    reference value (the correction the pages describe cancels in Ot / l); it only
+//    avoids the per-tile max and rescaling work.
 //  * Causal: key tiles wholly after the workgroup's last row are not loaded, tiles
 //    wholly after a wave's last row are skipped by that wave, and only tiles that
 //    cross the diagonal are masked.  Workgroups with the longest rows start first.
@@ -204,23 +205,38 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           }
       }
     }
-    // ---- step 2/4: row max, lazy move of the reference max --------------------------
-    float mt[QB];
-    bool grow = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
-      mt[qb] = wave_xor32_max(mx) * scale_log2;
-      grow |= mt[qb] > m_run[qb] + 8.0f;
-    }
-    if (__any(grow)) {
+    // ---- steps 2-4: probabilities against the running reference max -------------------
+    // P = exp2(S*c - m) with the current reference m.  The reference only has to keep
+    // the exponentials in a safe range: Ot / l and m + log2 l do not depend on it.  So
+    // the exact tile max is computed only on a wave's first tile and when some row's
+    // tile sum leaves [0, 2^30] (or is not finite); then Ot and l are rescaled by
+    // exp2(m_old - m_new) (the correction of the pages' step 4) and P is recomputed.
+    vec8 pf[QB][2 * KB];
+    float part[QB];
+    auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float mn = fmaxf(m_run[qb], mt[qb]);
+        const float neg_m = -m_run[qb];
+        part[qb] = 0.f;
+#pragma unroll
+        for (int c4 = 0; c4 < 2 * KB; ++c4) {
+          float pv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(s[qb][c4 >> 1][8 * (c4 & 1) + j], scale_log2, neg_m));
+          pf[qb][c4] = pack8<T>(pv);
+          part[qb] = sum8<T>(pf[qb][c4], part[qb]);
+        }
+      }
+    };
+    auto move_reference = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
+        const float mn = fmaxf(m_run[qb], wave_xor32_max(mx) * scale_log2);
         const float alpha = fast_exp2(m_run[qb] - mn);
         m_run[qb] = mn;
         l_run[qb] *= alpha;
@@ -229,23 +245,19 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[qb][t][r] *= alpha;
       }
+    };
+    if (kt == 0) move_reference();
+    probs();
+    bool unsafe = false;
+#pragma unroll
+    // 2^30 per tile keeps l below 2^44 for any N <= 2^24, far from fp32 overflow.
+    for (int qb = 0; qb < QB; ++qb) unsafe |= !(part[qb] <= 1073741824.0f);  // also catches NaN
+    if (__any(unsafe)) {
+      move_reference();
+      probs();
     }
-    // ---- step 2/3: P = exp2(S*c - m), row sums of the rounded P -----------------------
-    vec8 pf[QB][2 * KB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float neg_m = -m_run[qb];
-      float part = 0.f;
-#pragma unroll
-      for (int c4 = 0; c4 < 2 * KB; ++c4) {
-        float pv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(s[qb][c4 >> 1][8 * (c4 & 1) + j], scale_log2, neg_m));
-        pf[qb][c4] = pack8<T>(pv);
-        part = sum8<T>(pf[qb][c4], part);
-      }
-      l_run[qb] += part;
-    }
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += part[qb];
     // ---- step 5: O^T += V_j^T P^T ---------------------------------------------------
 #pragma unroll
     for (int c4 = 0; c4 < 2 * KB; ++c4) {
