@@ -14,11 +14,17 @@ kernel's extra recompute of S and dP is real work that is not counted.
 
 Timing: HIP events recorded on the stream the kernels run on (torch's current
 stream, which the binding passes to the library), around each pass of each of the
-K timed steps, after W untimed warm-up steps.  ``roofline`` is reported for the
-forward kernel (one launch per attn_fwd call): achieved = forward FLOP per launch
-/ mean launch time, against the dense bf16/fp16 MFMA peak of 2516.6 TFLOP/s
-(256 CUs x 4096 flop/clk x 2.4 GHz).  ``cpu_baseline`` times the fp64 oracle on the
-host for a bounded sample (a few heads of the same workload).
+K timed steps, after W untimed warm-up steps.  The backward is enqueued as its
+three kernels (attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq: exactly what
+attn_bwd launches) so that an event sits between every two launches.  ``kernels``
+gives each launch's mean/median/min/p90 time and its roofline: achieved = the
+algorithmic FLOP (or bytes, for the HBM-bound preprocess) per launch / mean launch
+time, against the dense bf16/fp16 MFMA peak of 2516.6 TFLOP/s (256 CUs x 4096
+flop/clk x 2.4 GHz) or HBM's 8 TB/s.  ``roofline`` repeats the entry of the
+kernel with the largest share of the step.  ``traffic`` is the HBM bytes per
+launch from committed rocprofv3 counter runs, or null once the kernel source has
+changed since they were taken.  ``cpu_baseline`` times the fp64 oracle on the
+host for a bounded sample (16 heads of the same workload).
 """
 
 from __future__ import annotations
@@ -37,12 +43,15 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}
 METRIC = "attention fwd/bwd TFLOP/s + % of bf16 MFMA peak, B*H=64 N=8192 d=128"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_mfma_traffic.json")
-FWD_SOURCES = [os.path.join(ROOT, "online_softmax_attn_amd", "csrc", f)
-               for f in ("fwd_mfma.hip", "common.h")]
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "online_softmax_attn_amd", "csrc")
+FWD_SOURCES = [os.path.join(CSRC, f) for f in ("fwd_mfma.hip", "common.h")]
+BWD_SOURCES = [os.path.join(CSRC, f) for f in ("bwd_mfma.hip", "common.h")]
+F32_SOURCES = [os.path.join(CSRC, "f32_kernels.hip")]
 
 
-def kernel_source_sha(paths=FWD_SOURCES) -> str:
+def kernel_source_sha(paths) -> str:
     h = hashlib.sha256()
     for p in paths:
         with open(p, "rb") as f:
@@ -50,23 +59,90 @@ def kernel_source_sha(paths=FWD_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload_name: str):
-    """HBM bytes per forward launch from committed rocprofv3 counter runs, if they
-    were taken on the current forward kernel source; else None."""
+def load_traffic():
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
+            return json.load(f)
     except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_sha") != kernel_source_sha():
-        return None
-    ent = t.get("workloads", {}).get(workload_name)
-    if not ent:
-        return None
-    return ent.get("hbm_bytes_per_launch")
+        return {}
 
 
-def cpu_baseline(w, inp, gpu_out, heads: int = 4):
+def traffic_of(traffic, kt, workload_name: str):
+    """HBM bytes per launch of one kernel from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs, scaled by the copy-kernel calibration; None unless the counters
+    were taken on the kernel's current source."""
+    ent = traffic.get("kernels", {}).get(kt["name"], {})
+    if ent.get("source_sha") != kernel_source_sha(kt["sources"]):
+        return None
+    return ent.get("workloads", {}).get(workload_name, {}).get("hbm_bytes_per_launch")
+
+
+COPY_BYTES = 512 * 1024 * 1024
+COPY_KERNEL = "copyBuffer"  # the runtime's device-to-device copy kernel
+
+
+def _counter_means(folder: str, counter: str):
+    """Mean per-dispatch value of one counter, per kernel name, from a rocprofv3
+    --pmc output folder (run_counter_collection.csv)."""
+    import csv
+    import glob
+    sums, counts = {}, {}
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                sums[name] = sums.get(name, 0.0) + float(r["Counter_Value"])
+                counts[name] = counts.get(name, 0) + 1
+    return {n: sums[n] / counts[n] for n in sums}
+
+
+def _pick(means, short):
+    hits = [v for n, v in means.items() if short in n]
+    if not hits:
+        raise SystemExit(f"no dispatch of {short} in the counter output")
+    return sum(hits) / len(hits)
+
+
+def write_traffic(folders, workload_name):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each kernel of the step by
+    what the same counters read for a plain copy of COPY_BYTES, and record the
+    result with the sha of each kernel's source."""
+    import synthetic as S
+    w = S.WORKLOADS[workload_name] if workload_name else S.HEADLINE
+    fetch, write, cfetch, cwrite = folders
+    fm, wm = _counter_means(fetch, "FETCH_SIZE"), _counter_means(write, "WRITE_SIZE")
+    cf = _pick(_counter_means(cfetch, "FETCH_SIZE"), COPY_KERNEL)
+    cw = _pick(_counter_means(cwrite, "WRITE_SIZE"), COPY_KERNEL)
+    fetch_scale, write_scale = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    old = load_traffic()
+    out = {"note": "HBM bytes per launch = FETCH_SIZE*1024*fetch_scale + WRITE_SIZE*1024*write_scale; "
+                   "the scales make a plain device copy of known size read and write its own size",
+           "copy_calibration": {"bytes_read_and_written": COPY_BYTES, "FETCH_SIZE_KiB": cf,
+                                "WRITE_SIZE_KiB": cw, "fetch_scale": round(fetch_scale, 5),
+                                "write_scale": round(write_scale, 5)},
+           "kernels": old.get("kernels", {})}
+    for kt in kernel_table(w):
+        f_kib, w_kib = _pick(fm, kt["name"]), _pick(wm, kt["name"])
+        hbm = f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale
+        ent = out["kernels"].get(kt["name"], {})
+        sha = kernel_source_sha(kt["sources"])
+        if ent.get("source_sha") != sha:
+            ent = {"source_sha": sha, "source_files": [os.path.relpath(p, ROOT) for p in kt["sources"]],
+                   "workloads": {}}
+        ent["workloads"][w.name] = {"FETCH_SIZE_KiB_per_dispatch": round(f_kib, 1),
+                                    "WRITE_SIZE_KiB_per_dispatch": round(w_kib, 1),
+                                    "hbm_bytes_per_launch": int(hbm),
+                                    "algorithmic_bytes_per_launch": kt["bytes"],
+                                    "ratio_to_algorithmic": round(hbm / kt["bytes"], 4)}
+        out["kernels"][kt["name"]] = ent
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def cpu_baseline(w, inp, gpu_out, heads: int = 16):
     """Time the fp64 oracle (fwd + bwd) on `heads` query heads of the workload."""
     import numpy as np
 
@@ -101,13 +177,22 @@ def cpu_baseline(w, inp, gpu_out, heads: int = 4):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time every point of the bf16 sweep (one JSON line each)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run three plain 512 MiB device copies (for scaling HBM counters)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="no GPU: turn four rocprofv3 --pmc output folders into "
+                         "profiles/hbm_traffic.json")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        write_traffic(args.traffic_from, args.workload)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
@@ -124,12 +209,58 @@ def main():
         sys.exit(1)
     osa.library()
 
+    if args.copy_calibration:
+        a = torch.randn(COPY_BYTES // 4, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES}))
+        return
+
     if args.sweep:
         for w in S.sweep_points():
             print(json.dumps(run_one(w, args, osa, torch, with_cpu=False)), flush=True)
         return
     w = S.WORKLOADS[args.workload] if args.workload else S.HEADLINE
     print(json.dumps(run_one(w, args, osa, torch, with_cpu=not args.no_cpu_baseline)), flush=True)
+
+
+def kernel_table(w):
+    """The four launches of one step, in order, with the algorithmic work each one
+    is charged: FLOP for the MFMA kernels (the counted matmuls of the method), bytes
+    for the HBM-bound preprocess."""
+    e = {"bf16": 2, "fp16": 2, "fp32": 4}[w.dtype]
+    qb = w.B * w.H * w.N * w.d * e      # one of Q, O, dO, dQ
+    kb = w.B * w.Hkv * w.N * w.d * e    # one of K, V, dK, dV
+    rb = w.B * w.H * w.N * 4            # one float32 per query row
+    f32 = w.dtype == "fp32"
+    fsrc = F32_SOURCES if f32 else FWD_SOURCES
+    bsrc = F32_SOURCES if f32 else BWD_SOURCES
+    rows = w.B * w.H * w.N
+    fwd_f, bwd_f = w.fwd_flop(), w.bwd_flop()
+    return [
+        # S = Q K^T and O = P V.
+        {"name": "fwd_mfma_kernel" if w.dtype != "fp32" else "fwd_f32_kernel", "bound": "mfma",
+         "work": fwd_f, "unit": "flop", "sources": fsrc, "bytes": 2 * qb + 2 * kb + rb},
+        # Reads O and dO (d elements each) and LSE; writes D and LSE*log2(e).
+        {"name": "bwd_preprocess_kernel", "bound": "hbm", "work": rows * (2 * w.d * e + 3 * 4),
+         "unit": "byte", "sources": BWD_SOURCES, "bytes": 2 * qb + 3 * rb},
+        # S recompute, dV = P^T dO, dP = dO V^T, dK = dS^T Q: four of the five matmuls.
+        {"name": "bwd_dkdv_kernel" if w.dtype != "fp32" else "bwd_dkdv_f32_kernel",
+         "bound": "mfma", "work": 0.8 * bwd_f, "unit": "flop", "sources": bsrc,
+         "bytes": 2 * qb + 4 * kb + 2 * rb},
+        # dQ = dS K (counted); the kernel also recomputes S and dP (executed, not counted).
+        {"name": "bwd_dq_kernel" if w.dtype != "fp32" else "bwd_dq_f32_kernel", "bound": "mfma",
+         "work": 0.2 * bwd_f, "unit": "flop", "sources": bsrc, "executed_work": 0.6 * bwd_f,
+         "bytes": 3 * qb + 2 * kb + 2 * rb},
+    ]
+
+
+def stats(xs):
+    ys = sorted(xs)
+    return {"mean": sum(ys) / len(ys), "median": ys[len(ys) // 2], "min": ys[0],
+            "p90": ys[min(len(ys) - 1, int(math.ceil(0.9 * len(ys))) - 1)]}
 
 
 def run_one(w, args, osa, torch, with_cpu: bool):
@@ -141,43 +272,69 @@ def run_one(w, args, osa, torch, with_cpu: bool):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), device="cuda", dtype=torch.float32)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(osa.attn_bwd_workspace_bytes(w.B, w.H, w.Hkv, w.N, w.d, q.dtype),
-                     device="cuda", dtype=torch.uint8)
+    ws = osa.new_bwd_workspace(q, k)
+    kw = dict(causal=w.causal, scale=w.scale)
 
-    def step():
-        osa.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
-        osa.attn_bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
-                     workspace=ws)
+    # One step = the forward, then the backward's three kernels.  attn_bwd enqueues
+    # exactly these three; calling them one by one lets an event sit between them.
+    launches = [
+        lambda: osa.attn_fwd(q, k, v, out=o, lse=lse, **kw),
+        lambda: osa.attn_bwd_preprocess(q, k, o, lse, do, ws),
+        lambda: osa.attn_bwd_dkdv(q, k, v, o, lse, do, ws, dk=dk, dv=dv, **kw),
+        lambda: osa.attn_bwd_dq(q, k, v, o, lse, do, ws, dq=dq, **kw),
+    ]
 
     for _ in range(args.warmup):
-        step()
+        for f in launches:
+            f()
     torch.cuda.synchronize()
 
+    # Events on the stream the library launches on (the binding passes torch's
+    # current stream to every call).
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    nl = len(launches)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        osa.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
-        ev[i][1].record(stream)
-        osa.attn_bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
-                     workspace=ws)
-        ev[i][2].record(stream)
+        for j, f in enumerate(launches):
+            f()
+            ev[i][j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    fwd_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
-    bwd_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
-    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(args.steps)]
-    mean = lambda xs: sum(xs) / len(xs)
-    med = lambda xs: sorted(xs)[len(xs) // 2]
-    fwd_f, bwd_f = w.fwd_flop(), w.bwd_flop()
+    step_ms = [ev[i][0].elapsed_time(ev[i][nl]) for i in range(args.steps)]
+    per_ms = [[ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)] for j in range(nl)]
     peak = PEAK_TFLOPS[w.dtype]
-    ms_step = mean(step_ms)
+    ms_step = stats(step_ms)["mean"]
+    fwd_f, bwd_f = w.fwd_flop(), w.bwd_flop()
     value = (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
-    fwd_tf = fwd_f / (mean(fwd_ms) * 1e-3) / 1e12
-    bwd_tf = bwd_f / (mean(bwd_ms) * 1e-3) / 1e12
+    fwd_ms = stats(per_ms[0])
+    bwd_ms = stats([sum(per_ms[j][i] for j in range(1, nl)) for i in range(args.steps)])
+    fwd_tf = fwd_f / (fwd_ms["mean"] * 1e-3) / 1e12
+    bwd_tf = bwd_f / (bwd_ms["mean"] * 1e-3) / 1e12
+    traffic = load_traffic()
+
+    kernels = []
+    for kt, ms in zip(kernel_table(w), per_ms):
+        st = stats(ms)
+        secs = st["mean"] * 1e-3
+        if kt["bound"] == "mfma":
+            ach, pk, unit = kt["work"] / secs / 1e12, peak, "TFLOP/s"
+        else:
+            ach, pk, unit = kt["work"] / secs / 1e9, HBM_PEAK_GBS, "GB/s"
+        ent = {"kernel": kt["name"], "bound": kt["bound"], "achieved": round(ach, 2), "peak": pk,
+               "unit": unit, "frac": round(ach / pk, 4),
+               "traffic": traffic_of(traffic, kt, w.name),
+               ("flop_per_launch" if kt["unit"] == "flop" else "bytes_per_launch"): kt["work"],
+               "ms": {k2: round(x, 4) for k2, x in st.items()}}
+        if "executed_work" in kt:
+            ent["executed_flop_per_launch"] = kt["executed_work"]
+            ent["executed_tflops"] = round(kt["executed_work"] / secs / 1e12, 2)
+        kernels.append(ent)
+    dominant = max(kernels, key=lambda e: e["ms"]["mean"])
+
     props = torch.cuda.get_device_properties(0)
     out = {
         "metric": METRIC,
@@ -193,16 +350,14 @@ def run_one(w, args, osa, torch, with_cpu: bool):
         "dtype": w.dtype,
         "data": "synthetic",
         "config": dict(w.describe(), step="fwd+bwd", parallelism="single GPU"),
-        "fwd": {"ms_mean": round(mean(fwd_ms), 4), "ms_median": round(med(fwd_ms), 4),
+        "fwd": {"ms_mean": round(fwd_ms["mean"], 4), "ms_median": round(fwd_ms["median"], 4),
                 "tflops": round(fwd_tf, 2), "frac_peak": round(fwd_tf / peak, 4)},
-        "bwd": {"ms_mean": round(mean(bwd_ms), 4), "ms_median": round(med(bwd_ms), 4),
+        "bwd": {"ms_mean": round(bwd_ms["mean"], 4), "ms_median": round(bwd_ms["median"], 4),
                 "tflops": round(bwd_tf, 2), "frac_peak": round(bwd_tf / peak, 4),
-                "launches": 3},
+                "launches": nl - 1},
         "frac_peak_step": round(value / peak, 4),
-        "roofline": {"bound": "mfma", "kernel": "fwd_mfma_kernel", "achieved": round(fwd_tf, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(fwd_tf / peak, 4),
-                     "traffic": traffic_for(w.name),
-                     "flop_per_launch": fwd_f},
+        "roofline": {k2: dominant[k2] for k2 in dominant if k2 != "ms"},
+        "kernels": kernels,
         "wall_s_timed": round(wall, 3),
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},

@@ -92,6 +92,43 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              int B, int H, int Hkv, int N, int d, float scale, int causal,
              int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The three kernels of attn_bwd, callable one at a time (for example to time
+ * each, or to put them on different streams).  Running attn_bwd_preprocess,
+ * then attn_bwd_dkdv and attn_bwd_dq (in either order, or concurrently once
+ * the preprocess is complete) with the same arguments and workspace gives the
+ * same dq, dk, dv as attn_bwd.
+ *
+ * attn_bwd_preprocess (softmax-backward page, the row dot product of the
+ * softmax JVP; FlashAttention-2 page, backward pass): reads o, lse, dO and
+ * writes D = rowsum(dO * O) and LSE * log2(e) into the workspace.  It reads no
+ * q, k, v; Hkv only enters the size validation.
+ *
+ * attn_bwd_dkdv (FlashAttention-2 page, backward pass: the key/value block owns
+ * its gradients and loops over query tiles): reads q, k, v, dO and the
+ * workspace filled by attn_bwd_preprocess (lse itself is read by the float32
+ * kernels only); writes dk and dv (fully overwritten).
+ *
+ * attn_bwd_dq (the separate-pass dQ of the FlashAttention-2 backward): reads
+ * the same inputs and writes dq (fully overwritten).
+ *
+ * Each entry point validates like attn_bwd and returns the same codes; the
+ * workspace is only read by attn_bwd_dkdv and attn_bwd_dq.
+ */
+int attn_bwd_preprocess(const void* o, const float* lse, const void* dO,
+                        int B, int H, int Hkv, int N, int d, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                  const void* dO, void* dk, void* dv,
+                  int B, int H, int Hkv, int N, int d, float scale, int causal,
+                  int dtype, const void* workspace, size_t workspace_bytes,
+                  void* stream);
+int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                const void* dO, void* dq,
+                int B, int H, int Hkv, int N, int d, float scale, int causal,
+                int dtype, const void* workspace, size_t workspace_bytes,
+                void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* attn_status_string(int status);
 

@@ -9,6 +9,10 @@ exception is raised.
     o, lse = attn_fwd(q, k, v, causal=False)          # q [B,H,N,d], k/v [B,Hkv,N,d]
     dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=False)
 
+The backward's three kernels can also be enqueued one at a time with
+``attn_bwd_preprocess``, ``attn_bwd_dkdv`` and ``attn_bwd_dq`` on a shared
+workspace (``new_bwd_workspace``).
+
 Tensors must be contiguous ROCm-device tensors of one dtype (float32, float16 or
 bfloat16); ``lse`` is float32 [B,H,N].  ``scale`` defaults to 1/sqrt(d).
 """
@@ -25,6 +29,10 @@ __all__ = [
     "attn_fwd",
     "attn_bwd",
     "attn_bwd_workspace_bytes",
+    "attn_bwd_preprocess",
+    "attn_bwd_dkdv",
+    "attn_bwd_dq",
+    "new_bwd_workspace",
     "status_string",
     "library",
     "library_path",
@@ -50,7 +58,8 @@ STATUS = {
 }
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
-EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string")
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
+            "attn_bwd_dkdv", "attn_bwd_dq", "attn_status_string")
 
 _lib = None
 
@@ -80,6 +89,13 @@ def library() -> ctypes.CDLL:
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp,
                              ctypes.c_size_t, vp]
     lib.attn_bwd.restype = i
+    sz = ctypes.c_size_t
+    lib.attn_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
+    lib.attn_bwd_preprocess.restype = i
+    lib.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.attn_bwd_dkdv.restype = i
+    lib.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.attn_bwd_dq.restype = i
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_string.argtypes = [i]
@@ -149,10 +165,7 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     return out, lse
 
 
-def attn_bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
-             dq=None, dk=None, dv=None, workspace=None):
-    """dQ, dK, dV from the forward's O and LSE; enqueued on the current stream."""
-    lib = library()
+def _bwd_checked(q, k, v, o, lse, do, scale, dq, dk, dv, workspace):
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _check_dev(name, t, q.dtype)
     _check_dev("lse", lse, torch.float32)
@@ -168,15 +181,83 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
         _check_dev(name, t, q.dtype)
         if t.shape != ref.shape:
             raise ValueError(f"{name} has the wrong shape")
-    need = attn_bwd_workspace_bytes(B, H, Hkv, N, d, q.dtype)
     if workspace is None:
-        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+        workspace = new_bwd_workspace(q, k)
     _check_dev("workspace", workspace)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    return (B, H, Hkv, N, d), float(scale), dq, dk, dv, workspace
+
+
+def new_bwd_workspace(q, k):
+    """An uninitialised device buffer of attn_bwd_workspace_bytes() for these tensors."""
+    B, H, Hkv, N, d = _dims(q, k)
+    need = attn_bwd_workspace_bytes(B, H, Hkv, N, d, q.dtype)
+    return torch.empty(need, device=q.device, dtype=torch.uint8)
+
+
+def _ws_bytes(ws):
+    return ws.numel() * ws.element_size()
+
+
+def attn_bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV from the forward's O and LSE; enqueued on the current stream."""
+    lib = library()
+    (B, H, Hkv, N, d), scale, dq, dk, dv, ws = _bwd_checked(q, k, v, o, lse, do, scale, dq, dk,
+                                                            dv, workspace)
     st = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                      B, H, Hkv, N, d, float(scale), int(bool(causal)), DTYPE_CODES[q.dtype],
-                      workspace.data_ptr(), ws_bytes, _stream_handle(q.device))
+                      B, H, Hkv, N, d, scale, int(bool(causal)), DTYPE_CODES[q.dtype],
+                      ws.data_ptr(), _ws_bytes(ws), _stream_handle(q.device))
     if st != 0:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv
+
+
+def attn_bwd_preprocess(q, k, o, lse, do, workspace):
+    """First backward kernel alone: D and LSE*log2(e) into ``workspace``.
+
+    q and k only supply the shapes (nothing is read from them)."""
+    lib = library()
+    for name, t in (("o", o), ("do", do)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    _check_dev("workspace", workspace)
+    B, H, Hkv, N, d = _dims(q, k)
+    if o.shape != q.shape or do.shape != q.shape or lse.shape != (B, H, N):
+        raise ValueError("inconsistent shapes")
+    st = lib.attn_bwd_preprocess(o.data_ptr(), lse.data_ptr(), do.data_ptr(), B, H, Hkv, N, d,
+                                 DTYPE_CODES[q.dtype], workspace.data_ptr(), _ws_bytes(workspace),
+                                 _stream_handle(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_preprocess")
+    return workspace
+
+
+def attn_bwd_dkdv(q, k, v, o, lse, do, workspace, causal: bool = False,
+                  scale: float | None = None, dk=None, dv=None):
+    """dK/dV kernel alone, after attn_bwd_preprocess filled ``workspace``."""
+    lib = library()
+    (B, H, Hkv, N, d), scale, _, dk, dv, ws = _bwd_checked(q, k, v, o, lse, do, scale, q, dk, dv,
+                                                           workspace)
+    st = lib.attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                           do.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, scale,
+                           int(bool(causal)), DTYPE_CODES[q.dtype], ws.data_ptr(), _ws_bytes(ws),
+                           _stream_handle(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_dkdv")
+    return dk, dv
+
+
+def attn_bwd_dq(q, k, v, o, lse, do, workspace, causal: bool = False,
+                scale: float | None = None, dq=None):
+    """dQ kernel alone, after attn_bwd_preprocess filled ``workspace``."""
+    lib = library()
+    (B, H, Hkv, N, d), scale, dq, _, _, ws = _bwd_checked(q, k, v, o, lse, do, scale, dq, k, v,
+                                                          workspace)
+    st = lib.attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                         dq.data_ptr(), B, H, Hkv, N, d, scale, int(bool(causal)),
+                         DTYPE_CODES[q.dtype], ws.data_ptr(), _ws_bytes(ws),
+                         _stream_handle(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_dq")
+    return dq

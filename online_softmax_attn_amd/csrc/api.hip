@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/osattn.h"
 #include "launch.h"
 
@@ -56,11 +58,17 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int dtype) 
   return 2 * round256((size_t)B * H * N * sizeof(float));
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-             const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
-             float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
-             void* stream) {
-  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return ATTN_ERR_NULL;
+namespace {
+
+bool aligned_all(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned16(p)) return false;
+  return true;
+}
+
+// Checks shared by every backward entry point (pointers are checked by the caller).
+int validate_bwd(int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype,
+                 const void* workspace, size_t workspace_bytes) {
   int st = validate_sizes(B, H, Hkv, N, d, dtype);
   if (st != ATTN_OK) return st;
   st = validate_scale(scale);
@@ -68,17 +76,74 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
   if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, Hkv, N, d, dtype))
     return ATTN_ERR_WORKSPACE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
-      !aligned16(workspace))
-    return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+osattn::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dO, void* dq, void* dk, void* dv, int B,
+                         int H, int Hkv, int N, int d, float scale, int causal, int dtype,
+                         const void* workspace, void* stream, int stages) {
   float* dvec = (float*)workspace;
   float* lse2 = (float*)((char*)workspace + round256((size_t)B * H * N * sizeof(float)));
-  osattn::BwdArgs a{q, k,   v, o, lse,   dO,     dq,    dk,    dv, dvec, lse2,
-                    B, H, Hkv, N, d, scale, causal, dtype, stream};
-  hipError_t e = osattn::launch_bwd_preprocess(a);
-  if (e == hipSuccess) e = dtype == ATTN_F32 ? osattn::launch_bwd_f32(a) : osattn::launch_bwd_mfma(a);
+  return osattn::BwdArgs{q,   k,   v, o, lse,   dO,     dq,    dk,     dv,     dvec, lse2, B,
+                         H, Hkv, N, d, scale, causal, dtype, stream, stages};
+}
+
+int run_bwd_kernels(const osattn::BwdArgs& a) {
+  const hipError_t e = a.dtype == ATTN_F32 ? osattn::launch_bwd_f32(a) : osattn::launch_bwd_mfma(a);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+             float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  const int st = validate_bwd(B, H, Hkv, N, d, scale, causal, dtype, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (!aligned_all({q, k, v, o, lse, dO, dq, dk, dv, workspace})) return ATTN_ERR_ALIGN;
+  const osattn::BwdArgs a = bwd_args(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale,
+                                     causal, dtype, workspace, stream,
+                                     osattn::kStageDkdv | osattn::kStageDq);
+  if (osattn::launch_bwd_preprocess(a) != hipSuccess) return ATTN_ERR_LAUNCH;
+  return run_bwd_kernels(a);
+}
+
+int attn_bwd_preprocess(const void* o, const float* lse, const void* dO, int B, int H, int Hkv,
+                        int N, int d, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!o || !lse || !dO) return ATTN_ERR_NULL;
+  const int st = validate_bwd(B, H, Hkv, N, d, 1.f, 0, dtype, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (!aligned_all({o, lse, dO, workspace})) return ATTN_ERR_ALIGN;
+  const osattn::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, o, lse, dO, nullptr, nullptr,
+                                     nullptr, B, H, Hkv, N, d, 1.f, 0, dtype, workspace, stream, 0);
+  return osattn::launch_bwd_preprocess(a) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                  void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale,
+                  int causal, int dtype, const void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!q || !k || !v || !lse || !dO || !dk || !dv) return ATTN_ERR_NULL;
+  const int st = validate_bwd(B, H, Hkv, N, d, scale, causal, dtype, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (!aligned_all({q, k, v, lse, dO, dk, dv, workspace})) return ATTN_ERR_ALIGN;
+  return run_bwd_kernels(bwd_args(q, k, v, nullptr, lse, dO, nullptr, dk, dv, B, H, Hkv, N, d,
+                                  scale, causal, dtype, workspace, stream, osattn::kStageDkdv));
+}
+
+int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                void* dq, int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype,
+                const void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !lse || !dO || !dq) return ATTN_ERR_NULL;
+  const int st = validate_bwd(B, H, Hkv, N, d, scale, causal, dtype, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (!aligned_all({q, k, v, lse, dO, dq, workspace})) return ATTN_ERR_ALIGN;
+  return run_bwd_kernels(bwd_args(q, k, v, nullptr, lse, dO, dq, nullptr, nullptr, B, H, Hkv, N,
+                                  d, scale, causal, dtype, workspace, stream, osattn::kStageDq));
 }
 
 const char* attn_status_string(int status) {

@@ -704,7 +704,7 @@ template <typename T, int D, bool CAUSAL>
 static hipError_t bwd_t(const BwdArgs& a) {
   constexpr int NB = OSATTN_BWD_NBUF;
   const float sl2 = a.scale * kLog2e;
-  {
+  if (a.stages & kStageDkdv) {
     using C = DkdvCfg<D, NB>;
     const int n_kt = (a.N + C::kKeys - 1) / C::kKeys;
     const long long blocks = (long long)n_kt * a.B * a.Hkv;
@@ -715,7 +715,7 @@ static hipError_t bwd_t(const BwdArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (a.stages & kStageDq) {
     using C = DqCfg<D, NB>;
     const int n_qt = (a.N + C::kRows - 1) / C::kRows;
     const long long blocks = (long long)n_qt * a.B * a.H;

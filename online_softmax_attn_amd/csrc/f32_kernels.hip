@@ -237,16 +237,20 @@ hipError_t fwd_f32_t(const FwdArgs& a) {
 
 template <int D, bool CAUSAL>
 hipError_t bwd_f32_t(const BwdArgs& a) {
-  dim3 gk((a.N + kRows - 1) / kRows, a.B * a.Hkv);
-  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), gk, dim3(64), 0, (hipStream_t)a.stream,
-                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dO,
-                     a.lse, a.dvec, (float*)a.dk, (float*)a.dv, a.H, a.Hkv, a.N, a.scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 gq((a.N + kRows - 1) / kRows, a.B * a.H);
-  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), gq, dim3(64), 0, (hipStream_t)a.stream,
-                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dO,
-                     a.lse, a.dvec, (float*)a.dq, a.H, a.Hkv, a.N, a.scale);
+  if (a.stages & kStageDkdv) {
+    dim3 gk((a.N + kRows - 1) / kRows, a.B * a.Hkv);
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), gk, dim3(64), 0, (hipStream_t)a.stream,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dO,
+                       a.lse, a.dvec, (float*)a.dk, (float*)a.dv, a.H, a.Hkv, a.N, a.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.stages & kStageDq) {
+    dim3 gq((a.N + kRows - 1) / kRows, a.B * a.H);
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), gq, dim3(64), 0, (hipStream_t)a.stream,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dO,
+                       a.lse, a.dvec, (float*)a.dq, a.H, a.Hkv, a.N, a.scale);
+  }
   return hipGetLastError();
 }
 

@@ -37,7 +37,11 @@ struct BwdArgs {
   int causal;
   int dtype;
   void* stream;
+  int stages;  // bit set of kStageDkdv and kStageDq: which backward kernels to launch
 };
+
+constexpr int kStageDkdv = 1;
+constexpr int kStageDq = 2;
 
 hipError_t launch_fwd_mfma(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);

@@ -112,6 +112,66 @@ def test_bwd_rejects(kw, code):
     assert bwd(**kw) == S[code]
 
 
+def pre(**kw):
+    a = dict(o=P, lse=P, do=P, B=1, H=2, Hkv=1, N=8, d=64, dtype=2, ws=P, ws_bytes=1 << 20,
+             stream=None)
+    a.update(kw)
+    return osa.library().attn_bwd_preprocess(a["o"], a["lse"], a["do"], a["B"], a["H"], a["Hkv"],
+                                             a["N"], a["d"], a["dtype"], a["ws"], a["ws_bytes"],
+                                             a["stream"])
+
+
+def stage(fn, **kw):
+    a = dict(q=P, k=P, v=P, lse=P, do=P, out1=P, out2=P, B=1, H=2, Hkv=1, N=8, d=64,
+             scale=0.125, causal=0, dtype=2, ws=P, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    lib = osa.library()
+    tail = (a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
+            a["ws"], a["ws_bytes"], a["stream"])
+    if fn == "dkdv":
+        return lib.attn_bwd_dkdv(a["q"], a["k"], a["v"], a["lse"], a["do"], a["out1"], a["out2"],
+                                 *tail)
+    return lib.attn_bwd_dq(a["q"], a["k"], a["v"], a["lse"], a["do"], a["out1"], *tail)
+
+
+STAGE_INVALID = [kw for kw in INVALID if "o" not in kw[0]] + [
+    ({"do": None}, "ATTN_ERR_NULL"),
+    ({"out1": None}, "ATTN_ERR_NULL"),
+    ({"ws": None}, "ATTN_ERR_WORKSPACE"),
+    ({"ws_bytes": 16}, "ATTN_ERR_WORKSPACE"),
+    ({"out1": P + 2}, "ATTN_ERR_ALIGN"),
+    ({"ws": P + 8}, "ATTN_ERR_ALIGN"),
+]
+
+
+@pytest.mark.parametrize("fn", ["dkdv", "dq"])
+@pytest.mark.parametrize("kw,code", STAGE_INVALID, ids=lambda x: str(x))
+def test_bwd_stage_rejects(fn, kw, code):
+    assert stage(fn, **kw) == S[code]
+
+
+def test_bwd_stage_dkdv_checks_second_output():
+    assert stage("dkdv", out2=None) == S["ATTN_ERR_NULL"]
+    assert stage("dkdv", out2=P + 4) == S["ATTN_ERR_ALIGN"]
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"o": None}, "ATTN_ERR_NULL"),
+    ({"lse": None}, "ATTN_ERR_NULL"),
+    ({"do": None}, "ATTN_ERR_NULL"),
+    ({"N": 0}, "ATTN_ERR_SHAPE"),
+    ({"d": 96}, "ATTN_ERR_HEAD_DIM"),
+    ({"H": 3, "Hkv": 2}, "ATTN_ERR_GQA"),
+    ({"dtype": 7}, "ATTN_ERR_DTYPE"),
+    ({"ws": None}, "ATTN_ERR_WORKSPACE"),
+    ({"ws_bytes": 100}, "ATTN_ERR_WORKSPACE"),
+    ({"o": P + 8}, "ATTN_ERR_ALIGN"),
+    ({"ws": P + 4}, "ATTN_ERR_ALIGN"),
+], ids=lambda x: str(x))
+def test_bwd_preprocess_rejects(kw, code):
+    assert pre(**kw) == S[code]
+
+
 def test_workspace_bytes():
     f = osa.library().attn_bwd_workspace_bytes
     assert f(1, 1, 1, 1, 64, 0) == 2 * 256

@@ -89,6 +89,33 @@ def test_backward_deterministic():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("dtype,causal,order", [("bf16", False, "dkdv_first"),
+                                                 ("fp16", True, "dq_first"),
+                                                 ("fp32", True, "dkdv_first")])
+def test_backward_stages_match_attn_bwd(dtype, causal, order):
+    """The three stage entry points, run one by one on a shared workspace, write
+    exactly what attn_bwd writes (same kernels, single writer per element)."""
+    need_gpu()
+    import online_softmax_attn_amd as osa
+    w = S.custom(dtype, 1, 4, 2, 300, 64 if dtype == "fp16" else 128, causal, seed_base=8050)
+    inp = S.make_inputs(w)
+    o, lse, dq, dk, dv = run_bwd(inp, causal, w.scale)
+    q, k, v, do = (t.to("cuda") for t in (inp["q"], inp["k"], inp["v"], inp["do"]))
+    ws = osa.new_bwd_workspace(q, k)
+    ws.fill_(0xFF)  # stale contents must not matter
+    osa.attn_bwd_preprocess(q, k, o, lse, do, ws)
+    kw = dict(causal=causal, scale=w.scale)
+    if order == "dq_first":
+        dq2 = osa.attn_bwd_dq(q, k, v, o, lse, do, ws, **kw)
+        dk2, dv2 = osa.attn_bwd_dkdv(q, k, v, o, lse, do, ws, **kw)
+    else:
+        dk2, dv2 = osa.attn_bwd_dkdv(q, k, v, o, lse, do, ws, **kw)
+        dq2 = osa.attn_bwd_dq(q, k, v, o, lse, do, ws, **kw)
+    torch.cuda.synchronize()
+    for x, y in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(x, y)
+
+
 def test_side_stream_matches_default_stream():
     need_gpu()
     w = S.custom("fp16", 1, 2, 2, 513, 64, False, seed_base=8100)
