@@ -86,6 +86,10 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const E* __restrict
 
 // ---------------------------------------------------------------------------
 // 2. dK / dV.
+#ifndef OSATTN_DKDV_PIPE
+#define OSATTN_DKDV_PIPE 1
+#endif
+
 template <int D, int NBUF>
 struct DkdvCfg {
   static constexpr int kNW = 4;                 // waves (one per SIMD)
@@ -113,16 +117,19 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
   constexpr int KB = C::kKB;
-  static_assert(NBUF == 2 || NBUF == 3, "two or three stages");
+  static_assert(NBUF >= 2 && NBUF <= 4, "two to four stages");
   __shared__ __attribute__((aligned(1024))) uint16_t lq0[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t ld0[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lq1[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t ld1[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lq2[NBUF > 2 ? C::kTileElems : 8];
   __shared__ __attribute__((aligned(1024))) uint16_t ld2[NBUF > 2 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lq3[NBUF > 3 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t ld3[NBUF > 3 ? C::kTileElems : 8];
   __shared__ __attribute__((aligned(256))) float ll0[C::kQT], lD0[C::kQT];
   __shared__ __attribute__((aligned(256))) float ll1[C::kQT], lD1[C::kQT];
   __shared__ __attribute__((aligned(256))) float ll2[C::kQT], lD2[C::kQT];
+  __shared__ __attribute__((aligned(256))) float ll3[NBUF > 3 ? C::kQT : 4], lD3[NBUF > 3 ? C::kQT : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -392,10 +399,143 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       }
     }
   };
+  // Software-pipelined variant for 32 keys per wave.  Per 32-row block qb the work
+  // is G1 (S and dP: 16 MFMAs), J (the softmax-JVP arithmetic: about 130 VALU
+  // instructions) and G2 (dV and dK: 16 MFMAs).  With one wave per SIMD nothing
+  // else hides J, so the tile runs
+  //   G1(0) | G1(1) with J(0) | G2(0) with J(1) | G2(1)
+  // and scheduling groups interleave the VALU work between the MFMAs of the same
+  // phase (MFMA and VALU of one wave overlap when they are independent).
+  struct RowOps {
+    u32x4 aq[D / 16], ad[D / 16];
+    f32x4 lse4[4], d4[4];  // rows 32qb + 8g + 4hi + 0..3 for register group g
+  };
+  struct TrOps {
+    vec8 adt[2][D / 32], aqt[2][D / 32];
+  };
+  auto read_rows = [&](RowOps& o, int qb, const char* qb_, const char* db_, const float* ll,
+                       const float* lD) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      o.aq[c] = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
+      o.ad[c] = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      o.lse4[g] = *(const f32x4*)&ll[32 * qb + 8 * g + 4 * hi];
+      o.d4[g] = *(const f32x4*)&lD[32 * qb + 8 * g + 4 * hi];
+    }
+  };
+  auto read_tr = [&](TrOps& o, int qb, const char* qb_, const char* db_)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int cq = 0; cq < 2; ++cq) {
+      const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        o.adt[cq][t] = join8<T>(lds_read_tr4(db_ + rowb + toff[t]), lds_read_tr4(db_ + rowb + toff8[t]));
+        o.aqt[cq][t] = join8<T>(lds_read_tr4(qb_ + rowb + toff[t]), lds_read_tr4(qb_ + rowb + toff8[t]));
+      }
+    }
+  };
+  auto g1 = [&](const RowOps& o, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      s = M::mma32(as_vec8<T>(o.aq[c]), kf[0][c], s);
+      dp = M::mma32(as_vec8<T>(o.ad[c]), vf[0][c], dp);
+    }
+  };
+  auto jvp = [&](auto mask_c, int i0, int qb, const RowOps& o, const f32x16& s, const f32x16& dp,
+                 vec8 (&pp)[2], vec8 (&ps)[2]) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    const int key = kw + l32;
+#pragma unroll
+    for (int cq = 0; cq < 2; ++cq) {
+      float p8[8], d8[8];
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int g = 2 * cq + g2;
+        const int ql = 32 * qb + 8 * g + 4 * hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float pv = fast_exp2(fmaf(s[r], scale_log2, -o.lse4[g][e]));
+          if (MASK && key > i0 + ql + e) pv = 0.f;
+          p8[4 * g2 + e] = pv;
+          d8[4 * g2 + e] = pv * (dp[r] - o.d4[g][e]);
+        }
+      }
+      pp[cq] = pack8<T>(p8);
+      ps[cq] = pack8<T>(d8);
+    }
+  };
+  auto g2 = [&](const TrOps& o, const vec8 (&pp)[2], const vec8 (&ps)[2])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int cq = 0; cq < 2; ++cq)
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) {
+        dv_acc[0][t] = M::mma32(o.adt[cq][t], pp[cq], dv_acc[0][t]);
+        dk_acc[0][t] = M::mma32(o.aqt[cq][t], ps[cq], dk_acc[0][t]);
+      }
+  };
+  // One phase's interleave: n_ds LDS reads and n_v0 VALU first (to cover the first
+  // MFMA's operand latency), then 16 times one MFMA, ds_per LDS reads, v_per VALU.
+  auto interleave16 = [&](auto n_ds_c, auto n_v0_c, auto ds_per_c, auto v_per_c)
+      __attribute__((always_inline)) {
+    constexpr int kVALU = 0x2 | 0x400;  // VALU including transcendental
+    __builtin_amdgcn_sched_group_barrier(0x100, decltype(n_ds_c)::value, 0);
+    __builtin_amdgcn_sched_group_barrier(kVALU, decltype(n_v0_c)::value, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, decltype(ds_per_c)::value, 0);
+      __builtin_amdgcn_sched_group_barrier(kVALU, decltype(v_per_c)::value, 0);
+    }
+  };
+  auto compute_tile_pipe = [&](auto mask_c, int i0, const char* qb_, const char* db_,
+                               const float* ll, const float* lD) __attribute__((always_inline)) {
+    using IC0 = std::integral_constant<int, 0>;
+    RowOps r0, r1;
+    TrOps t0, t1;
+    f32x16 s0, dp0, s1, dp1;
+    vec8 pp0[2], ps0[2], pp1[2], ps1[2];
+    // G1(0)
+    read_rows(r0, 0, qb_, db_, ll, lD);
+    g1(r0, s0, dp0);
+    __builtin_amdgcn_sched_barrier(0);
+    // G1(1) with J(0); block 0's transposed operands are requested here too
+    read_rows(r1, 1, qb_, db_, ll, lD);
+    read_tr(t0, 0, qb_, db_);
+    jvp(mask_c, i0, 0, r0, s0, dp0, pp0, ps0);
+    g1(r1, s1, dp1);
+    interleave16(std::integral_constant<int, 24>{}, std::integral_constant<int, 16>{},
+                 std::integral_constant<int, 2>{}, std::integral_constant<int, 7>{});
+    __builtin_amdgcn_sched_barrier(0);
+    // G2(0) with J(1); block 1's transposed operands
+    read_tr(t1, 1, qb_, db_);
+    jvp(mask_c, i0, 1, r1, s1, dp1, pp1, ps1);
+    g2(t0, pp0, ps0);
+    interleave16(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+                 std::integral_constant<int, 2>{}, std::integral_constant<int, 8>{});
+    __builtin_amdgcn_sched_barrier(0);
+    // G2(1)
+    g2(t1, pp1, ps1);
+    (void)IC0{};
+  };
   auto compute_tile = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
                           const float* lD) __attribute__((always_inline)) {
-    if constexpr (KB == 1) compute_tile_fenced(mask_c, i0, qb_, db_, ll, lD);
-    else compute_tile_wide(mask_c, i0, qb_, db_, ll, lD);
+    if constexpr (KB == 1) {
+      if constexpr (OSATTN_DKDV_PIPE) compute_tile_pipe(mask_c, i0, qb_, db_, ll, lD);
+      else compute_tile_fenced(mask_c, i0, qb_, db_, ll, lD);
+    } else {
+      compute_tile_wide(mask_c, i0, qb_, db_, ll, lD);
+    }
   };
   auto compute = [&](int it, const char* qb_, const char* db_, const float* ll, const float* lD)
       __attribute__((always_inline)) {
@@ -412,21 +552,31 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     constexpr int S = decltype(sc)::value;
     if constexpr (S == 0) fn(lq0, ld0, ll0, lD0);
     else if constexpr (S == 1) fn(lq1, ld1, ll1, lD1);
-    else fn(lq2, ld2, ll2, lD2);
+    else if constexpr (S == 2) fn(lq2, ld2, ll2, lD2);
+    else fn(lq3, ld3, ll3, lD3);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   if (0 < n_iter) stage(I0{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd) { issue(0, a, d, l, dd); });
   if (NBUF > 2 && 1 < n_iter)
     stage(I1{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd) { issue(1, a, d, l, dd); });
+  if (NBUF > 3 && 2 < n_iter)
+    stage(I2{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd) { issue(2, a, d, l, dd); });
 
   auto step = [&](auto sc, int it) __attribute__((always_inline)) {
     constexpr int S = decltype(sc)::value;
     constexpr int SN = (S + NBUF - 1) % NBUF;  // receives tile it + NBUF - 1
-    // Tile `it` has landed once at most the next tile's loads are outstanding.
-    if (NBUF > 2 && it + 1 < n_iter) {
-      if (wave == 0) wait_vmcnt<2 * C::kCPW + 2>();
-      else wait_vmcnt<2 * C::kCPW>();
+    // Tile `it` has landed once at most the loads of the tiles issued after it
+    // (up to NBUF - 2 of them) are outstanding.
+    constexpr int kPer = 2 * C::kCPW;  // loads per tile and wave (+2 on wave 0)
+    const int ahead = min(NBUF - 2, n_iter - 1 - it);
+    if (NBUF > 3 && ahead >= 2) {
+      if (wave == 0) wait_vmcnt<2 * (kPer + 2)>();
+      else wait_vmcnt<2 * kPer>();
+    } else if (NBUF > 2 && ahead >= 1) {
+      if (wave == 0) wait_vmcnt<kPer + 2>();
+      else wait_vmcnt<kPer>();
     } else {
       wait_vmcnt<0>();
     }
@@ -443,7 +593,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     step(I0{}, it);
     if (it + 1 < n_iter) step(I1{}, it + 1);
     if constexpr (NBUF > 2)
-      if (it + 2 < n_iter) step(std::integral_constant<int, 2>{}, it + 2);
+      if (it + 2 < n_iter) step(I2{}, it + 2);
+    if constexpr (NBUF > 3)
+      if (it + 3 < n_iter) step(std::integral_constant<int, 3>{}, it + 3);
   }
 
   // Store: lane = key, register r of tile t = column 32t + 8(r/4) + 4hi + r%4.
@@ -498,13 +650,15 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   using C = DqCfg<D, NBUF>;
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
-  static_assert(NBUF == 2 || NBUF == 3, "two or three stages");
+  static_assert(NBUF >= 2 && NBUF <= 4, "two to four stages");
   __shared__ __attribute__((aligned(1024))) uint16_t lk0[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lv0[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lk1[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lv1[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lk2[NBUF > 2 ? C::kTileElems : 8];
   __shared__ __attribute__((aligned(1024))) uint16_t lv2[NBUF > 2 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lk3[NBUF > 3 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv3[NBUF > 3 ? C::kTileElems : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -632,22 +786,30 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     constexpr int S = decltype(sc)::value;
     if constexpr (S == 0) return lk0;
     else if constexpr (S == 1) return lk1;
-    else return lk2;
+    else if constexpr (S == 2) return lk2;
+    else return lk3;
   };
   auto stage_v = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
     constexpr int S = decltype(sc)::value;
     if constexpr (S == 0) return lv0;
     else if constexpr (S == 1) return lv1;
-    else return lv2;
+    else if constexpr (S == 2) return lv2;
+    else return lv3;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   if (0 < n_kt) issue(0, stage_k(I0{}), stage_v(I0{}));
   if (NBUF > 2 && 1 < n_kt) issue(1, stage_k(I1{}), stage_v(I1{}));
+  if (NBUF > 3 && 2 < n_kt) issue(2, stage_k(I2{}), stage_v(I2{}));
 
   auto step = [&](auto sc, int kt) __attribute__((always_inline)) {
     constexpr int SN = (decltype(sc)::value + NBUF - 1) % NBUF;
-    if (NBUF > 2 && kt + 1 < n_kt) wait_vmcnt<2 * C::kCPW>();
+    // Tile kt has landed once at most the loads of the (up to NBUF - 2) tiles
+    // issued after it are outstanding.
+    const int ahead = min(NBUF - 2, n_kt - 1 - kt);
+    if (NBUF > 3 && ahead >= 2) wait_vmcnt<4 * C::kCPW>();
+    else if (NBUF > 2 && ahead >= 1) wait_vmcnt<2 * C::kCPW>();
     else wait_vmcnt<0>();
     block_barrier();
     if (kt + NBUF - 1 < n_kt)
@@ -659,7 +821,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     step(I0{}, kt);
     if (kt + 1 < n_kt) step(I1{}, kt + 1);
     if constexpr (NBUF > 2)
-      if (kt + 2 < n_kt) step(std::integral_constant<int, 2>{}, kt + 2);
+      if (kt + 2 < n_kt) step(I2{}, kt + 2);
+    if constexpr (NBUF > 3)
+      if (kt + 3 < n_kt) step(std::integral_constant<int, 3>{}, kt + 3);
   }
 
   if (row < N) {
@@ -699,16 +863,20 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a) {
 #ifndef OSATTN_BWD_NBUF
 #define OSATTN_BWD_NBUF 3
 #endif
+#ifndef OSATTN_DKDV_NBUF
+#define OSATTN_DKDV_NBUF 4
+#endif
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t bwd_t(const BwdArgs& a) {
   constexpr int NB = OSATTN_BWD_NBUF;
+  constexpr int NBK = OSATTN_DKDV_NBUF;
   const float sl2 = a.scale * kLog2e;
   if (a.stages & kStageDkdv) {
-    using C = DkdvCfg<D, NB>;
+    using C = DkdvCfg<D, NBK>;
     const int n_kt = (a.N + C::kKeys - 1) / C::kKeys;
     const long long blocks = (long long)n_kt * a.B * a.Hkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NB, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NBK, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0,
                        (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse2, a.dvec,
                        (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.Hkv, a.N, n_kt, a.scale, sl2);

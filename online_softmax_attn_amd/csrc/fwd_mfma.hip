@@ -70,13 +70,15 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // One array per pipeline stage: with the stage known at compile time, the
   // compiler can tell that reads of one stage do not alias the DMA writes still in
   // flight into the others, and inserts no wait for them.
-  static_assert(NBUF == 2 || NBUF == 3, "two or three stages");
+  static_assert(NBUF >= 2 && NBUF <= 4, "two to four stages");
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[C::kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k2[NBUF > 2 ? C::kTileElems : 8];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v2[NBUF > 2 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k3[NBUF > 3 ? C::kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v3[NBUF > 3 ? C::kTileElems : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -271,29 +273,51 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
   };
 
+  auto stage_k = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return lds_k0;
+    else if constexpr (S == 1) return lds_k1;
+    else if constexpr (S == 2) return lds_k2;
+    else return lds_k3;
+  };
+  auto stage_v = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return lds_v0;
+    else if constexpr (S == 1) return lds_v1;
+    else if constexpr (S == 2) return lds_v2;
+    else return lds_v3;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   if (0 < n_kt) issue(0, lds_k0, lds_v0);
   if (NBUF > 2 && 1 < n_kt) issue(1, lds_k1, lds_v1);
+  if (NBUF > 3 && 2 < n_kt) issue(2, lds_k2, lds_v2);
 
   // One pipeline step for tile kt held in stage S (compile-time).
   auto step = [&](auto stage_c, int kt) __attribute__((always_inline)) {
-    constexpr int S = decltype(stage_c)::value;
-    uint16_t* lk = S == 0 ? lds_k0 : (S == 1 ? lds_k1 : lds_k2);
-    uint16_t* lv = S == 0 ? lds_v0 : (S == 1 ? lds_v1 : lds_v2);
-    constexpr int SN = (S + NBUF - 1) % NBUF;  // stage that receives tile kt + NBUF - 1
-    uint16_t* nk = SN == 0 ? lds_k0 : (SN == 1 ? lds_k1 : lds_k2);
-    uint16_t* nv = SN == 0 ? lds_v0 : (SN == 1 ? lds_v1 : lds_v2);
-    // Tile kt has landed once at most the later tiles' loads are outstanding.
-    if (NBUF > 2 && kt + 1 < n_kt) wait_vmcnt<(NBUF > 2 ? (NBUF - 2) * 2 * C::kCPW : 0)>();
+    constexpr int SN = (decltype(stage_c)::value + NBUF - 1) % NBUF;  // receives tile kt + NBUF - 1
+    uint16_t* lk = stage_k(stage_c);
+    uint16_t* lv = stage_v(stage_c);
+    uint16_t* nk = stage_k(std::integral_constant<int, SN>{});
+    uint16_t* nv = stage_v(std::integral_constant<int, SN>{});
+    // Tile kt has landed once at most the loads of the (up to NBUF - 2) tiles
+    // issued after it are outstanding.
+    const int ahead = min(NBUF - 2, n_kt - 1 - kt);
+    if (NBUF > 3 && ahead >= 2) wait_vmcnt<4 * C::kCPW>();
+    else if (NBUF > 2 && ahead >= 1) wait_vmcnt<2 * C::kCPW>();
     else wait_vmcnt<0>();
     block_barrier();  // every wave's share of tile kt is in LDS; tile kt-1 is free
     if (kt + NBUF - 1 < n_kt) issue(kt + NBUF - 1, nk, nv);
     compute(kt, (const char*)lk, (const char*)lv);
   };
   for (int kt = 0; kt < n_kt; kt += NBUF) {
-    step(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < n_kt) step(std::integral_constant<int, 1>{}, kt + 1);
+    step(I0{}, kt);
+    if (kt + 1 < n_kt) step(I1{}, kt + 1);
     if constexpr (NBUF > 2)
-      if (kt + 2 < n_kt) step(std::integral_constant<int, 2>{}, kt + 2);
+      if (kt + 2 < n_kt) step(I2{}, kt + 2);
+    if constexpr (NBUF > 3)
+      if (kt + 3 < n_kt) step(std::integral_constant<int, 3>{}, kt + 3);
   }
 
   // ---- final normalisation: O = Ot / l, LSE = ln(2) * (m + log2 l) ---------------
