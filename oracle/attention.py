@@ -34,9 +34,26 @@ n_rep = H / Hkv (contiguous groups, as in the SnapKV ``view(b, n_kv_head, n_rep,
 grouping on the KV-cache page); dK and dV of a key/value head are the sums over the
 n_rep query heads of its group.
 
-Layouts: q, o, do, dq are [B, H, N, d]; k, v, dk, dv are [B, Hkv, N, d]; lse is
-[B, H, N].  Inputs are upcast to float64 exactly as given (the GPU receives the
+Layouts: q, o, do, dq are [B, H, Nq, d]; k, v, dk, dv are [B, Hkv, Nk, d]; lse is
+[B, H, Nq].  Inputs are upcast to float64 exactly as given (the GPU receives the
 dtype-rounded tensors; the oracle receives those same values).
+
+Queries and keys may differ in number (decoding: a few new queries against a long
+key/value history).  The pages only draw the square causal mask, so the reading
+taken for Nq != Nk is the bottom-right alignment: the Nq queries are the last Nq
+positions of the sequence, query i sits at position i + (Nk - Nq) and sees keys
+0 .. i + Nk - Nq.  For Nq == Nk this is the square mask above.
+
+Split-KV merge (ml-notes page, the split-K sparse-attention notes: each key chunk
+keeps its max m, denominator l and unnormalised output o, and rescaling by
+exp(m_s - m) onto a common max makes the merge exact and order-free; the
+attnres-kernel-lab page merges two softmax partitions the same way): with the
+chunk results written as a normalised output O_s = o_s / l_s and a logsumexp
+LSE_s = m_s + ln l_s, the whole-row result is
+
+    LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s,
+
+where a chunk with no visible key has LSE_s = -inf and weight 0.
 
 Large shapes are processed in blocks of complete rows: each row's full set of N
 scores is formed before its softmax, so no online rescaling happens here.
@@ -56,6 +73,8 @@ __all__ = [
     "attention_backward",
     "attention_forward_rows",
     "attention_head",
+    "causal_key_offset",
+    "merge_partials",
 ]
 
 
@@ -74,19 +93,28 @@ def kv_head_of(h: int, H: int, Hkv: int) -> int:
 
 
 def scores(q_rows: np.ndarray, k: np.ndarray, scale: float, causal: bool,
-           row_ids: np.ndarray | None = None) -> np.ndarray:
-    """S = scale * Q K^T for the given query rows against all N keys.
+           row_ids: np.ndarray | None = None, key_offset: int = 0) -> np.ndarray:
+    """S = scale * Q K^T for the given query rows against all Nk keys.
 
-    q_rows is [R, d], k is [N, d]; row_ids are the absolute query indices of the
-    R rows (needed for the causal mask, which keeps key index <= query index).
+    q_rows is [R, d], k is [Nk, d]; row_ids are the query indices of the R rows.
+    The causal mask keeps key index <= query index + key_offset, where key_offset =
+    Nk - Nq places the queries at the end of the key sequence (0 when Nq == Nk).
     """
     s = scale * (q_rows @ k.T)
     if causal:
         if row_ids is None:
             row_ids = np.arange(q_rows.shape[0])
         key_ids = np.arange(k.shape[0])
-        s = np.where(key_ids[None, :] > row_ids[:, None], -np.inf, s)
+        s = np.where(key_ids[None, :] > row_ids[:, None] + key_offset, -np.inf, s)
     return s
+
+
+def causal_key_offset(nq: int, nk: int, causal: bool) -> int:
+    """Nk - Nq: position of query 0 in the key sequence (bottom-right alignment).
+    A causal problem needs Nk >= Nq so that every query sees at least key 0."""
+    if causal and nk < nq:
+        raise ValueError("causal attention needs at least as many keys as queries")
+    return nk - nq
 
 
 def softmax_rows(s: np.ndarray) -> np.ndarray:
@@ -121,7 +149,8 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     are this query head's contributions (a GQA group sums them).
     """
     n = q.shape[0]
-    o = np.empty_like(q)
+    off = causal_key_offset(n, k.shape[0], causal)
+    o = np.empty((n, v.shape[1]))
     lse = np.empty(n)
     want_grad = do is not None
     if want_grad:
@@ -131,7 +160,7 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
         dvec = np.empty(n)
     for r0 in range(0, n, row_block):
         rows = np.arange(r0, min(n, r0 + row_block))
-        s = scores(q[rows], k, scale, causal, rows)
+        s = scores(q[rows], k, scale, causal, rows, off)
         p = softmax_rows(s)
         o[rows] = p @ v
         lse[rows] = logsumexp_rows(s)
@@ -149,7 +178,8 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 def attention_forward(q, k, v, scale: float, causal: bool = False,
                       row_block: int = 1024):
-    """O [B,H,N,d] and LSE [B,H,N] in float64 for the whole batch."""
+    """O [B,H,Nq,d] and LSE [B,H,Nq] in float64 for the whole batch (k, v may
+    hold a different number of rows Nk; see causal_key_offset)."""
     B, H, N, d = q.shape
     Hkv = k.shape[1]
     o = np.empty((B, H, N, d))
@@ -212,9 +242,25 @@ def attention_forward_rows(q, k, v, scale: float, causal: bool, picks):
         kg, vg = _f64(k[b, g]), _f64(v[b, g])
         idx = np.array([i for _, i in items])
         qi = _f64(q[b, h])[idx] if isinstance(q, np.ndarray) else _f64(q[b, h, idx])
-        s = scores(qi, kg, scale, causal, idx)
+        s = scores(qi, kg, scale, causal, idx, causal_key_offset(q.shape[2], kg.shape[0], causal))
         p = softmax_rows(s)
         for (n, _), o_row, l_row in zip(items, p @ vg, logsumexp_rows(s)):
             o_rows[n] = o_row
             lse_rows[n] = l_row
     return o_rows, lse_rows
+
+
+def merge_partials(o_parts, lse_parts):
+    """Exact merge of per-chunk results: o_parts [S, ..., d], lse_parts [S, ...].
+
+    Chunk s contributes exp(LSE_s - LSE) of its normalised output, LSE being the
+    logsumexp of the chunk LSEs (taken about their max); chunks with LSE_s = -inf
+    (no visible key) get weight zero.  Returns (O, LSE).
+    """
+    o_parts = _f64(o_parts)
+    lse_parts = _f64(lse_parts)
+    m = np.max(lse_parts, axis=0)
+    w = np.exp(lse_parts - m[None])            # 0 for -inf chunks
+    z = np.sum(w, axis=0)
+    o = np.sum(w[..., None] * o_parts, axis=0) / z[..., None]
+    return o, m + np.log(z)

@@ -20,7 +20,8 @@ def _probs(q, k, scale, causal):
     for i in range(n):
         row = []
         for j in range(nk):
-            if causal and j > i:
+            # Query i is position i + nk - n of the sequence (bottom-right alignment).
+            if causal and j > i + nk - n:
                 row.append(None)
             else:
                 row.append(scale * sum(q[i][c] * k[j][c] for c in range(len(q[i]))))

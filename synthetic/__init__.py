@@ -6,7 +6,8 @@ workloads.  Both the HIP path and the CPU oracle consume what it returns (the
 oracle upcasts the same rounded values to float64).
 
 Seeds: tensor t of workload k uses seed 1000*k + t with t = 0 (Q), 1 (K), 2 (V),
-3 (dO).  Point p of the throughput sweep uses 5000 + 10*p + t.  The GQA workload
+3 (dO).  Point p of the throughput sweep uses 5000 + 10*p + t; the decoding
+workloads (fewer queries than keys) use 6000, 6100 and 6200 + t.  The GQA workload
 additionally scales ceil(1%) of all key rows by 8 (exact in bf16), rows picked by
 a seed-4100 permutation over the flattened (batch, kv-head, position) rows, before
 the dtype cast: those rows produce scores far above the rest and move the running
@@ -39,6 +40,11 @@ class Workload:
     k_outlier_scale: float = 8.0
     k_outlier_seed: int = 0
     notes: str = ""
+    Nk: int = 0  # key/value rows; 0 means the same as N (queries)
+
+    @property
+    def nk(self) -> int:
+        return self.Nk or self.N
 
     @property
     def scale(self) -> float:
@@ -50,20 +56,35 @@ class Workload:
 
     @property
     def shape_kv(self):
-        return (self.B, self.Hkv, self.N, self.d)
+        return (self.B, self.Hkv, self.nk, self.d)
 
     def fwd_flop(self) -> float:
-        """4*B*H*N^2*d for the two forward matmuls, halved under a causal mask."""
-        f = 4.0 * self.B * self.H * self.N * self.N * self.d
-        return f / 2 if self.causal else f
+        """4*B*H*N^2*d for the two forward matmuls, halved under a causal mask.  With
+        fewer queries than keys: 4*B*H*d per visible (query, key) pair, the causal
+        mask being aligned bottom-right (query i sees keys 0 .. i + Nk - N)."""
+        if self.nk == self.N:
+            f = 4.0 * self.B * self.H * self.N * self.N * self.d
+            return f / 2 if self.causal else f
+        pairs = self.N * self.nk
+        if self.causal:
+            pairs -= self.N * (self.N - 1) // 2
+        return 4.0 * self.B * self.H * pairs * self.d
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V: what a decoding step must read at least once."""
+        e = DTYPES[self.dtype].itemsize
+        return 2 * self.B * self.Hkv * self.nk * self.d * e
 
     def bwd_flop(self) -> float:
         """Five N^2*d matmuls (S recompute, dV, dP, dK, dQ): 2.5x the forward."""
         return 2.5 * self.fwd_flop()
 
     def describe(self) -> dict:
-        return {"workload": self.name, "dtype": self.dtype, "B": self.B, "H": self.H,
-                "Hkv": self.Hkv, "N": self.N, "d": self.d, "causal": self.causal}
+        out = {"workload": self.name, "dtype": self.dtype, "B": self.B, "H": self.H,
+               "Hkv": self.Hkv, "N": self.N, "d": self.d, "causal": self.causal}
+        if self.nk != self.N:
+            out["Nq"], out["Nk"] = out.pop("N"), self.nk
+        return out
 
 
 SWEEP_N = (1024, 2048, 4096, 8192, 16384)
@@ -95,6 +116,19 @@ WORKLOADS = {
 for _w in sweep_points():
     WORKLOADS[_w.name] = _w
 
+# Decoding with a long key/value history (split-KV forward): one new query per head,
+# or a block of 16 (speculative / chunked decoding), against 16384 cached positions;
+# causal with the queries at the end of the sequence.
+DECODE = {
+    "decode_bf16_gqa_q1": Workload("decode_bf16_gqa_B4_H32_Hkv8_Nq1_Nk16384_d128", "bf16", 4, 32,
+                                   8, 1, 128, True, False, 6000, Nk=16384),
+    "decode_bf16_gqa_q16": Workload("decode_bf16_gqa_B4_H32_Hkv8_Nq16_Nk16384_d128", "bf16", 4,
+                                    32, 8, 16, 128, True, False, 6100, Nk=16384),
+    "decode_fp16_mha_q1": Workload("decode_fp16_mha_B8_H16_Nq1_Nk8192_d64", "fp16", 8, 16, 16, 1,
+                                   64, False, False, 6200, Nk=8192),
+}
+WORKLOADS.update(DECODE)
+
 # The throughput headline: bf16, non-causal, B*H = 64, N = 8192, d = 128.
 HEADLINE = WORKLOADS["sweep_bf16_B4_H16_N8192_d128"]
 
@@ -111,7 +145,7 @@ def make_inputs(w: Workload, with_grad: bool | None = None) -> dict:
     k = randn(w.shape_kv, w.seed_base + 1)
     v = randn(w.shape_kv, w.seed_base + 2)
     if w.k_outlier_frac > 0:
-        rows = w.B * w.Hkv * w.N
+        rows = w.B * w.Hkv * w.nk
         n_sel = math.ceil(w.k_outlier_frac * rows)
         g = torch.Generator(device="cpu").manual_seed(w.k_outlier_seed)
         sel = torch.randperm(rows, generator=g)[:n_sel]
@@ -126,9 +160,11 @@ def make_inputs(w: Workload, with_grad: bool | None = None) -> dict:
 
 def custom(dtype: str, B: int, H: int, Hkv: int, N: int, d: int, causal: bool,
            seed_base: int, **kw) -> Workload:
-    """A small ad-hoc workload (edge cases in tests)."""
-    return Workload(f"case_{dtype}_B{B}_H{H}_Hkv{Hkv}_N{N}_d{d}_{'c' if causal else 'nc'}",
-                    dtype, B, H, Hkv, N, d, causal, True, seed_base, **kw)
+    """A small ad-hoc workload (edge cases in tests); Nk=... for fewer queries than keys."""
+    nk = kw.get("Nk", 0)
+    tag = f"N{N}" if not nk else f"Nq{N}_Nk{nk}"
+    return Workload(f"case_{dtype}_B{B}_H{H}_Hkv{Hkv}_{tag}_d{d}_{'c' if causal else 'nc'}",
+                    dtype, B, H, Hkv, N, d, causal, not nk, seed_base, **kw)
 
 
 def with_dtype(w: Workload, dtype: str) -> Workload:

@@ -293,6 +293,88 @@ def pin_row_blocking(seed=14, causal=True):
     return max(np.max(np.abs(a[n] - b[n])) for n in ("o", "lse", "dq", "dk", "dv", "D"))
 
 
+# --- queries fewer than keys (decoding) and the split-KV merge ------------------------
+
+def rect_case(seed, B=1, H=2, Hkv=1, Nq=3, Nk=9, d=4):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((B, H, Nq, d))
+    k = r.standard_normal((B, Hkv, Nk, d))
+    v = r.standard_normal((B, Hkv, Nk, d))
+    return q, k, v, 1.0 / math.sqrt(d)
+
+
+def pin_rect_causal_is_tail_of_square(seed=20, Nq=3, Nk=9):
+    """Bottom-right alignment: Nq queries against Nk keys give the last Nq rows of the
+    square causal problem whose final query rows are those queries."""
+    q, k, v, scale = rect_case(seed, 1, 2, 1, Nq, Nk)
+    r = np.random.default_rng(seed + 1)
+    q_full = np.concatenate([r.standard_normal((1, 2, Nk - Nq, q.shape[-1])), q], axis=2)
+    o_sq, lse_sq = A.attention_forward(q_full, k, v, scale, causal=True)
+    o, lse = A.attention_forward(q, k, v, scale, causal=True)
+    return max(np.max(np.abs(o - o_sq[:, :, Nk - Nq:])), np.max(np.abs(lse - lse_sq[:, :, Nk - Nq:])))
+
+
+def pin_decode_row_sees_all_keys(seed=21, Nk=10):
+    """A single causal query is the last position: it sees every key (equals non-causal),
+    and with Nk = 1 its output is v_0."""
+    q, k, v, scale = rect_case(seed, 1, 2, 2, 1, Nk)
+    o_c, lse_c = A.attention_forward(q, k, v, scale, causal=True)
+    o_n, lse_n = A.attention_forward(q, k, v, scale, causal=False)
+    o1, _ = A.attention_forward(q, k[:, :, :1], v[:, :, :1], scale, causal=True)
+    return max(np.max(np.abs(o_c - o_n)), np.max(np.abs(lse_c - lse_n)),
+               np.max(np.abs(o1 - v[:, :, :1])))
+
+
+def pin_brute_force_rect(seed=22, Nq=3, Nk=7, d=3, causal=True):
+    """The pure-Python loops (their own mask test) against the oracle for Nq < Nk."""
+    q, k, v, scale = rect_case(seed, 1, 1, 1, Nq, Nk, d)
+    o, lse = A.attention_forward(q, k, v, scale, causal)
+    o_b, lse_b = BR.forward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), scale, causal)
+    return max(np.max(np.abs(o[0, 0] - np.array(o_b))), np.max(np.abs(lse[0, 0] - np.array(lse_b))))
+
+
+def _chunk_results(q, k, v, scale, causal, bounds):
+    """Per-chunk (O_s, LSE_s) of one head computed on the chunk's keys alone, with
+    the causal mask at the keys' absolute positions; rows that see none of the
+    chunk's keys get O_s = 0 and LSE_s = -inf."""
+    nq, nk = q.shape[0], k.shape[0]
+    off = nk - nq
+    o_parts, lse_parts = [], []
+    for a, b in bounds:
+        s = A.scores(q, k[a:b], scale, causal, np.arange(nq), off - a)
+        vis = np.isfinite(s).any(axis=1)
+        o_s = np.zeros((nq, v.shape[1]))
+        l_s = np.full(nq, -np.inf)
+        if vis.any():
+            o_s[vis] = A.softmax_rows(s[vis]) @ v[a:b]
+            l_s[vis] = A.logsumexp_rows(s[vis])
+        o_parts.append(o_s)
+        lse_parts.append(l_s)
+    return np.array(o_parts), np.array(lse_parts)
+
+
+def pin_merge_exact(seed=23, Nq=4, Nk=23, causal=False, order=None):
+    """Splitting the keys into chunks and merging the chunk results gives the whole-row
+    attention, for uneven chunks, in any order, and (causal) with chunks that some
+    rows cannot see at all."""
+    q, k, v, scale = rect_case(seed, 1, 1, 1, Nq, Nk, 5)
+    bounds = [(0, 5), (5, 6), (6, 14), (14, 20), (20, 23)]
+    if order is not None:
+        bounds = [bounds[i] for i in order]
+    o_p, l_p = _chunk_results(q[0, 0], k[0, 0], v[0, 0], scale, causal, bounds)
+    o_m, lse_m = A.merge_partials(o_p, l_p)
+    o, lse = A.attention_forward(q, k, v, scale, causal)
+    return max(np.max(np.abs(o_m - o[0, 0])), np.max(np.abs(lse_m - lse[0, 0])))
+
+
+def pin_merge_single_chunk(seed=24):
+    """One chunk holding every key: the merge returns it unchanged."""
+    q, k, v, scale = rect_case(seed, 1, 1, 1, 3, 8, 4)
+    o, lse = A.attention_forward(q, k, v, scale, False)
+    o_m, lse_m = A.merge_partials(o[0, 0][None], lse[0, 0][None])
+    return max(np.max(np.abs(o_m - o[0, 0])), np.max(np.abs(lse_m - lse[0, 0])))
+
+
 ALL_PINS = {
     "worked_example_walk": (pin_worked_example_walk, 1e-12),
     "worked_example_scores": (pin_worked_example_scores, 0.0),
@@ -319,4 +401,13 @@ ALL_PINS = {
     "torch_library_causal_gqa": (lambda: pin_torch_library(causal=True, gqa=True), 1e-12),
     "row_sampling": (pin_row_sampling, 1e-13),
     "row_blocking": (pin_row_blocking, 1e-13),
+    "rect_causal_is_tail_of_square": (pin_rect_causal_is_tail_of_square, 1e-13),
+    "rect_causal_one_query": (lambda: pin_rect_causal_is_tail_of_square(Nq=1, Nk=6), 1e-13),
+    "decode_row_sees_all_keys": (pin_decode_row_sees_all_keys, 1e-13),
+    "brute_force_rect_causal": (pin_brute_force_rect, 1e-13),
+    "brute_force_rect": (lambda: pin_brute_force_rect(causal=False, Nq=2, Nk=5), 1e-13),
+    "merge_exact": (pin_merge_exact, 1e-13),
+    "merge_exact_causal": (lambda: pin_merge_exact(causal=True, Nq=9), 1e-13),
+    "merge_exact_reordered": (lambda: pin_merge_exact(causal=True, Nq=9, order=[3, 0, 4, 2, 1]), 1e-13),
+    "merge_single_chunk": (pin_merge_single_chunk, 1e-14),
 }

@@ -50,10 +50,17 @@ MUTANTS = {
     "jvp_drops_dot": ("softmax_backward_rows", lambda p, g: p * g),
     "jvp_sign_flip": ("softmax_backward_rows",
                       lambda p, g: p * (np.sum(p * g, axis=-1, keepdims=True) - g)),
-    "scores_no_scale": ("scores", lambda q, k, scale, causal, row_ids=None:
-                        P_orig_scores(q, k, 1.0, causal, row_ids)),
-    "causal_off_by_one": ("scores", lambda q, k, scale, causal, row_ids=None:
-                          _shifted_mask(q, k, scale, causal, row_ids)),
+    "scores_no_scale": ("scores", lambda q, k, scale, causal, row_ids=None, key_offset=0:
+                        P_orig_scores(q, k, 1.0, causal, row_ids, key_offset)),
+    "causal_off_by_one": ("scores", lambda q, k, scale, causal, row_ids=None, key_offset=0:
+                          _shifted_mask(q, k, scale, causal, row_ids, key_offset + 1)),
+    "causal_top_left_for_rect": ("scores", lambda q, k, scale, causal, row_ids=None, key_offset=0:
+                                 P_orig_scores(q, k, scale, causal, row_ids, 0)),
+    "causal_offset_sign": ("scores", lambda q, k, scale, causal, row_ids=None, key_offset=0:
+                           P_orig_scores(q, k, scale, causal, row_ids, -key_offset)),
+    "merge_unnormalised": ("merge_partials", lambda o, l: _bad_merge(o, l, "unnormalised")),
+    "merge_plain_mean": ("merge_partials", lambda o, l: _bad_merge(o, l, "mean")),
+    "merge_lse_is_max": ("merge_partials", lambda o, l: _bad_merge(o, l, "lse_max")),
     "lse_drops_max": ("logsumexp_rows",
                       lambda s: np.log(np.sum(np.exp(s - np.max(s, axis=-1, keepdims=True)), axis=-1))),
     "gqa_modulo_map": ("kv_head_of", lambda h, H, Hkv: h % Hkv),
@@ -67,13 +74,25 @@ MUTANTS = {
 P_orig_scores = A.scores
 
 
-def _shifted_mask(q, k, scale, causal, row_ids):
+def _shifted_mask(q, k, scale, causal, row_ids, key_offset):
     s = scale * (q @ k.T)
     if causal:
         if row_ids is None:
             row_ids = np.arange(q.shape[0])
-        s = np.where(np.arange(k.shape[0])[None, :] > row_ids[:, None] + 1, -np.inf, s)
+        s = np.where(np.arange(k.shape[0])[None, :] > row_ids[:, None] + key_offset, -np.inf, s)
     return s
+
+
+def _bad_merge(o_parts, lse_parts, how):
+    o_parts, lse_parts = np.asarray(o_parts, float), np.asarray(lse_parts, float)
+    m = np.max(lse_parts, axis=0)
+    w = np.exp(lse_parts - m[None])
+    z = np.sum(w, axis=0)
+    if how == "unnormalised":
+        return np.sum(w[..., None] * o_parts, axis=0), m + np.log(z)
+    if how == "mean":
+        return np.mean(o_parts, axis=0), m + np.log(z)
+    return np.sum(w[..., None] * o_parts, axis=0) / z[..., None], m
 
 
 def _failing_pins():
