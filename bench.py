@@ -1,7 +1,7 @@
 """Throughput benchmark of the fused attention path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--sweep]
+                    [--no-cpu-baseline] [--sweep] [--decode]
 
 A step is one pass of the whole path over one batch of resident synthetic input:
 the forward kernel (O and LSE) followed by the backward (D preprocess, dK/dV
@@ -183,6 +183,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time every point of the bf16 sweep (one JSON line each)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the split-KV forward on the decoding workloads (one line each)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 512 MiB device copies (for scaling HBM counters)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -222,6 +224,10 @@ def main():
         for w in S.sweep_points():
             print(json.dumps(run_one(w, args, osa, torch, with_cpu=False)), flush=True)
         return
+    if args.decode:
+        for w in S.DECODE.values():
+            print(json.dumps(run_decode(w, args, osa, torch)), flush=True)
+        return
     w = S.WORKLOADS[args.workload] if args.workload else S.HEADLINE
     print(json.dumps(run_one(w, args, osa, torch, with_cpu=not args.no_cpu_baseline)), flush=True)
 
@@ -255,6 +261,48 @@ def kernel_table(w):
          "work": 0.2 * bwd_f, "unit": "flop", "sources": bsrc, "executed_work": 0.6 * bwd_f,
          "bytes": 3 * qb + 2 * kb + 2 * rb},
     ]
+
+
+def run_decode(w, args, osa, torch):
+    """One split-KV forward (chunk kernel + merge kernel) per step on a decoding
+    workload; HBM-bound, so the roofline is bytes: K and V read once, plus Q read and
+    O and LSE written (the fp32 chunk results in the workspace are overhead)."""
+    import synthetic as S
+
+    inp = S.make_inputs(w, with_grad=False)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), device="cuda", dtype=torch.float32)
+    need = osa.attn_fwd_splitkv_workspace_bytes(w.B, w.H, w.Hkv, w.N, w.nk, w.d, w.causal, q.dtype)
+    ws = torch.empty(need, device="cuda", dtype=torch.uint8)
+
+    def step():
+        osa.attn_fwd_splitkv(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    st = stats([e[0].elapsed_time(e[1]) for e in ev])
+    e = q.element_size()
+    algo = w.kv_bytes() + 2 * q.numel() * e + lse.numel() * 4
+    gbs = algo / (st["mean"] * 1e-3) / 1e9
+    return {"metric": "split-KV decode forward: compulsory HBM bytes per second",
+            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(st["mean"], 4), "higher_is_better": True,
+            "dtype": w.dtype, "data": "synthetic", "config": w.describe(),
+            "tflops": round(w.fwd_flop() / (st["mean"] * 1e-3) / 1e12, 2),
+            "workspace_bytes": need,
+            "roofline": {"bound": "hbm", "kernel": "splitkv_partial_kernel + splitkv_merge_kernel",
+                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": algo,
+                         "ms": {k2: round(x, 4) for k2, x in st.items()}}}
 
 
 def stats(xs):

@@ -129,6 +129,38 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                 int dtype, const void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/*
+ * Split-KV forward for few queries against many keys (decoding).
+ *
+ * Same operation as attn_fwd with Nq queries and Nk keys/values per head:
+ *     q, o : [B][H][Nq][d]      k, v : [B][Hkv][Nk][d]      lse : [B][H][Nq]
+ * The causal mask, when asked for, is aligned bottom-right: query i is position
+ * i + Nk - Nq of the sequence and sees keys 0 .. i + Nk - Nq (for Nq == Nk this
+ * is attn_fwd's mask); causal calls need Nk >= Nq.
+ *
+ * The key axis is cut into n_splits chunks computed in parallel; each chunk
+ * keeps the online-softmax state (running max, denominator, unnormalised
+ * output) over its keys and the chunks are then merged exactly by rescaling
+ * them to a common max (ml-notes page, the split-K notes of the sparse
+ * attention kernel; attnres-kernel-lab page, the exact two-partition merge;
+ * FlashAttention-2 page, inner loop).  n_splits = 0 lets the library choose;
+ * a request above one chunk per 32 keys is capped there.
+ *
+ * dtype must be ATTN_F16 or ATTN_BF16 (ATTN_ERR_DTYPE otherwise); d in {64, 128}.
+ * `workspace` is caller-owned device memory of at least
+ * attn_fwd_splitkv_workspace_bytes() for the same arguments (fp32 chunk
+ * outputs and logsumexps); its contents on entry do not matter.  Calls that may
+ * overlap in time need distinct workspaces.  Returns ATTN_OK or a negative
+ * attn_status_t (ATTN_ERR_SHAPE also for n_splits < 0 and causal with Nk < Nq);
+ * on a validation error nothing is launched.
+ */
+size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d,
+                                        int causal, int dtype, int n_splits);
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                     int causal, int dtype, int n_splits, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* attn_status_string(int status);
 

@@ -33,6 +33,8 @@ __all__ = [
     "attn_bwd_dkdv",
     "attn_bwd_dq",
     "new_bwd_workspace",
+    "attn_fwd_splitkv",
+    "attn_fwd_splitkv_workspace_bytes",
     "status_string",
     "library",
     "library_path",
@@ -59,7 +61,8 @@ STATUS = {
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
-            "attn_bwd_dkdv", "attn_bwd_dq", "attn_status_string")
+            "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
+            "attn_status_string")
 
 _lib = None
 
@@ -96,6 +99,10 @@ def library() -> ctypes.CDLL:
     lib.attn_bwd_dkdv.restype = i
     lib.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.attn_bwd_dq.restype = i
+    lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.attn_fwd_splitkv.restype = i
+    lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
+    lib.attn_fwd_splitkv_workspace_bytes.restype = sz
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_string.argtypes = [i]
@@ -261,3 +268,45 @@ def attn_bwd_dq(q, k, v, o, lse, do, workspace, causal: bool = False,
     if st != 0:
         raise AttnError(st, "attn_bwd_dq")
     return dq
+
+
+def attn_fwd_splitkv_workspace_bytes(B, H, Hkv, Nq, Nk, d, causal, dtype, n_splits=0) -> int:
+    code = DTYPE_CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(library().attn_fwd_splitkv_workspace_bytes(B, H, Hkv, Nq, Nk, d, int(bool(causal)),
+                                                          code, int(n_splits)))
+
+
+def attn_fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, n_splits: int = 0,
+                     out=None, lse=None, workspace=None):
+    """Split-KV forward: q [B,H,Nq,d] against k/v [B,Hkv,Nk,d] (Nq may be much smaller
+    than Nk; the causal mask is aligned bottom-right).  fp16/bf16 only."""
+    lib = library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    if q.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,H,Nq,d] and k, v [B,Hkv,Nk,d]")
+    B, H, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32) if lse is None else lse
+    _check_dev("out", out, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    if out.shape != q.shape or lse.shape != (B, H, Nq):
+        raise ValueError("out / lse have the wrong shape")
+    if workspace is None:
+        need = attn_fwd_splitkv_workspace_bytes(B, H, Hkv, Nq, Nk, d, causal, q.dtype, n_splits)
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _check_dev("workspace", workspace)
+    st = lib.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                              DTYPE_CODES[q.dtype], int(n_splits), workspace.data_ptr(),
+                              _ws_bytes(workspace), _stream_handle(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_splitkv")
+    return out, lse

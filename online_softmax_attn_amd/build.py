@@ -17,7 +17,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libosattn.so")
-SOURCES = ["api.hip", "fwd_mfma.hip", "bwd_mfma.hip", "f32_kernels.hip"]
+SOURCES = ["api.hip", "fwd_mfma.hip", "bwd_mfma.hip", "f32_kernels.hip", "splitkv.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

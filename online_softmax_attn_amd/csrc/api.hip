@@ -146,6 +146,83 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, c
                                   d, scale, causal, dtype, workspace, stream, osattn::kStageDq));
 }
 
+namespace {
+
+struct SplitPlan {
+  int n_splits;    // non-empty chunks
+  int split_keys;  // keys per chunk (multiple of 32)
+};
+
+// Chunking of the key axis.  Requested n_splits >= 1 is honoured up to one chunk
+// per 32-key tile; 0 picks enough chunks for about 1024 single-wave workgroups,
+// keeping at least four tiles per chunk.
+SplitPlan split_plan(int B, int Hkv, int n_rep, int Nq, int Nk, int n_splits) {
+  const long long tiles = (Nk + 31) / 32;
+  const long long rowblocks = ((long long)n_rep * Nq + 31) / 32;
+  long long want = n_splits;
+  if (want <= 0) {
+    const long long base = (long long)B * Hkv * rowblocks;
+    want = (1024 + base - 1) / base;
+    want = want > tiles / 4 ? tiles / 4 : want;
+  }
+  if (want > tiles) want = tiles;
+  if (want < 1) want = 1;
+  const long long per_tiles = (tiles + want - 1) / want;
+  SplitPlan p;
+  p.split_keys = (int)(per_tiles * 32);
+  p.n_splits = (int)((Nk + p.split_keys - 1) / p.split_keys);
+  return p;
+}
+
+int validate_split(int B, int H, int Hkv, int Nq, int Nk, int d, int causal, int dtype,
+                   int n_splits) {
+  if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || n_splits < 0) return ATTN_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
+  if (causal && Nk < Nq) return ATTN_ERR_SHAPE;  // every query must see key 0
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (H % Hkv != 0) return ATTN_ERR_GQA;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  // 32-bit row indices and byte offsets inside one head / one query group.
+  if ((long long)B * H * Nq >= (1LL << 31) || (long long)B * Hkv * Nk >= (1LL << 31))
+    return ATTN_ERR_SHAPE;
+  if ((long long)Nk * d * 4 >= (1LL << 31) || (long long)(H / Hkv) * Nq * d * 4 >= (1LL << 31))
+    return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+size_t split_workspace(int B, int H, int Nq, int d, const SplitPlan& p) {
+  const size_t rows = (size_t)B * H * Nq;
+  return round256((size_t)p.n_splits * rows * d * sizeof(float)) +
+         round256((size_t)p.n_splits * rows * sizeof(float));
+}
+
+}  // namespace
+
+size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d,
+                                        int causal, int dtype, int n_splits) {
+  if (validate_split(B, H, Hkv, Nq, Nk, d, causal, dtype, n_splits) != ATTN_OK) return 0;
+  return split_workspace(B, H, Nq, d, split_plan(B, Hkv, H / Hkv, Nq, Nk, n_splits));
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                     int n_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  int st = validate_split(B, H, Hkv, Nq, Nk, d, causal, dtype, n_splits);
+  if (st != ATTN_OK) return st;
+  st = validate_scale(scale);
+  if (st != ATTN_OK) return st;
+  const SplitPlan p = split_plan(B, Hkv, H / Hkv, Nq, Nk, n_splits);
+  if (!workspace || workspace_bytes < split_workspace(B, H, Nq, d, p)) return ATTN_ERR_WORKSPACE;
+  if (!aligned_all({q, k, v, o, lse, workspace})) return ATTN_ERR_ALIGN;
+  const size_t rows = (size_t)B * H * Nq;
+  float* o_part = (float*)workspace;
+  float* lse_part = (float*)((char*)workspace + round256((size_t)p.n_splits * rows * d * sizeof(float)));
+  osattn::SplitArgs a{q,  k, v,  o,     lse,    o_part, lse_part,   B,          H,
+                      Hkv, Nq, Nk, d, scale, causal, dtype, p.n_splits, p.split_keys, stream};
+  return osattn::launch_splitkv(a) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

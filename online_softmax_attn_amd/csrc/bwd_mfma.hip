@@ -627,11 +627,15 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // 3. dQ.
+#ifndef OSATTN_DQ_BC
+#define OSATTN_DQ_BC 64
+#endif
+
 template <int D, int NBUF>
 struct DqCfg {
   static constexpr int kNW = 8;              // waves (two per SIMD)
   static constexpr int kRows = kNW * 32;     // query rows per workgroup
-  static constexpr int kBC = 64;             // keys per staged tile
+  static constexpr int kBC = OSATTN_DQ_BC;   // keys per staged tile
   static constexpr int kRowBytes = D * 2;
   static constexpr int kTileElems = kBC * D;
   static constexpr int kChunks = kBC * kRowBytes / 1024;
@@ -743,7 +747,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     if (CAUSAL && k0 > wrow0 + 31) return;  // every key of the tile is after every row
     const bool need_mask = (k0 + C::kBC > N) || (CAUSAL && k0 + C::kBC - 1 > wrow0);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < C::kBC / 32; ++kb) {
       // S^T = K Q^T, dP^T = V dO^T (lane = query row, register = key)
       f32x16 s, dp;
 #pragma unroll

@@ -40,6 +40,23 @@ struct BwdArgs {
   int stages;  // bit set of kStageDkdv and kStageDq: which backward kernels to launch
 };
 
+struct SplitArgs {
+  const void* q;  // [B][H][Nq][d]
+  const void* k;  // [B][Hkv][Nk][d]
+  const void* v;
+  void* o;        // [B][H][Nq][d]
+  float* lse;     // [B][H][Nq]
+  float* o_part;  // workspace: [n_splits][B*H*Nq][d] chunk outputs
+  float* lse_part;  // workspace: [n_splits][B*H*Nq] chunk logsumexps
+  int B, H, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  int dtype;       // 1 fp16, 2 bf16
+  int n_splits;    // chunks actually launched (each non-empty)
+  int split_keys;  // keys per chunk, a multiple of 32
+  void* stream;
+};
+
 constexpr int kStageDkdv = 1;
 constexpr int kStageDq = 2;
 
@@ -48,5 +65,6 @@ hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_preprocess(const BwdArgs& a);
 hipError_t launch_bwd_mfma(const BwdArgs& a);
 hipError_t launch_bwd_f32(const BwdArgs& a);
+hipError_t launch_splitkv(const SplitArgs& a);
 
 }  // namespace osattn

@@ -1,0 +1,328 @@
+// Split-KV forward for few queries against a long key/value sequence (decoding).
+//
+// With a handful of query rows per head the row-partitioned forward launches too
+// few workgroups to fill 256 CUs, so the key axis is cut instead (ml-notes page,
+// the split-K notes of the sparse-attention kernel: more independent blocks, each
+// carrying the online-softmax state over its own key chunk, then an exact merge).
+//
+//  1. splitkv_partial_kernel: one wave per workgroup, 32 query rows.  The rows of
+//     a workgroup are the n_rep query heads of one key/value head times the Nq
+//     queries (grouped-query decoding reads each K/V chunk once for the whole
+//     group); in memory these rows are contiguous, [h_local][i].  The wave walks
+//     its chunk of keys in 32-key tiles with the FlashAttention-2 online softmax
+//     (FlashAttention-2 page, inner loop steps 1-5, exact running max per tile)
+//     and writes the chunk's normalised output O_s = Ot / l and LSE_s = m + ln l
+//     in fp32 (LSE_s = -inf and O_s = 0 for rows that see no key of the chunk).
+//  2. splitkv_merge_kernel: one wave per query row combines the chunks,
+//     LSE = ln sum_s exp(LSE_s) taken about the max, O = sum_s exp(LSE_s - LSE) O_s
+//     (the exact rescale-to-a-common-max merge of the ml-notes page and of
+//     "Phase 2" on the attnres-kernel-lab page), and writes O in the I/O dtype.
+//
+// Causal masks are aligned bottom-right: query i is position i + Nk - Nq.
+// The step is HBM-bound (K and V are read once); K/V tiles go straight from
+// memory into LDS with 16-byte DMA, four tiles in flight per wave, and the same
+// MFMA layouts as the main forward: S^T = K Q^T with one query row per lane,
+// O^T += V^T P^T with P from registers and V read transposed from LDS.
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace osattn {
+
+namespace {
+
+constexpr int kSplitTile = 32;  // keys per tile
+constexpr int kSplitNbuf = 4;   // tiles in flight
+// s_waitcnt lgkmcnt(0) with vmcnt and expcnt left at their maxima (gfx9 encoding).
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
+
+template <int D>
+struct SplitSwizzle {
+  // 16-byte granule XOR of tile row `row` (conflict-free 128-bit K reads and
+  // transposed V reads; the V swizzle is equal for rows r and r + 8).
+  static __device__ __forceinline__ int k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  static __device__ __forceinline__ int v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64)))
+void splitkv_partial_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                            const uint16_t* __restrict__ V, float* __restrict__ Opart,
+                            float* __restrict__ Lpart, int H, int Hkv, int Nq, int Nk,
+                            int n_rowblocks, int n_splits, int split_keys, long long rows_total,
+                            float scale_log2) {
+  using M = Mfma<T>;
+  using vec8 = typename M::vec8;
+  using Swz = SplitSwizzle<D>;
+  constexpr int kRowBytes = D * 2;
+  constexpr int kTileElems = kSplitTile * D;
+  constexpr int kChunks = kSplitTile * kRowBytes / 1024;  // 1 KB DMA chunks per tile
+  __shared__ __attribute__((aligned(1024))) uint16_t lk0[kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv0[kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lk1[kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv1[kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lk2[kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv2[kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lk3[kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv3[kTileElems];
+
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // blockIdx.x = (bg * n_splits + split) * n_rowblocks + rb: row blocks of one chunk
+  // are adjacent (they read the same K/V tiles).
+  const int rb = blockIdx.x % n_rowblocks;
+  const int split = (blockIdx.x / n_rowblocks) % n_splits;
+  const int bg = blockIdx.x / (n_rowblocks * n_splits);  // b * Hkv + g
+  const int g = bg % Hkv;
+  const int b = bg / Hkv;
+  const int n_rep = H / Hkv;
+  const int R = n_rep * Nq;           // rows of this group
+  const int r = 32 * rb + l32;        // this lane's row within the group
+  const bool row_ok = r < R;
+  const long long row0 = ((long long)b * H + (long long)g * n_rep) * Nq;  // group's first row
+
+  // Query fragments (B operand of S^T = K Q^T); rows >= R read zero.
+  const auto rq = make_rsrc(Q + row0 * D, (uint32_t)R * kRowBytes);
+  vec8 qf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+    qf[c] = as_vec8<T>(buffer_load16(rq, (uint32_t)r * kRowBytes + (16 * c + 8 * hi) * 2));
+
+  // Key range of this chunk, shortened (causal) to the last key any row can see.
+  const int ks = split * split_keys;
+  const int ke = min(Nk, ks + split_keys);
+  const int lim = (row_ok ? r % Nq : 0) + Nk - Nq;  // last visible key of this row (causal)
+  int kend = ke;
+  if (CAUSAL) {
+    const int first = 32 * rb, last = min(R, 32 * rb + 32) - 1;
+    int max_i;
+    if (last - first + 1 >= Nq) max_i = Nq - 1;
+    else max_i = (last % Nq >= first % Nq) ? last % Nq : Nq - 1;
+    kend = min(ke, max_i + Nk - Nq + 1);
+  }
+  const int n_t = kend > ks ? (kend - ks + kSplitTile - 1) / kSplitTile : 0;
+
+  const auto rk = make_rsrc(K + (size_t)bg * Nk * D, (uint32_t)Nk * kRowBytes);
+  const auto rv = make_rsrc(V + (size_t)bg * Nk * D, (uint32_t)Nk * kRowBytes);
+  uint32_t goff_k[kChunks], goff_v[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int off = i * 1024 + lane * 16;
+    const int row = off / kRowBytes;
+    const int pg = (off % kRowBytes) / 16;
+    goff_k[i] = row * kRowBytes + ((pg ^ Swz::k(row)) * 16);
+    goff_v[i] = row * kRowBytes + ((pg ^ Swz::v(row)) * 16);
+  }
+  auto issue = [&](int t, uint16_t* lk, uint16_t* lv) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(ks + t * kSplitTile) * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      buffer_load16_lds(rk, lk + i * 512, base + goff_k[i]);
+      buffer_load16_lds(rv, lv + i * 512, base + goff_v[i]);
+    }
+  };
+
+  uint32_t koff[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) koff[c] = l32 * kRowBytes + (((2 * c + hi) ^ Swz::k(l32)) * 16);
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  uint32_t voff[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    const int col = 32 * t + tr_col;
+    voff[t] = tr_row * kRowBytes + (((col >> 3) ^ Swz::v(tr_row)) * 16) + (col & 7) * 2;
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+  // Running max (log2 units, finite sentinel) and this lane's half of the running sum.
+  float m_run = -1e30f, l_run = 0.f;
+
+  auto compute = [&](int t, const char* kbase, const char* vbase) __attribute__((always_inline)) {
+    const int k0 = ks + t * kSplitTile;
+    f32x16 s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const u32x4 a = *(const u32x4*)(kbase + koff[c]);
+      s = M::mma32(as_vec8<T>(a), qf[c], s);
+    }
+    const bool need_mask = (k0 + kSplitTile > ke) || (CAUSAL && k0 + kSplitTile - 1 > Nk - Nq);
+    float x[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      x[e] = s[e] * scale_log2;
+      if (need_mask) {
+        const int key = k0 + 8 * (e >> 2) + 4 * hi + (e & 3);
+        if (key >= ke || (CAUSAL && key > lim)) x[e] = -INFINITY;
+      }
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
+    const float m_new = fmaxf(m_run, wave_xor32_max(mx));
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    vec8 pf[2];
+    float part = 0.f;
+#pragma unroll
+    for (int c4 = 0; c4 < 2; ++c4) {
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = fast_exp2(x[8 * c4 + j] - m_new);
+      pf[c4] = pack8<T>(p);
+      part = sum8<T>(pf[c4], part);
+    }
+    l_run = l_run * alpha + part;
+#pragma unroll
+    for (int tt = 0; tt < D / 32; ++tt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[tt][e] *= alpha;
+#pragma unroll
+    for (int c4 = 0; c4 < 2; ++c4)
+#pragma unroll
+      for (int tt = 0; tt < D / 32; ++tt) {
+        const char* vb = vbase + 16 * c4 * kRowBytes + voff[tt];
+        const vec8 a = join8<T>(lds_read_tr4(vb), lds_read_tr4(vb + 8 * kRowBytes));
+        acc[tt] = M::mma32(a, pf[c4], acc[tt]);
+      }
+  };
+
+  auto stage_k = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return lk0;
+    else if constexpr (S == 1) return lk1;
+    else if constexpr (S == 2) return lk2;
+    else return lk3;
+  };
+  auto stage_v = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return lv0;
+    else if constexpr (S == 1) return lv1;
+    else if constexpr (S == 2) return lv2;
+    else return lv3;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  if (0 < n_t) issue(0, lk0, lv0);
+  if (1 < n_t) issue(1, lk1, lv1);
+  if (2 < n_t) issue(2, lk2, lv2);
+  auto step = [&](auto sc, int t) __attribute__((always_inline)) {
+    constexpr int SN = (decltype(sc)::value + kSplitNbuf - 1) % kSplitNbuf;
+    // Tile t has landed once at most the loads of the tiles issued after it
+    // (up to two) are outstanding.
+    const int ahead = min(kSplitNbuf - 2, n_t - 1 - t);
+    if (ahead >= 2) wait_vmcnt<4 * kChunks>();
+    else if (ahead == 1) wait_vmcnt<2 * kChunks>();
+    else wait_vmcnt<0>();
+    // The stage receiving tile t + 3 was read by tile t - 1: let those LDS reads
+    // complete before the DMA may overwrite it.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    if (t + kSplitNbuf - 1 < n_t)
+      issue(t + kSplitNbuf - 1, stage_k(std::integral_constant<int, SN>{}),
+            stage_v(std::integral_constant<int, SN>{}));
+    compute(t, (const char*)stage_k(sc), (const char*)stage_v(sc));
+  };
+  for (int t = 0; t < n_t; t += kSplitNbuf) {
+    step(I0{}, t);
+    if (t + 1 < n_t) step(I1{}, t + 1);
+    if (t + 2 < n_t) step(I2{}, t + 2);
+    if (t + 3 < n_t) step(I3{}, t + 3);
+  }
+
+  // Chunk result: O_s = Ot / l and LSE_s = ln(2) * (m + log2 l), or 0 and -inf.
+  const float l = wave_xor32_sum(l_run);
+  if (row_ok) {
+    const long long row = row0 + r;
+    float* op = Opart + ((long long)split * rows_total + row) * D;
+    const bool any = l > 0.f;
+    const float inv = any ? 1.0f / l : 0.f;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = acc[t][4 * gq + e] * inv;
+        *(f32x4*)(op + 32 * t + 8 * gq + 4 * hi) = w;
+      }
+    if (hi == 0)
+      Lpart[(long long)split * rows_total + row] = any ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+// One wave per query row: merge the n_splits chunk results of that row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restrict__ Opart,
+                                                            const float* __restrict__ Lpart,
+                                                            uint16_t* __restrict__ O,
+                                                            float* __restrict__ LSE,
+                                                            long long rows, int n_splits) {
+  constexpr int kCols = D / 64;  // columns per lane
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) m = fmaxf(m, Lpart[(long long)s * rows + row]);
+  float o[kCols];
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) o[c] = 0.f;
+  float z = 0.f;
+  if (m > -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const float ls = Lpart[(long long)s * rows + row];
+      const float w = ls > -INFINITY ? __expf(ls - m) : 0.f;
+      z += w;
+      const float* op = Opart + ((long long)s * rows + row) * D + kCols * lane;
+#pragma unroll
+      for (int c = 0; c < kCols; ++c) o[c] = fmaf(w, op[c], o[c]);
+    }
+  }
+  const float inv = z > 0.f ? 1.0f / z : 0.f;
+  uint16_t* out = O + row * D + kCols * lane;
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) out[c] = to_bits<T>(o[c] * inv);
+  if (lane == 0) LSE[row] = z > 0.f ? m + __logf(z) : -INFINITY;
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t splitkv_t(const SplitArgs& a) {
+  const int n_rep = a.H / a.Hkv;
+  const int n_rb = (n_rep * a.Nq + 31) / 32;
+  const long long rows = (long long)a.B * a.H * a.Nq;
+  const long long blocks = (long long)a.B * a.Hkv * a.n_splits * n_rb;
+  hipLaunchKernelGGL((splitkv_partial_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(64), 0,
+                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, a.o_part, a.lse_part, a.H, a.Hkv, a.Nq, a.Nk, n_rb,
+                     a.n_splits, a.split_keys, rows, a.scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((splitkv_merge_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                     (hipStream_t)a.stream, a.o_part, a.lse_part, (uint16_t*)a.o, a.lse, rows,
+                     a.n_splits);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t splitkv_dt(const SplitArgs& a) {
+  if (a.d == 64) return a.causal ? splitkv_t<T, 64, true>(a) : splitkv_t<T, 64, false>(a);
+  return a.causal ? splitkv_t<T, 128, true>(a) : splitkv_t<T, 128, false>(a);
+}
+
+}  // namespace
+
+hipError_t launch_splitkv(const SplitArgs& a) {
+  return a.dtype == 2 ? splitkv_dt<__bf16>(a) : splitkv_dt<_Float16>(a);
+}
+
+}  // namespace osattn

@@ -189,3 +189,51 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         osa.attn_fwd(q, q, q)
+
+
+def split(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, Hkv=2, Nq=3, Nk=100, d=128, scale=0.125,
+             causal=1, dtype=2, n_splits=0, ws=P, ws_bytes=1 << 24, stream=None)
+    a.update(kw)
+    return osa.library().attn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                          a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                                          a["causal"], a["dtype"], a["n_splits"], a["ws"],
+                                          a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, "ATTN_ERR_NULL"),
+    ({"lse": None}, "ATTN_ERR_NULL"),
+    ({"Nq": 0}, "ATTN_ERR_SHAPE"),
+    ({"Nk": 0}, "ATTN_ERR_SHAPE"),
+    ({"B": 0}, "ATTN_ERR_SHAPE"),
+    ({"n_splits": -1}, "ATTN_ERR_SHAPE"),
+    ({"causal": 2}, "ATTN_ERR_SHAPE"),
+    ({"causal": 1, "Nq": 101}, "ATTN_ERR_SHAPE"),
+    ({"d": 96}, "ATTN_ERR_HEAD_DIM"),
+    ({"H": 3}, "ATTN_ERR_GQA"),
+    ({"dtype": 0}, "ATTN_ERR_DTYPE"),
+    ({"dtype": 5}, "ATTN_ERR_DTYPE"),
+    ({"scale": 0.0}, "ATTN_ERR_SCALE"),
+    ({"ws": None}, "ATTN_ERR_WORKSPACE"),
+    ({"ws_bytes": 64}, "ATTN_ERR_WORKSPACE"),
+    ({"o": P + 8}, "ATTN_ERR_ALIGN"),
+    ({"ws": P + 4}, "ATTN_ERR_ALIGN"),
+], ids=lambda x: str(x))
+def test_splitkv_rejects(kw, code):
+    assert split(**kw) == S[code]
+
+
+def test_splitkv_workspace_bytes():
+    f = osa.library().attn_fwd_splitkv_workspace_bytes
+    r256 = lambda x: (x + 255) // 256 * 256
+    # One query of 4 heads, 100 keys = 4 tiles, auto: at most one chunk per 4 tiles.
+    assert f(1, 4, 2, 1, 100, 128, 1, 2, 0) == r256(1 * 4 * 1 * 128 * 4) + r256(4 * 4)
+    # Explicit chunk counts: 3 chunks of 2 tiles (64 keys) leave 2 non-empty chunks.
+    assert f(1, 4, 2, 1, 100, 128, 0, 2, 3) == r256(2 * 4 * 128 * 4) + r256(2 * 4 * 4)
+    # Requests above one chunk per 32 keys are capped at 4 chunks here.
+    assert f(1, 4, 2, 1, 100, 64, 0, 1, 99) == r256(4 * 4 * 64 * 4) + r256(4 * 4 * 4)
+    # Invalid arguments give 0.
+    assert f(1, 4, 2, 1, 100, 128, 1, 0, 0) == 0       # fp32 has no split-KV kernel
+    assert f(1, 4, 2, 200, 100, 128, 1, 2, 0) == 0     # causal with Nq > Nk
+    assert f(1, 4, 2, 1, 100, 128, 0, 2, -2) == 0
