@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#ifndef OSATTN_SPLIT_NBUF
+#define OSATTN_SPLIT_NBUF 4  // K/V tiles staged per split-KV workgroup (3 or 4)
+#endif
+
 namespace osattn {
 
 struct FwdArgs {
@@ -56,6 +60,15 @@ struct SplitArgs {
   int split_keys;  // keys per chunk, a multiple of 32
   void* stream;
 };
+
+// Waves per split-KV workgroup (32 query rows each) for a query group of `rows`
+// rows: one per 32 rows, up to four.
+inline int splitkv_waves(int rows) {
+  const int rb32 = (rows + 31) / 32;
+  return rb32 >= 4 ? 4 : (rb32 >= 2 ? 2 : 1);
+}
+// LDS bytes of one split-KV workgroup: staged K and V tiles of 32 rows.
+inline int splitkv_lds_bytes(int d) { return OSATTN_SPLIT_NBUF * 2 * 32 * d * 2; }
 
 constexpr int kStageDkdv = 1;
 constexpr int kStageDq = 2;

@@ -5,11 +5,11 @@
 // the split-K notes of the sparse-attention kernel: more independent blocks, each
 // carrying the online-softmax state over its own key chunk, then an exact merge).
 //
-//  1. splitkv_partial_kernel: one wave per workgroup, 32 query rows.  The rows of
-//     a workgroup are the n_rep query heads of one key/value head times the Nq
-//     queries (grouped-query decoding reads each K/V chunk once for the whole
-//     group); in memory these rows are contiguous, [h_local][i].  The wave walks
-//     its chunk of keys in 32-key tiles with the FlashAttention-2 online softmax
+//  1. splitkv_partial_kernel: one to four waves per workgroup, 32 query rows per
+//     wave, sharing the K/V tiles.  The rows are the n_rep query heads of one
+//     key/value head times the Nq queries (grouped-query decoding reads each K/V
+//     chunk once for the whole group); in memory these rows are contiguous,
+//     [h_local][i].  Each wave walks the chunk of keys in 32-key tiles with the FlashAttention-2 online softmax
 //     (FlashAttention-2 page, inner loop steps 1-5, exact running max per tile)
 //     and writes the chunk's normalised output O_s = Ot / l and LSE_s = m + ln l
 //     in fp32 (LSE_s = -inf and O_s = 0 for rows that see no key of the chunk).
@@ -20,7 +20,7 @@
 //
 // Causal masks are aligned bottom-right: query i is position i + Nk - Nq.
 // The step is HBM-bound (K and V are read once); K/V tiles go straight from
-// memory into LDS with 16-byte DMA, four tiles in flight per wave, and the same
+// memory into LDS with 16-byte DMA, three or four tiles staged, and the same
 // MFMA layouts as the main forward: S^T = K Q^T with one query row per lane,
 // O^T += V^T P^T with P from registers and V read transposed from LDS.
 #include <type_traits>
@@ -33,7 +33,7 @@ namespace osattn {
 namespace {
 
 constexpr int kSplitTile = 32;  // keys per tile
-constexpr int kSplitNbuf = 4;   // tiles in flight
+constexpr int kSplitNbuf = OSATTN_SPLIT_NBUF;  // tiles in flight (3 or 4)
 // s_waitcnt lgkmcnt(0) with vmcnt and expcnt left at their maxima (gfx9 encoding).
 constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
 
@@ -45,8 +45,8 @@ struct SplitSwizzle {
   static __device__ __forceinline__ int v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 };
 
-template <typename T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(64, 64)))
+template <typename T, int D, int NW, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 void splitkv_partial_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                             const uint16_t* __restrict__ V, float* __restrict__ Opart,
                             float* __restrict__ Lpart, int H, int Hkv, int Nq, int Nk,
@@ -55,19 +55,24 @@ void splitkv_partial_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
   using Swz = SplitSwizzle<D>;
+  constexpr int NBUF = kSplitNbuf;
+  static_assert(NBUF == 3 || NBUF == 4, "three or four stages");
   constexpr int kRowBytes = D * 2;
   constexpr int kTileElems = kSplitTile * D;
   constexpr int kChunks = kSplitTile * kRowBytes / 1024;  // 1 KB DMA chunks per tile
+  constexpr int kCPW = kChunks / NW;                       // of them per wave
+  static_assert(kCPW >= 1 && kChunks % NW == 0, "tile must split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) uint16_t lk0[kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lv0[kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lk1[kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lv1[kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lk2[kTileElems];
   __shared__ __attribute__((aligned(1024))) uint16_t lv2[kTileElems];
-  __shared__ __attribute__((aligned(1024))) uint16_t lk3[kTileElems];
-  __shared__ __attribute__((aligned(1024))) uint16_t lv3[kTileElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lk3[NBUF > 3 ? kTileElems : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lv3[NBUF > 3 ? kTileElems : 8];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -79,8 +84,9 @@ void splitkv_partial_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
   const int g = bg % Hkv;
   const int b = bg / Hkv;
   const int n_rep = H / Hkv;
-  const int R = n_rep * Nq;           // rows of this group
-  const int r = 32 * rb + l32;        // this lane's row within the group
+  const int R = n_rep * Nq;                       // rows of this group
+  const int wr0 = 32 * (NW * rb + wave);          // this wave's first row within the group
+  const int r = wr0 + l32;                        // this lane's row
   const bool row_ok = r < R;
   const long long row0 = ((long long)b * H + (long long)g * n_rep) * Nq;  // group's first row
 
@@ -91,13 +97,14 @@ void splitkv_partial_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
   for (int c = 0; c < D / 16; ++c)
     qf[c] = as_vec8<T>(buffer_load16(rq, (uint32_t)r * kRowBytes + (16 * c + 8 * hi) * 2));
 
-  // Key range of this chunk, shortened (causal) to the last key any row can see.
+  // Key range of this chunk, shortened (causal) to the last key any row of the
+  // workgroup can see.
   const int ks = split * split_keys;
   const int ke = min(Nk, ks + split_keys);
   const int lim = (row_ok ? r % Nq : 0) + Nk - Nq;  // last visible key of this row (causal)
   int kend = ke;
   if (CAUSAL) {
-    const int first = 32 * rb, last = min(R, 32 * rb + 32) - 1;
+    const int first = 32 * NW * rb, last = min(R, first + 32 * NW) - 1;
     int max_i;
     if (last - first + 1 >= Nq) max_i = Nq - 1;
     else max_i = (last % Nq >= first % Nq) ? last % Nq : Nq - 1;
@@ -107,10 +114,10 @@ void splitkv_partial_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
 
   const auto rk = make_rsrc(K + (size_t)bg * Nk * D, (uint32_t)Nk * kRowBytes);
   const auto rv = make_rsrc(V + (size_t)bg * Nk * D, (uint32_t)Nk * kRowBytes);
-  uint32_t goff_k[kChunks], goff_v[kChunks];
+  uint32_t goff_k[kCPW], goff_v[kCPW];
 #pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const int off = i * 1024 + lane * 16;
+  for (int i = 0; i < kCPW; ++i) {
+    const int off = (wave * kCPW + i) * 1024 + lane * 16;
     const int row = off / kRowBytes;
     const int pg = (off % kRowBytes) / 16;
     goff_k[i] = row * kRowBytes + ((pg ^ Swz::k(row)) * 16);
@@ -119,9 +126,10 @@ void splitkv_partial_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
   auto issue = [&](int t, uint16_t* lk, uint16_t* lv) __attribute__((always_inline)) {
     const uint32_t base = (uint32_t)(ks + t * kSplitTile) * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      buffer_load16_lds(rk, lk + i * 512, base + goff_k[i]);
-      buffer_load16_lds(rv, lv + i * 512, base + goff_v[i]);
+    for (int i = 0; i < kCPW; ++i) {
+      const int ch = wave * kCPW + i;
+      buffer_load16_lds(rk, lk + ch * 512, base + goff_k[i]);
+      buffer_load16_lds(rv, lv + ch * 512, base + goff_v[i]);
     }
   };
 
@@ -144,8 +152,10 @@ void splitkv_partial_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
   // Running max (log2 units, finite sentinel) and this lane's half of the running sum.
   float m_run = -1e30f, l_run = 0.f;
+  const bool wave_live = wr0 < R;  // waves whose rows are all padding only stage tiles
 
   auto compute = [&](int t, const char* kbase, const char* vbase) __attribute__((always_inline)) {
+    if (!wave_live) return;
     const int k0 = ks + t * kSplitTile;
     f32x16 s;
 #pragma unroll
@@ -216,28 +226,30 @@ void splitkv_partial_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
   using I3 = std::integral_constant<int, 3>;
   if (0 < n_t) issue(0, lk0, lv0);
   if (1 < n_t) issue(1, lk1, lv1);
-  if (2 < n_t) issue(2, lk2, lv2);
+  if (NBUF > 3 && 2 < n_t) issue(2, lk2, lv2);
   auto step = [&](auto sc, int t) __attribute__((always_inline)) {
-    constexpr int SN = (decltype(sc)::value + kSplitNbuf - 1) % kSplitNbuf;
-    // Tile t has landed once at most the loads of the tiles issued after it
-    // (up to two) are outstanding.
-    const int ahead = min(kSplitNbuf - 2, n_t - 1 - t);
-    if (ahead >= 2) wait_vmcnt<4 * kChunks>();
-    else if (ahead == 1) wait_vmcnt<2 * kChunks>();
+    constexpr int SN = (decltype(sc)::value + NBUF - 1) % NBUF;
+    // Tile t has landed once at most this wave's loads of the tiles issued after it
+    // (up to NBUF - 2) are outstanding.
+    const int ahead = min(NBUF - 2, n_t - 1 - t);
+    if (NBUF > 3 && ahead >= 2) wait_vmcnt<4 * kCPW>();
+    else if (ahead >= 1) wait_vmcnt<2 * kCPW>();
     else wait_vmcnt<0>();
-    // The stage receiving tile t + 3 was read by tile t - 1: let those LDS reads
-    // complete before the DMA may overwrite it.
+    // The stage receiving tile t + NBUF - 1 was read for tile t - 1: those LDS reads
+    // complete before any wave may overwrite it.
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    if (t + kSplitNbuf - 1 < n_t)
-      issue(t + kSplitNbuf - 1, stage_k(std::integral_constant<int, SN>{}),
+    if constexpr (NW > 1) block_barrier();  // every wave's share of tile t is in LDS
+    if (t + NBUF - 1 < n_t)
+      issue(t + NBUF - 1, stage_k(std::integral_constant<int, SN>{}),
             stage_v(std::integral_constant<int, SN>{}));
     compute(t, (const char*)stage_k(sc), (const char*)stage_v(sc));
   };
-  for (int t = 0; t < n_t; t += kSplitNbuf) {
+  for (int t = 0; t < n_t; t += NBUF) {
     step(I0{}, t);
     if (t + 1 < n_t) step(I1{}, t + 1);
     if (t + 2 < n_t) step(I2{}, t + 2);
-    if (t + 3 < n_t) step(I3{}, t + 3);
+    if constexpr (NBUF > 3)
+      if (t + 3 < n_t) step(I3{}, t + 3);
   }
 
   // Chunk result: O_s = Ot / l and LSE_s = ln(2) * (m + log2 l), or 0 and -inf.
@@ -261,7 +273,11 @@ void splitkv_partial_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
   }
 }
 
-// One wave per query row: merge the n_splits chunk results of that row.
+// One wave per query row: merge the n_splits chunk results of that row.  The
+// chunk logsumexps are read one per lane (64 at a time) and reduced across the
+// wave; the weighted sum of the chunk outputs then streams over the chunks with
+// the weight broadcast from the lane that holds it, four chunks per iteration so
+// that their loads are in flight together.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restrict__ Opart,
                                                             const float* __restrict__ Lpart,
@@ -272,20 +288,51 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restr
   const int lane = threadIdx.x & 63;
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
+  // Pass 1: max and sum of exp over the chunk logsumexps.
   float m = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) m = fmaxf(m, Lpart[(long long)s * rows + row]);
+  for (int s0 = 0; s0 < n_splits; s0 += 64) {
+    const int s = s0 + lane;
+    const float ls = s < n_splits ? Lpart[(long long)s * rows + row] : -INFINITY;
+    m = fmaxf(m, ls);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   float o[kCols];
 #pragma unroll
   for (int c = 0; c < kCols; ++c) o[c] = 0.f;
   float z = 0.f;
   if (m > -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float ls = Lpart[(long long)s * rows + row];
-      const float w = ls > -INFINITY ? __expf(ls - m) : 0.f;
-      z += w;
-      const float* op = Opart + ((long long)s * rows + row) * D + kCols * lane;
+    for (int s0 = 0; s0 < n_splits; s0 += 64) {
+      const int s = s0 + lane;
+      const float ls = s < n_splits ? Lpart[(long long)s * rows + row] : -INFINITY;
+      const float w_lane = ls > -INFINITY ? __expf(ls - m) : 0.f;
+      float zl = w_lane;
 #pragma unroll
-      for (int c = 0; c < kCols; ++c) o[c] = fmaf(w, op[c], o[c]);
+      for (int off = 32; off >= 1; off >>= 1) zl += __shfl_xor(zl, off);
+      z += zl;
+      // Pass 2 over these (up to 64) chunks.
+      const int cnt = min(64, n_splits - s0);
+      const float* base = Opart + ((long long)s0 * rows + row) * D + kCols * lane;
+      const long long stride = rows * D;
+      int j = 0;
+      for (; j + 4 <= cnt; j += 4) {
+        float v[4][kCols];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int c = 0; c < kCols; ++c) v[u][c] = base[(j + u) * stride + c];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = __shfl(w_lane, j + u);
+#pragma unroll
+          for (int c = 0; c < kCols; ++c) o[c] = fmaf(w, v[u][c], o[c]);
+        }
+      }
+      for (; j < cnt; ++j) {
+        const float w = __shfl(w_lane, j);
+#pragma unroll
+        for (int c = 0; c < kCols; ++c) o[c] = fmaf(w, base[j * stride + c], o[c]);
+      }
     }
   }
   const float inv = z > 0.f ? 1.0f / z : 0.f;
@@ -295,16 +342,16 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restr
   if (lane == 0) LSE[row] = z > 0.f ? m + __logf(z) : -INFINITY;
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, int NW, bool CAUSAL>
 hipError_t splitkv_t(const SplitArgs& a) {
   const int n_rep = a.H / a.Hkv;
-  const int n_rb = (n_rep * a.Nq + 31) / 32;
+  const int n_rb = (n_rep * a.Nq + 32 * NW - 1) / (32 * NW);
   const long long rows = (long long)a.B * a.H * a.Nq;
   const long long blocks = (long long)a.B * a.Hkv * a.n_splits * n_rb;
-  hipLaunchKernelGGL((splitkv_partial_kernel<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(64), 0,
-                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, a.o_part, a.lse_part, a.H, a.Hkv, a.Nq, a.Nk, n_rb,
-                     a.n_splits, a.split_keys, rows, a.scale * kLog2e);
+  hipLaunchKernelGGL((splitkv_partial_kernel<T, D, NW, CAUSAL>), dim3((unsigned)blocks),
+                     dim3(NW * 64), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.o_part, a.lse_part, a.H, a.Hkv,
+                     a.Nq, a.Nk, n_rb, a.n_splits, a.split_keys, rows, a.scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((splitkv_merge_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
@@ -313,10 +360,19 @@ hipError_t splitkv_t(const SplitArgs& a) {
   return hipGetLastError();
 }
 
+// Waves per workgroup: one per 32 rows of a query group, up to four.
+template <typename T, int D, bool CAUSAL>
+hipError_t splitkv_nw(const SplitArgs& a) {
+  const int nw = splitkv_waves((a.H / a.Hkv) * a.Nq);
+  if (nw == 4) return splitkv_t<T, D, 4, CAUSAL>(a);
+  if (nw == 2) return splitkv_t<T, D, 2, CAUSAL>(a);
+  return splitkv_t<T, D, 1, CAUSAL>(a);
+}
+
 template <typename T>
 hipError_t splitkv_dt(const SplitArgs& a) {
-  if (a.d == 64) return a.causal ? splitkv_t<T, 64, true>(a) : splitkv_t<T, 64, false>(a);
-  return a.causal ? splitkv_t<T, 128, true>(a) : splitkv_t<T, 128, false>(a);
+  if (a.d == 64) return a.causal ? splitkv_nw<T, 64, true>(a) : splitkv_nw<T, 64, false>(a);
+  return a.causal ? splitkv_nw<T, 128, true>(a) : splitkv_nw<T, 128, false>(a);
 }
 
 }  // namespace

@@ -44,6 +44,7 @@ SHAPES = [  # (B, H, Hkv, Nq, Nk)
     (1, 4, 4, 16, 1000),
     (1, 2, 1, 33, 257),     # 66 rows per group: three 32-row blocks, the last partial
     (1, 32, 8, 1, 2048),    # n_rep = 4 packed rows of one group
+    (1, 8, 1, 20, 500),     # 160 rows per group: four-wave workgroups, one wave all padding
 ]
 
 
