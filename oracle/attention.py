@@ -55,6 +55,13 @@ LSE_s = m_s + ln l_s, the whole-row result is
 
 where a chunk with no visible key has LSE_s = -inf and weight 0.
 
+General masks: each query row i of batch b sees the keys lo[b, i] <= j <= hi[b, i]
+(an interval, clamped to 0 .. Nk-1; the same for every head).  Causal, bottom-right
+causal, sliding-window, prefix-LM and document (packed variable-length) masks are all
+such intervals (the FlashAttention-2 page's mask-then-softmax of "Option A" with the
+predicate replaced).  A row whose interval holds no key has no softmax; the reading
+taken is O = 0, LSE = -inf, dQ = 0, and no contribution to dK, dV or D = 0.
+
 Large shapes are processed in blocks of complete rows: each row's full set of N
 scores is formed before its softmax, so no online rescaling happens here.
 """
@@ -75,6 +82,10 @@ __all__ = [
     "attention_head",
     "causal_key_offset",
     "merge_partials",
+    "interval_scores",
+    "attention_head_intervals",
+    "attention_forward_intervals",
+    "attention_backward_intervals",
 ]
 
 
@@ -264,3 +275,89 @@ def merge_partials(o_parts, lse_parts):
     z = np.sum(w, axis=0)
     o = np.sum(w[..., None] * o_parts, axis=0) / z[..., None]
     return o, m + np.log(z)
+
+
+def interval_scores(q_rows: np.ndarray, k: np.ndarray, scale: float, lo: np.ndarray,
+                    hi: np.ndarray) -> np.ndarray:
+    """S = scale * Q K^T with S_ij = -inf unless lo_i <= j <= hi_i."""
+    s = scale * (q_rows @ k.T)
+    key_ids = np.arange(k.shape[0])[None, :]
+    keep = (key_ids >= np.asarray(lo)[:, None]) & (key_ids <= np.asarray(hi)[:, None])
+    return np.where(keep, s, -np.inf)
+
+
+def attention_head_intervals(q, k, v, scale, lo, hi, do=None):
+    """One query head under an interval mask; rows with an empty interval give O = 0,
+    LSE = -inf, dQ = 0, D = 0 and add nothing to dK, dV.  Same returns as
+    attention_head."""
+    n = q.shape[0]
+    lo = np.clip(np.asarray(lo, dtype=np.int64), 0, k.shape[0])
+    hi = np.clip(np.asarray(hi, dtype=np.int64), -1, k.shape[0] - 1)
+    live = lo <= hi
+    o = np.zeros((n, v.shape[1]))
+    lse = np.full(n, -np.inf)
+    want_grad = do is not None
+    if want_grad:
+        dq = np.zeros_like(q)
+        dk = np.zeros_like(k)
+        dv = np.zeros_like(v)
+        dvec = np.zeros(n)
+    rows = np.nonzero(live)[0]
+    if rows.size:
+        s = interval_scores(q[rows], k, scale, lo[rows], hi[rows])
+        p = softmax_rows(s)
+        o[rows] = p @ v
+        lse[rows] = logsumexp_rows(s)
+        if want_grad:
+            dp = do[rows] @ v.T
+            ds = softmax_backward_rows(p, dp)
+            dvec[rows] = np.sum(p * dp, axis=-1)
+            dq[rows] = scale * (ds @ k)
+            dk += scale * (ds.T @ q[rows])
+            dv += p.T @ do[rows]
+    if want_grad:
+        return o, lse, dq, dk, dv, dvec
+    return o, lse
+
+
+def attention_forward_intervals(q, k, v, scale: float, kv_lo, kv_hi):
+    """O [B,H,Nq,d] and LSE [B,H,Nq] under per-row key intervals kv_lo, kv_hi [B,Nq]."""
+    B, H, Nq, d = q.shape
+    Hkv = k.shape[1]
+    kv_lo, kv_hi = np.asarray(kv_lo), np.asarray(kv_hi)
+    o = np.empty((B, H, Nq, d))
+    lse = np.empty((B, H, Nq))
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            o[b, h], lse[b, h] = attention_head_intervals(_f64(q[b, h]), _f64(k[b, g]),
+                                                          _f64(v[b, g]), scale, kv_lo[b], kv_hi[b])
+    return o, lse
+
+
+def attention_backward_intervals(q, k, v, do, scale: float, kv_lo, kv_hi, heads=None):
+    """Forward + backward under per-row key intervals; same dict as attention_backward
+    (dk, dv have the keys' length Nk)."""
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    n_rep = H // Hkv
+    kv_lo, kv_hi = np.asarray(kv_lo), np.asarray(kv_hi)
+    out = {name: np.full((B, H, Nq, d), np.nan) for name in ("o", "dq")}
+    out["lse"] = np.full((B, H, Nq), np.nan)
+    out["D"] = np.full((B, H, Nq), np.nan)
+    out["dk"] = np.full((B, Hkv, Nk, d), np.nan)
+    out["dv"] = np.full((B, Hkv, Nk, d), np.nan)
+    groups = heads if heads is not None else [(b, g) for b in range(B) for g in range(Hkv)]
+    for b, g in groups:
+        kg, vg = _f64(k[b, g]), _f64(v[b, g])
+        dk_sum = np.zeros((Nk, d))
+        dv_sum = np.zeros((Nk, d))
+        for h in range(g * n_rep, (g + 1) * n_rep):
+            o, lse, dq, dk, dv, dvec = attention_head_intervals(
+                _f64(q[b, h]), kg, vg, scale, kv_lo[b], kv_hi[b], _f64(do[b, h]))
+            out["o"][b, h], out["lse"][b, h], out["dq"][b, h], out["D"][b, h] = o, lse, dq, dvec
+            dk_sum += dk
+            dv_sum += dv
+        out["dk"][b, g] = dk_sum
+        out["dv"][b, g] = dv_sum
+    return out

@@ -13,7 +13,9 @@ import math
 __all__ = ["forward", "backward"]
 
 
-def _probs(q, k, scale, causal):
+def _probs(q, k, scale, causal, visible=None):
+    """visible(i, j) -> bool overrides the causal rule when given; a row that sees no
+    key gets all-zero probabilities and LSE = -inf."""
     n, nk = len(q), len(k)
     p = []
     lse = []
@@ -21,30 +23,36 @@ def _probs(q, k, scale, causal):
         row = []
         for j in range(nk):
             # Query i is position i + nk - n of the sequence (bottom-right alignment).
-            if causal and j > i + nk - n:
+            hidden = (not visible(i, j)) if visible is not None else (causal and j > i + nk - n)
+            if hidden:
                 row.append(None)
             else:
                 row.append(scale * sum(q[i][c] * k[j][c] for c in range(len(q[i]))))
-        m = max(x for x in row if x is not None)
-        z = sum(math.exp(x - m) for x in row if x is not None)
+        seen = [x for x in row if x is not None]
+        if not seen:
+            p.append([0.0] * nk)
+            lse.append(-math.inf)
+            continue
+        m = max(seen)
+        z = sum(math.exp(x - m) for x in seen)
         p.append([0.0 if x is None else math.exp(x - m) / z for x in row])
         lse.append(m + math.log(z))
     return p, lse
 
 
-def forward(q, k, v, scale, causal=False):
+def forward(q, k, v, scale, causal=False, visible=None):
     """Returns (O, LSE) as nested lists."""
-    p, lse = _probs(q, k, scale, causal)
+    p, lse = _probs(q, k, scale, causal, visible)
     d = len(v[0])
     o = [[sum(p[i][j] * v[j][c] for j in range(len(k))) for c in range(d)]
          for i in range(len(q))]
     return o, lse
 
 
-def backward(q, k, v, do, scale, causal=False):
+def backward(q, k, v, do, scale, causal=False, visible=None):
     """Returns (dQ, dK, dV) as nested lists, each entry a scalar sum."""
     n, nk, d = len(q), len(k), len(q[0])
-    p, _ = _probs(q, k, scale, causal)
+    p, _ = _probs(q, k, scale, causal, visible)
     dv = [[sum(p[i][j] * do[i][c] for i in range(n)) for c in range(d)] for j in range(nk)]
     dp = [[sum(do[i][c] * v[j][c] for c in range(d)) for j in range(nk)] for i in range(n)]
     ds = []

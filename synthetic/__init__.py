@@ -169,3 +169,56 @@ def custom(dtype: str, B: int, H: int, Hkv: int, N: int, d: int, causal: bool,
 
 def with_dtype(w: Workload, dtype: str) -> Workload:
     return replace(w, dtype=dtype, name=w.name + "_as_" + dtype)
+
+
+def mask_intervals(kind: str, B: int, Nq: int, Nk: int, seed: int = 0, **kw):
+    """Per-row visible key intervals (kv_lo, kv_hi), int32 [B, Nq], inclusive.
+
+    These are inputs (like q, k, v), the same for the oracle and the GPU:
+      causal    query i sees keys 0 .. i + Nk - Nq (queries at the end of the sequence)
+      sliding   keys i + off - left .. i + off + right (right = 0 with causal=True)
+      document  doc_lens[b] splits the positions into documents (Nq == Nk); a row sees its
+                own document (up to itself with causal=True)
+      prefix    prefix-LM: keys 0 .. max(prefix - 1, i + off)
+      random    seeded random intervals, some of them empty (lo > hi)
+    """
+    off = Nk - Nq
+    i = torch.arange(Nq, dtype=torch.int64)
+    if kind == "causal":
+        lo = torch.zeros(Nq, dtype=torch.int64)
+        hi = i + off
+    elif kind == "sliding":
+        left, right = kw.get("left", 128), kw.get("right", 0)
+        lo = (i + off - left).clamp(min=0)
+        hi = (i + off + (0 if kw.get("causal", True) else right)).clamp(max=Nk - 1)
+    elif kind == "prefix":
+        lo = torch.zeros(Nq, dtype=torch.int64)
+        hi = torch.maximum(torch.full((Nq,), kw["prefix"] - 1), i + off).clamp(max=Nk - 1)
+    elif kind == "document":
+        if Nq != Nk:
+            raise ValueError("document masks need Nq == Nk")
+        los, his = [], []
+        for b in range(B):
+            lens = kw["doc_lens"][b]
+            if sum(lens) != Nq:
+                raise ValueError("document lengths must add up to N")
+            start = torch.tensor([0] + list(lens[:-1])).cumsum(0)
+            doc = torch.repeat_interleave(torch.arange(len(lens)), torch.tensor(lens))
+            s_b = start[doc]
+            e_b = s_b + torch.tensor(lens)[doc] - 1
+            los.append(s_b)
+            his.append(torch.minimum(e_b, i) if kw.get("causal", True) else e_b)
+        return torch.stack(los).to(torch.int32).contiguous(), torch.stack(his).to(torch.int32).contiguous()
+    elif kind == "random":
+        g = torch.Generator(device="cpu").manual_seed(seed)
+        a = torch.randint(0, Nk, (B, Nq), generator=g)
+        w = torch.randint(0, max(1, Nk // 2), (B, Nq), generator=g)
+        lo, hi = a, (a + w).clamp(max=Nk - 1)
+        empty = torch.rand((B, Nq), generator=g) < kw.get("empty_frac", 0.05)
+        lo = torch.where(empty, hi + 1, lo)
+        return lo.to(torch.int32).contiguous(), hi.to(torch.int32).contiguous()
+    else:
+        raise ValueError(f"unknown mask kind {kind}")
+    lo = lo.to(torch.int32).expand(B, Nq).contiguous()
+    hi = hi.to(torch.int32).expand(B, Nq).contiguous()
+    return lo, hi

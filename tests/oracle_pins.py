@@ -375,6 +375,119 @@ def pin_merge_single_chunk(seed=24):
     return max(np.max(np.abs(o_m - o[0, 0])), np.max(np.abs(lse_m - lse[0, 0])))
 
 
+# --- interval (general) masks ------------------------------------------------------
+
+def _np(t):
+    return t.numpy().astype(np.int64)
+
+
+def pin_intervals_causal(seed=30, Nq=6, Nk=6):
+    """The causal mask written as intervals gives the causal oracle's forward and
+    backward (square and with queries at the end of a longer key sequence)."""
+    import synthetic as S
+    q, k, v, do, scale = rng_case(seed, 2, 4, 2, Nq, 5)
+    if Nk != Nq:
+        r = np.random.default_rng(seed + 1)
+        k, v = r.standard_normal((2, 2, Nk, 5)), r.standard_normal((2, 2, Nk, 5))
+    lo, hi = S.mask_intervals("causal", 2, Nq, Nk)
+    a = A.attention_backward_intervals(q, k, v, do, scale, _np(lo), _np(hi))
+    if Nk == Nq:
+        b = A.attention_backward(q, k, v, do, scale, True)
+        names = ("o", "lse", "dq", "dk", "dv", "D")
+    else:
+        o, l = A.attention_forward(q, k, v, scale, True)
+        b, names = {"o": o, "lse": l}, ("o", "lse")
+    return max(np.max(np.abs(a[n] - b[n])) for n in names)
+
+
+def pin_intervals_documents(seed=31, causal=True):
+    """A document mask equals attention run on each document on its own."""
+    import synthetic as S
+    lens = [[3, 5, 1, 4], [13]]
+    q, k, v, do, scale = rng_case(seed, 2, 2, 1, 13, 4)
+    lo, hi = S.mask_intervals("document", 2, 13, 13, doc_lens=lens, causal=causal)
+    a = A.attention_backward_intervals(q, k, v, do, scale, _np(lo), _np(hi))
+    err = 0.0
+    for b in range(2):
+        s0 = 0
+        for n in lens[b]:
+            sl = slice(s0, s0 + n)
+            part = A.attention_backward(q[b:b + 1, :, sl], k[b:b + 1, :, sl], v[b:b + 1, :, sl],
+                                        do[b:b + 1, :, sl], scale, causal)
+            for name in ("o", "lse", "dq", "dk", "dv"):
+                err = max(err, np.max(np.abs(a[name][b, :, sl] - part[name][0])))
+            s0 += n
+    return err
+
+
+def pin_intervals_brute(seed=32, Nq=7, Nk=9, d=3):
+    """Random intervals, some empty: the vectorised oracle against the scalar loops
+    (forward and all three gradients; empty rows give O = 0, LSE = -inf, dQ = 0)."""
+    import synthetic as S
+    r = np.random.default_rng(seed)
+    q, k, v, do = (r.standard_normal(s) for s in ((1, 1, Nq, d), (1, 1, Nk, d), (1, 1, Nk, d),
+                                                  (1, 1, Nq, d)))
+    scale = 0.7
+    lo, hi = S.mask_intervals("random", 1, Nq, Nk, seed=seed, empty_frac=0.3)
+    lo, hi = _np(lo)[0], _np(hi)[0]
+    assert np.any(lo > hi) and np.any(lo <= hi)
+    out = A.attention_backward_intervals(q, k, v, do, scale, lo[None], hi[None])
+    vis = lambda i, j: lo[i] <= j <= hi[i]
+    ql, kl, vl, dol = (x[0, 0].tolist() for x in (q, k, v, do))
+    o_b, lse_b = BR.forward(ql, kl, vl, scale, visible=vis)
+    dq_b, dk_b, dv_b = BR.backward(ql, kl, vl, dol, scale, visible=vis)
+    lse_o = out["lse"][0, 0]
+    lse_ref = np.array(lse_b)
+    if not np.array_equal(np.isinf(lse_o), np.isinf(lse_ref)):
+        return np.inf
+    fin = np.isfinite(lse_ref)
+    err = max(np.max(np.abs(out["o"][0, 0] - np.array(o_b))),
+              np.max(np.abs(lse_o[fin] - lse_ref[fin])))
+    for name, ref in (("dq", dq_b), ("dk", dk_b), ("dv", dv_b)):
+        err = max(err, np.max(np.abs(out[name][0, 0] - np.array(ref))))
+    return err
+
+
+def pin_intervals_wide_window(seed=33):
+    """A sliding window wider than the sequence is the plain (causal or full) mask."""
+    import synthetic as S
+    q, k, v, _, scale = rng_case(seed, 1, 2, 2, 9, 4)
+    err = 0.0
+    for causal in (True, False):
+        lo, hi = S.mask_intervals("sliding", 1, 9, 9, left=50, right=50, causal=causal)
+        o, l = A.attention_forward_intervals(q, k, v, scale, _np(lo), _np(hi))
+        o2, l2 = A.attention_forward(q, k, v, scale, causal)
+        err = max(err, np.max(np.abs(o - o2)), np.max(np.abs(l - l2)))
+    return err
+
+
+def pin_intervals_finite_differences(seed=34, h=1e-6):
+    """Gradients under a sliding-window mask against central differences of
+    L = sum(dO * O) (relative to max |grad|)."""
+    import synthetic as S
+    q, k, v, do, scale = rng_case(seed, 1, 2, 1, 8, 3)
+    lo, hi = S.mask_intervals("sliding", 1, 8, 8, left=2, causal=True)
+    lo, hi = _np(lo), _np(hi)
+    out = A.attention_backward_intervals(q, k, v, do, scale, lo, hi)
+
+    def loss(qq, kk, vv):
+        o, _ = A.attention_forward_intervals(qq, kk, vv, scale, lo, hi)
+        return float(np.sum(do * o))
+
+    worst = 0.0
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        worst = max(worst, np.max(np.abs(fd - out[name])) / np.max(np.abs(fd)))
+    return worst
+
+
 ALL_PINS = {
     "worked_example_walk": (pin_worked_example_walk, 1e-12),
     "worked_example_scores": (pin_worked_example_scores, 0.0),
@@ -410,4 +523,11 @@ ALL_PINS = {
     "merge_exact_causal": (lambda: pin_merge_exact(causal=True, Nq=9), 1e-13),
     "merge_exact_reordered": (lambda: pin_merge_exact(causal=True, Nq=9, order=[3, 0, 4, 2, 1]), 1e-13),
     "merge_single_chunk": (pin_merge_single_chunk, 1e-14),
+    "intervals_causal": (pin_intervals_causal, 1e-13),
+    "intervals_causal_rect": (lambda: pin_intervals_causal(Nq=4, Nk=9), 1e-13),
+    "intervals_documents_causal": (pin_intervals_documents, 1e-13),
+    "intervals_documents": (lambda: pin_intervals_documents(causal=False), 1e-13),
+    "intervals_brute": (pin_intervals_brute, 1e-13),
+    "intervals_wide_window": (pin_intervals_wide_window, 1e-13),
+    "intervals_finite_differences": (pin_intervals_finite_differences, 1e-7),
 }

@@ -58,6 +58,12 @@ MUTANTS = {
                                  P_orig_scores(q, k, scale, causal, row_ids, 0)),
     "causal_offset_sign": ("scores", lambda q, k, scale, causal, row_ids=None, key_offset=0:
                            P_orig_scores(q, k, scale, causal, row_ids, -key_offset)),
+    "interval_hi_exclusive": ("interval_scores", lambda q, k, scale, lo, hi:
+                              P_orig_interval(q, k, scale, lo, np.asarray(hi) - 1)),
+    "interval_lo_ignored": ("interval_scores", lambda q, k, scale, lo, hi:
+                            P_orig_interval(q, k, scale, np.zeros_like(np.asarray(lo)), hi)),
+    "interval_transposed_keep": ("interval_scores", lambda q, k, scale, lo, hi:
+                                 _interval_rows_as_keys(q, k, scale, lo, hi)),
     "merge_unnormalised": ("merge_partials", lambda o, l: _bad_merge(o, l, "unnormalised")),
     "merge_plain_mean": ("merge_partials", lambda o, l: _bad_merge(o, l, "mean")),
     "merge_lse_is_max": ("merge_partials", lambda o, l: _bad_merge(o, l, "lse_max")),
@@ -72,6 +78,15 @@ MUTANTS = {
 }
 
 P_orig_scores = A.scores
+P_orig_interval = A.interval_scores
+
+
+def _interval_rows_as_keys(q, k, scale, lo, hi):
+    """Masks by query index instead of key index (a transposed keep test)."""
+    s = scale * (q @ k.T)
+    rows = np.arange(q.shape[0])[:, None]
+    keep = (rows >= np.asarray(lo)[:, None]) & (rows <= np.asarray(hi)[:, None])
+    return np.where(np.broadcast_to(keep, s.shape), s, -np.inf)
 
 
 def _shifted_mask(q, k, scale, causal, row_ids, key_offset):
