@@ -72,6 +72,25 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, void* stream);
 
 /*
+ * Forward pass under a general mask (FlashAttention-2 page, causal masking "Option A":
+ * mask the score tile, then the online softmax, with the mask predicate replaced):
+ * query row i of batch b sees exactly the keys j with
+ *     kv_lo[b*Nq + i] <= j <= kv_hi[b*Nq + i]
+ * (device int32 arrays [B][Nq], the same for every head; values are clamped to
+ * 0 .. Nk-1).  Causal (kv_lo = 0, kv_hi = i), causal with the queries at the end of
+ * a longer key sequence (kv_hi = i + Nk - Nq), sliding windows, prefix-LM masks and
+ * document masks of packed variable-length sequences are all such intervals.  A row
+ * whose interval holds no key gets O = 0 and LSE = -inf.
+ *     q, o : [B][H][Nq][d]      k, v : [B][Hkv][Nk][d]      lse : [B][H][Nq]
+ * Tiles wholly outside a wave's rows' intervals are skipped, so cost follows the
+ * number of visible pairs.  Same dtypes, d and return codes as attn_fwd (kv_lo and
+ * kv_hi must be 4-byte aligned).
+ */
+int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                    const int* kv_lo, const int* kv_hi, int dtype, void* stream);
+
+/*
  * Bytes of device workspace attn_bwd needs for these sizes: two float32 values
  * per query row (D = rowsum(dO * O) and LSE * log2(e)), each array rounded up to
  * 256 bytes.  Returns 0 for invalid sizes.  Callers should always ask this

@@ -35,6 +35,7 @@ __all__ = [
     "new_bwd_workspace",
     "attn_fwd_splitkv",
     "attn_fwd_splitkv_workspace_bytes",
+    "attn_fwd_masked",
     "status_string",
     "library",
     "library_path",
@@ -62,7 +63,7 @@ DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
             "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
-            "attn_status_string")
+            "attn_fwd_masked", "attn_status_string")
 
 _lib = None
 
@@ -99,6 +100,8 @@ def library() -> ctypes.CDLL:
     lib.attn_bwd_dkdv.restype = i
     lib.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.attn_bwd_dq.restype = i
+    lib.attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, i, vp]
+    lib.attn_fwd_masked.restype = i
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.attn_fwd_splitkv.restype = i
     lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
@@ -309,4 +312,42 @@ def attn_fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, 
                               _ws_bytes(workspace), _stream_handle(q.device))
     if st != 0:
         raise AttnError(st, "attn_fwd_splitkv")
+    return out, lse
+
+
+def _check_intervals(kv_lo, kv_hi, B, Nq):
+    for name, t in (("kv_lo", kv_lo), ("kv_hi", kv_hi)):
+        _check_dev(name, t, torch.int32)
+        if tuple(t.shape) != (B, Nq):
+            raise ValueError(f"{name} must be int32 [B, Nq] = {(B, Nq)}, got {tuple(t.shape)}")
+
+
+def attn_fwd_masked(q, k, v, kv_lo, kv_hi, scale: float | None = None, out=None, lse=None):
+    """Forward under per-row visible key intervals: query i of batch b sees keys
+    kv_lo[b, i] .. kv_hi[b, i] (int32 [B, Nq] device tensors); k/v may be longer than q."""
+    lib = library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    if q.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,H,Nq,d] and k, v [B,Hkv,Nk,d]")
+    B, H, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _check_intervals(kv_lo, kv_hi, B, Nq)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32) if lse is None else lse
+    _check_dev("out", out, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    if out.shape != q.shape or lse.shape != (B, H, Nq):
+        raise ValueError("out / lse have the wrong shape")
+    st = lib.attn_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, H, Hkv, Nq, Nk, d, float(scale), kv_lo.data_ptr(),
+                             kv_hi.data_ptr(), DTYPE_CODES[q.dtype], _stream_handle(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_masked")
     return out, lse

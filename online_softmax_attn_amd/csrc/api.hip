@@ -52,6 +52,35 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+namespace {
+
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Sizes of the interval-masked calls: the attn_fwd limits for Nq and for Nk.
+int validate_masked_sizes(int B, int H, int Hkv, int Nq, int Nk, int d, int dtype) {
+  int st = validate_sizes(B, H, Hkv, Nq, d, dtype);
+  if (st != ATTN_OK) return st;
+  return validate_sizes(B, H, Hkv, Nk, d, dtype);
+}
+
+}  // namespace
+
+int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                    int Hkv, int Nq, int Nk, int d, float scale, const int* kv_lo,
+                    const int* kv_hi, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !kv_lo || !kv_hi) return ATTN_ERR_NULL;
+  int st = validate_masked_sizes(B, H, Hkv, Nq, Nk, d, dtype);
+  if (st != ATTN_OK) return st;
+  st = validate_scale(scale);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned4(kv_lo) || !aligned4(kv_hi))
+    return ATTN_ERR_ALIGN;
+  osattn::FwdArgs a{q, k, v, o, lse, B, H, Hkv, Nq, d, scale, 0, dtype, stream, Nk, kv_lo, kv_hi};
+  const hipError_t e = dtype == ATTN_F32 ? osattn::launch_fwd_f32(a) : osattn::launch_fwd_mfma(a);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 size_t attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int dtype) {
   if (validate_sizes(B, H, Hkv, N, d, dtype) != ATTN_OK) return 0;
   // D and LSE * log2(e), one float32 per query row each.

@@ -34,13 +34,36 @@ __device__ __forceinline__ void stage_rows(float* lds, const float* g, int first
   }
 }
 
-template <int D, bool CAUSAL>
+// Interval mask of one query row (clamped; empty = lo > hi) and, over the 32 rows of a
+// wave, the smallest lo and largest hi (both lane halves hold the same rows).
+__device__ __forceinline__ void row_interval(const int* kv_lo, const int* kv_hi, int b, int Nq,
+                                             int Nk, int row, int& lo, int& hi) {
+  lo = Nk;
+  hi = -1;
+  if (row < Nq) {
+    lo = max(kv_lo[(size_t)b * Nq + row], 0);
+    hi = min(kv_hi[(size_t)b * Nq + row], Nk - 1);
+  }
+}
+__device__ __forceinline__ void wave_span(int lo, int hi, int& w_lo, int& w_hi) {
+  w_lo = lo <= hi ? lo : INT32_MAX;
+  w_hi = lo <= hi ? hi : -1;
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+    w_lo = min(w_lo, __shfl_xor(w_lo, off));
+    w_hi = max(w_hi, __shfl_xor(w_hi, off));
+  }
+}
+
+template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q,
                                                      const float* __restrict__ K,
                                                      const float* __restrict__ V,
                                                      float* __restrict__ O,
                                                      float* __restrict__ LSE, int H, int Hkv,
-                                                     int N, float scale) {
+                                                     int Nq, int Nk, float scale,
+                                                     const int* __restrict__ kv_lo,
+                                                     const int* __restrict__ kv_hi) {
   __shared__ float ks[kRows * D];
   __shared__ float vs[kRows * D];
   const int lane = threadIdx.x;
@@ -49,23 +72,31 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
   const int h = bh % H, b = bh / H;
   const int kvh = h / (H / Hkv);
   const int row = blockIdx.x * kRows + (lane & 31);
-  const float* Qp = Q + (size_t)bh * N * D;
-  const float* Kp = K + (size_t)(b * Hkv + kvh) * N * D;
-  const float* Vp = V + (size_t)(b * Hkv + kvh) * N * D;
+  const float* Qp = Q + (size_t)bh * Nq * D;
+  const float* Kp = K + (size_t)(b * Hkv + kvh) * Nk * D;
+  const float* Vp = V + (size_t)(b * Hkv + kvh) * Nk * D;
 
   float q[D / 2], o[D / 2];
 #pragma unroll
   for (int c = 0; c < D / 2; ++c) {
-    q[c] = row < N ? Qp[(size_t)row * D + half * (D / 2) + c] : 0.f;
+    q[c] = row < Nq ? Qp[(size_t)row * D + half * (D / 2) + c] : 0.f;
     o[c] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  int n_keys = N;
-  if (CAUSAL) n_keys = min(N, blockIdx.x * kRows + kRows);
-  for (int k0 = 0; k0 < n_keys; k0 += kRows) {
+  int k_begin = 0, k_end = Nk;
+  if (CAUSAL) k_end = min(Nk, blockIdx.x * kRows + kRows);
+  int lo = 0, hi = Nk - 1;
+  if constexpr (MASK) {
+    row_interval(kv_lo, kv_hi, b, Nq, Nk, row, lo, hi);
+    int w_lo, w_hi;
+    wave_span(lo, hi, w_lo, w_hi);
+    k_begin = w_hi >= 0 ? (w_lo / kRows) * kRows : 0;
+    k_end = w_hi >= 0 ? w_hi + 1 : 0;
+  }
+  for (int k0 = k_begin; k0 < k_end; k0 += kRows) {
     __syncthreads();
-    stage_rows<D>(ks, Kp, k0, N);
-    stage_rows<D>(vs, Vp, k0, N);
+    stage_rows<D>(ks, Kp, k0, Nk);
+    stage_rows<D>(vs, Vp, k0, Nk);
     __syncthreads();
     float s[kRows];
     float mt = -INFINITY;
@@ -74,7 +105,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
       float x = half_dot<D>(q, ks + j * D + half * (D / 2));
       x = (x + __shfl_xor(x, 32)) * scale;
       const int key = k0 + j;
-      if (key >= N || (CAUSAL && key > row)) x = -INFINITY;
+      if (key >= Nk || (CAUSAL && key > row) || (MASK && (key < lo || key > hi))) x = -INFINITY;
       s[j] = x;
       mt = fmaxf(mt, x);
     }
@@ -94,11 +125,13 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
     }
     m = mn;
   }
-  if (row < N) {
-    const float inv = 1.f / l;
+  if (row < Nq) {
+    // A row that sees no key (interval masks only): O = 0, LSE = -inf.
+    const bool empty = !(l > 0.f);
+    const float inv = empty ? 0.f : 1.f / l;
 #pragma unroll
-    for (int c = 0; c < D / 2; ++c) O[((size_t)bh * N + row) * D + half * (D / 2) + c] = o[c] * inv;
-    if (half == 0) LSE[(size_t)bh * N + row] = m + logf(l);
+    for (int c = 0; c < D / 2; ++c) O[((size_t)bh * Nq + row) * D + half * (D / 2) + c] = o[c] * inv;
+    if (half == 0) LSE[(size_t)bh * Nq + row] = empty ? -INFINITY : m + logf(l);
   }
 }
 
@@ -226,12 +259,12 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASK>
 hipError_t fwd_f32_t(const FwdArgs& a) {
   dim3 grid((a.N + kRows - 1) / kRows, a.B * a.H);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, (hipStream_t)a.stream,
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, MASK>), grid, dim3(64), 0, (hipStream_t)a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
-                     a.H, a.Hkv, a.N, a.scale);
+                     a.H, a.Hkv, a.N, a.Nk ? a.Nk : a.N, a.scale, a.kv_lo, a.kv_hi);
   return hipGetLastError();
 }
 
@@ -257,8 +290,9 @@ hipError_t bwd_f32_t(const BwdArgs& a) {
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdArgs& a) {
-  if (a.d == 64) return a.causal ? fwd_f32_t<64, true>(a) : fwd_f32_t<64, false>(a);
-  return a.causal ? fwd_f32_t<128, true>(a) : fwd_f32_t<128, false>(a);
+  if (a.kv_lo) return a.d == 64 ? fwd_f32_t<64, false, true>(a) : fwd_f32_t<128, false, true>(a);
+  if (a.d == 64) return a.causal ? fwd_f32_t<64, true, false>(a) : fwd_f32_t<64, false, false>(a);
+  return a.causal ? fwd_f32_t<128, true, false>(a) : fwd_f32_t<128, false, false>(a);
 }
 
 hipError_t launch_bwd_f32(const BwdArgs& a) {

@@ -56,13 +56,14 @@ struct FwdCfg {
   static_assert(kCPW >= 1 && kChunks % NW == 0, "tile must split evenly over the waves");
 };
 
-template <typename T, int D, int NW, int QB, int NBUF, int BC, bool CAUSAL>
+template <typename T, int D, int NW, int QB, int NBUF, int BC, bool CAUSAL, bool MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
 __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                     float* __restrict__ LSE, int H, int Hkv, int N, int n_qtiles,
-                     float scale_log2) {
+                     float* __restrict__ LSE, int H, int Hkv, int Nq, int Nk, int n_qtiles,
+                     float scale_log2, const int* __restrict__ kv_lo,
+                     const int* __restrict__ kv_hi) {
   using C = FwdCfg<D, NW, QB, NBUF, BC>;
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
@@ -96,10 +97,10 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int q0 = qt * C::kBR;
   const int wrow0 = q0 + wave * 32 * QB;
 
-  const uint32_t head_bytes = (uint32_t)N * C::kRowBytes;
-  const auto rq = make_rsrc(Q + (size_t)bh * N * D, head_bytes);
-  const auto rk = make_rsrc(K + (size_t)(b * Hkv + kvh) * N * D, head_bytes);
-  const auto rv = make_rsrc(V + (size_t)(b * Hkv + kvh) * N * D, head_bytes);
+  const auto rq = make_rsrc(Q + (size_t)bh * Nq * D, (uint32_t)Nq * C::kRowBytes);
+  const uint32_t kv_bytes = (uint32_t)Nk * C::kRowBytes;
+  const auto rk = make_rsrc(K + (size_t)(b * Hkv + kvh) * Nk * D, kv_bytes);
+  const auto rv = make_rsrc(V + (size_t)(b * Hkv + kvh) * Nk * D, kv_bytes);
 
   // Query fragments (B operand of S^T = K Q^T): lane holds row l32 of each block,
   // columns 16c + 8*hi .. +7 for every 16-column chunk c.  Rows >= N read zero.
@@ -111,8 +112,62 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     for (int c = 0; c < D / 16; ++c) qf[qb][c] = as_vec8<T>(buffer_load16(rq, rowoff + (16 * c + 8 * hi) * 2));
   }
 
-  int n_kt = (N + C::kBC - 1) / C::kBC;
+  int kt0 = 0;  // first key tile of the loop
+  int n_kt = (Nk + C::kBC - 1) / C::kBC;
   if (CAUSAL) n_kt = min(n_kt, (q0 + C::kBR + C::kBC - 1) / C::kBC);
+
+  // Interval masks: row i sees keys lo_i .. hi_i (clamped to the sequence; an empty
+  // interval, and any row past Nq, is lo = Nk, hi = -1).  A wave skips tiles outside
+  // the union of its rows' intervals and masks only tiles not inside all of them;
+  // the workgroup loads only the tiles some wave needs.
+  int lo_r[QB], hi_r[QB];
+  int w_lo = 0, w_hi = 0, w_maxlo = 0, w_minhi = 0;
+  if constexpr (MASK) {
+    __shared__ int wg_bounds[2 * NW];
+    w_lo = Nk;
+    w_hi = -1;
+    w_maxlo = 0;
+    w_minhi = Nk - 1;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = wrow0 + 32 * qb + l32;
+      int lo = Nk, hi = -1;
+      if (row < Nq) {
+        lo = max(kv_lo[(size_t)b * Nq + row], 0);
+        hi = min(kv_hi[(size_t)b * Nq + row], Nk - 1);
+        if (lo > hi) {
+          lo = Nk;
+          hi = -1;
+        }
+      }
+      lo_r[qb] = lo;
+      hi_r[qb] = hi;
+      w_lo = min(w_lo, lo);
+      w_hi = max(w_hi, hi);
+      w_maxlo = max(w_maxlo, lo);
+      w_minhi = min(w_minhi, hi);
+    }
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {  // over the 32 rows (both lane halves agree)
+      w_lo = min(w_lo, __shfl_xor(w_lo, off));
+      w_hi = max(w_hi, __shfl_xor(w_hi, off));
+      w_maxlo = max(w_maxlo, __shfl_xor(w_maxlo, off));
+      w_minhi = min(w_minhi, __shfl_xor(w_minhi, off));
+    }
+    if (lane == 0) {
+      wg_bounds[2 * wave] = w_lo;
+      wg_bounds[2 * wave + 1] = w_hi;
+    }
+    __syncthreads();
+    int g_lo = Nk, g_hi = -1;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      g_lo = min(g_lo, wg_bounds[2 * w]);
+      g_hi = max(g_hi, wg_bounds[2 * w + 1]);
+    }
+    kt0 = g_hi >= g_lo ? g_lo / C::kBC : 0;
+    n_kt = g_hi >= g_lo ? g_hi / C::kBC + 1 - kt0 : 0;
+  }
 
   // Global offsets of this lane's 16 bytes in each of its LDS-DMA chunks: chunk ch
   // covers LDS bytes [ch*1024, +1024) of the tile, i.e. tile row off / kRowBytes,
@@ -127,7 +182,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     goff_v[i] = row * C::kRowBytes + ((pg ^ Swz::v(row)) * 16);
   }
   auto issue = [&](int kt, uint16_t* lk, uint16_t* lv) __attribute__((always_inline)) {
-    const uint32_t base = (uint32_t)kt * C::kBC * C::kRowBytes;
+    const uint32_t base = (uint32_t)(kt0 + kt) * C::kBC * C::kRowBytes;
 #pragma unroll
     for (int i = 0; i < C::kCPW; ++i) {
       const int ch = wave * C::kCPW + i;
@@ -170,8 +225,9 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 
   auto compute = [&](int kt, const char* kbase, const char* vbase) __attribute__((always_inline)) {
-    const int k0 = kt * C::kBC;
-    const bool active = !CAUSAL || (k0 <= wrow0 + 32 * QB - 1);
+    const int k0 = (kt0 + kt) * C::kBC;
+    const bool active = (!CAUSAL || (k0 <= wrow0 + 32 * QB - 1)) &&
+                        (!MASK || (k0 <= w_hi && k0 + C::kBC - 1 >= w_lo));
     if (!active) return;
 
     // ---- step 1: S^T = K_j Q_i^T -------------------------------------------------
@@ -193,7 +249,8 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       }
     }
     // ---- causal / ragged-tail mask (only on tiles that need it) ------------------------
-    const bool need_mask = (k0 + C::kBC > N) || (CAUSAL && k0 + C::kBC - 1 > wrow0);
+    const bool need_mask = (k0 + C::kBC > Nk) || (CAUSAL && k0 + C::kBC - 1 > wrow0) ||
+                           (MASK && !(k0 >= w_maxlo && k0 + C::kBC - 1 <= w_minhi));
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -203,7 +260,9 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= N || (CAUSAL && key > row)) s[qb][kb][r] = -INFINITY;
+            if (key >= Nk || (CAUSAL && key > row) ||
+                (MASK && (key < lo_r[qb] || key > hi_r[qb])))
+              s[qb][kb][r] = -INFINITY;
           }
       }
     }
@@ -248,7 +307,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           for (int r = 0; r < 16; ++r) acc[qb][t][r] *= alpha;
       }
     };
-    if (kt == 0) move_reference();
+    if (!MASK && kt == 0) move_reference();  // masked rows may start later: left to the range check
     probs();
     bool unsafe = false;
 #pragma unroll
@@ -325,9 +384,10 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wrow0 + 32 * qb + l32;
     const float l = wave_xor32_sum(l_run[qb]);
-    const float inv = 1.0f / l;
-    if (row < N) {
-      uint16_t* op = O + ((size_t)bh * N + row) * D;
+    const bool empty = MASK && !(l > 0.f);  // a row that sees no key: O = 0, LSE = -inf
+    const float inv = empty ? 0.f : 1.0f / l;
+    if (row < Nq) {
+      uint16_t* op = O + ((size_t)bh * Nq + row) * D;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -339,20 +399,21 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                  ((uint32_t)to_bits<T>(acc[qb][t][4 * g + 3] * inv) << 16);
           *(u32x2*)(op + 32 * t + 8 * g + 4 * hi) = w;
         }
-      if (hi == 0) LSE[(size_t)bh * N + row] = (m_run[qb] + __log2f(l)) * kLn2;
+      if (hi == 0) LSE[(size_t)bh * Nq + row] = empty ? -INFINITY : (m_run[qb] + __log2f(l)) * kLn2;
     }
   }
 }
 
-template <typename T, int D, int NW, int QB, int NBUF, int BC, bool CAUSAL>
+template <typename T, int D, int NW, int QB, int NBUF, int BC, bool CAUSAL, bool MASK>
 static hipError_t launch_fwd_t(const FwdArgs& a) {
   using C = FwdCfg<D, NW, QB, NBUF, BC>;
   const int n_qtiles = (a.N + C::kBR - 1) / C::kBR;
   const long long blocks = (long long)n_qtiles * a.B * a.H;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW, QB, NBUF, BC, CAUSAL>), dim3((unsigned)blocks),
-                     dim3(NW * 64), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.H, a.Hkv,
-                     a.N, n_qtiles, a.scale * kLog2e);
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, NW, QB, NBUF, BC, CAUSAL, MASK>),
+                     dim3((unsigned)blocks), dim3(NW * 64), 0, (hipStream_t)a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (uint16_t*)a.o, a.lse, a.H, a.Hkv, a.N, a.Nk ? a.Nk : a.N, n_qtiles,
+                     a.scale * kLog2e, a.kv_lo, a.kv_hi);
   return hipGetLastError();
 }
 
@@ -375,8 +436,9 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
 template <typename T, int D>
 static hipError_t launch_fwd_d(const FwdArgs& a) {
   constexpr int NW = OSATTN_FWD_NW, QB = OSATTN_FWD_QB, NB = OSATTN_FWD_NBUF, BC = OSATTN_FWD_BC;
-  if (a.causal) return launch_fwd_t<T, D, NW, QB, NB, BC, true>(a);
-  return launch_fwd_t<T, D, NW, QB, NB, BC, false>(a);
+  if (a.kv_lo) return launch_fwd_t<T, D, NW, QB, NB, BC, false, true>(a);
+  if (a.causal) return launch_fwd_t<T, D, NW, QB, NB, BC, true, false>(a);
+  return launch_fwd_t<T, D, NW, QB, NB, BC, false, false>(a);
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a) {

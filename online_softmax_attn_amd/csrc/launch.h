@@ -22,6 +22,11 @@ struct FwdArgs {
   int causal;
   int dtype;  // 0 fp32, 1 fp16, 2 bf16
   void* stream;
+  // Interval masks (attn_fwd_masked): N is then the query count, Nk the key count,
+  // and query row i of batch b sees keys kv_lo[b*N + i] .. kv_hi[b*N + i].
+  int Nk = 0;                  // 0: same as N
+  const int* kv_lo = nullptr;  // nullptr: no interval mask
+  const int* kv_hi = nullptr;
 };
 
 struct BwdArgs {

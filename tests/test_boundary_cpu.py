@@ -237,3 +237,29 @@ def test_splitkv_workspace_bytes():
     assert f(1, 4, 2, 1, 100, 128, 1, 0, 0) == 0       # fp32 has no split-KV kernel
     assert f(1, 4, 2, 200, 100, 128, 1, 2, 0) == 0     # causal with Nq > Nk
     assert f(1, 4, 2, 1, 100, 128, 0, 2, -2) == 0
+
+
+def masked(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=4, Hkv=2, Nq=3, Nk=100, d=128, scale=0.125,
+             lo=P, hi=P, dtype=2, stream=None)
+    a.update(kw)
+    return osa.library().attn_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                         a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["lo"],
+                                         a["hi"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, "ATTN_ERR_NULL"),
+    ({"lo": None}, "ATTN_ERR_NULL"),
+    ({"hi": None}, "ATTN_ERR_NULL"),
+    ({"Nq": 0}, "ATTN_ERR_SHAPE"),
+    ({"Nk": 0}, "ATTN_ERR_SHAPE"),
+    ({"d": 32}, "ATTN_ERR_HEAD_DIM"),
+    ({"H": 3}, "ATTN_ERR_GQA"),
+    ({"dtype": 9}, "ATTN_ERR_DTYPE"),
+    ({"scale": -2.0}, "ATTN_ERR_SCALE"),
+    ({"o": P + 8}, "ATTN_ERR_ALIGN"),
+    ({"lo": P + 2}, "ATTN_ERR_ALIGN"),
+], ids=lambda x: str(x))
+def test_masked_fwd_rejects(kw, code):
+    assert masked(**kw) == S[code]
