@@ -180,6 +180,23 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
                      int causal, int dtype, int n_splits, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * Backward pass under the interval mask of attn_fwd_masked (same kv_lo, kv_hi,
+ * Nq, Nk; lse as written by attn_fwd_masked).  Writes dq [B][H][Nq][d] and dk, dv
+ * [B][Hkv][Nk][d] (fully overwritten; keys no query sees get zero gradients, rows
+ * that see no key get dq = 0).  The workspace holds D and LSE * log2(e) per query
+ * row and a 4-int summary of the intervals per 64-row query tile, which the dK/dV
+ * kernel uses to skip query tiles that cannot see its keys.  Same validation and
+ * return codes as attn_bwd.
+ */
+size_t attn_bwd_masked_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d,
+                                       int dtype);
+int attn_bwd_masked(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                    int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                    const int* kv_lo, const int* kv_hi, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* attn_status_string(int status);
 

@@ -36,6 +36,8 @@ __all__ = [
     "attn_fwd_splitkv",
     "attn_fwd_splitkv_workspace_bytes",
     "attn_fwd_masked",
+    "attn_bwd_masked",
+    "attn_bwd_masked_workspace_bytes",
     "status_string",
     "library",
     "library_path",
@@ -63,7 +65,8 @@ DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
             "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
-            "attn_fwd_masked", "attn_status_string")
+            "attn_fwd_masked", "attn_bwd_masked", "attn_bwd_masked_workspace_bytes",
+            "attn_status_string")
 
 _lib = None
 
@@ -102,6 +105,10 @@ def library() -> ctypes.CDLL:
     lib.attn_bwd_dq.restype = i
     lib.attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, i, vp]
     lib.attn_fwd_masked.restype = i
+    lib.attn_bwd_masked.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, vp, vp, i, vp, sz, vp]
+    lib.attn_bwd_masked.restype = i
+    lib.attn_bwd_masked_workspace_bytes.argtypes = [i] * 7
+    lib.attn_bwd_masked_workspace_bytes.restype = sz
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.attn_fwd_splitkv.restype = i
     lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
@@ -351,3 +358,46 @@ def attn_fwd_masked(q, k, v, kv_lo, kv_hi, scale: float | None = None, out=None,
     if st != 0:
         raise AttnError(st, "attn_fwd_masked")
     return out, lse
+
+
+def attn_bwd_masked_workspace_bytes(B, H, Hkv, Nq, Nk, d, dtype) -> int:
+    code = DTYPE_CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(library().attn_bwd_masked_workspace_bytes(B, H, Hkv, Nq, Nk, d, code))
+
+
+def attn_bwd_masked(q, k, v, o, lse, do, kv_lo, kv_hi, scale: float | None = None,
+                    dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV under the same per-row key intervals as attn_fwd_masked."""
+    lib = library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,H,Nq,d] and k, v [B,Hkv,Nk,d]")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d or o.shape != q.shape or do.shape != q.shape \
+            or lse.shape != (B, H, Nq):
+        raise ValueError("inconsistent shapes")
+    _check_intervals(kv_lo, kv_hi, B, Nq)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_dev(name, t, q.dtype)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} has the wrong shape")
+    if workspace is None:
+        need = attn_bwd_masked_workspace_bytes(B, H, Hkv, Nq, Nk, d, q.dtype)
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    _check_dev("workspace", workspace)
+    st = lib.attn_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), B, H, Hkv, Nq, Nk, d, float(scale), kv_lo.data_ptr(),
+                             kv_hi.data_ptr(), DTYPE_CODES[q.dtype], workspace.data_ptr(),
+                             _ws_bytes(workspace), _stream_handle(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_masked")
+    return dq, dk, dv

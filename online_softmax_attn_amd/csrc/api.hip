@@ -275,6 +275,42 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   return osattn::launch_splitkv(a) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+size_t attn_bwd_masked_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int dtype) {
+  if (validate_masked_sizes(B, H, Hkv, Nq, Nk, d, dtype) != ATTN_OK) return 0;
+  // D and LSE * log2(e) per query row, then 4 int32 per (batch, 64-row query tile).
+  const size_t rows = round256((size_t)B * H * Nq * sizeof(float));
+  const size_t tiles = round256((size_t)B * ((Nq + 63) / 64) * 4 * sizeof(int));
+  return 2 * rows + tiles;
+}
+
+int attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq,
+                    int Nk, int d, float scale, const int* kv_lo, const int* kv_hi, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !kv_lo || !kv_hi)
+    return ATTN_ERR_NULL;
+  int st = validate_masked_sizes(B, H, Hkv, Nq, Nk, d, dtype);
+  if (st != ATTN_OK) return st;
+  st = validate_scale(scale);
+  if (st != ATTN_OK) return st;
+  if (!workspace ||
+      workspace_bytes < attn_bwd_masked_workspace_bytes(B, H, Hkv, Nq, Nk, d, dtype))
+    return ATTN_ERR_WORKSPACE;
+  if (!aligned_all({q, k, v, o, lse, dO, dq, dk, dv, workspace}) || !aligned4(kv_lo) ||
+      !aligned4(kv_hi))
+    return ATTN_ERR_ALIGN;
+  const size_t rows = round256((size_t)B * H * Nq * sizeof(float));
+  osattn::BwdArgs a{q,      k,         v,      o,  lse,
+                    dO,     dq,        dk,     dv, (float*)workspace,
+                    (float*)((char*)workspace + rows),
+                    B,      H,         Hkv,    Nq, d,
+                    scale,  0,         dtype,  stream,
+                    osattn::kStageDkdv | osattn::kStageDq,
+                    Nk,     kv_lo,     kv_hi,  (char*)workspace + 2 * rows};
+  if (osattn::launch_bwd_preprocess(a) != hipSuccess) return ATTN_ERR_LAUNCH;
+  return run_bwd_kernels(a);
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

@@ -80,8 +80,40 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const E* __restrict
   for (int off = kTPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && (threadIdx.x % kTPR) == 0) {
     Dv[row] = acc;
-    if (lse2) lse2[row] = LSE[row] * kLog2e;
+    // A row that sees no key (interval masks) has LSE = -inf: store +inf so that
+    // exp2(S*c - LSE*log2e) is 0 for it rather than inf.
+    if (lse2) lse2[row] = LSE[row] == -INFINITY ? INFINITY : LSE[row] * kLog2e;
   }
+}
+
+// Per 64-row query tile of each batch, the interval summary the dK/dV kernel uses
+// to pick and classify tiles: (min lo, max hi) over rows that see some key, and
+// (max lo, min hi) over all rows (an empty row, or a row past Nq, counts as
+// lo = Nk, hi = -1, which forces masking of any tile holding it).
+__global__ __launch_bounds__(64) void mask_tiles_kernel(const int* __restrict__ kv_lo,
+                                                        const int* __restrict__ kv_hi,
+                                                        i32x4* __restrict__ tile_sum, int Nq,
+                                                        int Nk, int n_qt) {
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int row = t * 64 + (int)threadIdx.x;
+  int lo = Nk, hi = -1;
+  if (row < Nq) {
+    lo = max(kv_lo[(size_t)b * Nq + row], 0);
+    hi = min(kv_hi[(size_t)b * Nq + row], Nk - 1);
+    if (lo > hi) {
+      lo = Nk;
+      hi = -1;
+    }
+  }
+  int mn_lo = lo, mx_hi = hi, mx_lo = lo, mn_hi = hi;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    mn_lo = min(mn_lo, __shfl_xor(mn_lo, off));
+    mx_hi = max(mx_hi, __shfl_xor(mx_hi, off));
+    mx_lo = max(mx_lo, __shfl_xor(mx_lo, off));
+    mn_hi = min(mn_hi, __shfl_xor(mn_hi, off));
+  }
+  if (threadIdx.x == 0) tile_sum[(size_t)b * n_qt + t] = i32x4{mn_lo, mx_hi, mx_lo, mn_hi};
 }
 
 // ---------------------------------------------------------------------------
@@ -105,14 +137,20 @@ struct DkdvCfg {
   static_assert(kCPW >= 1 && kChunks % kNW == 0, "tile must split evenly over the waves");
 };
 
-template <typename T, int D, int NBUF, bool CAUSAL>
+template <typename T, int D, int NBUF, bool CAUSAL, bool IMASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                      const float* __restrict__ LSE2, const float* __restrict__ Dv,
                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int H, int Hkv,
-                     int N, int n_ktiles, float scale, float scale_log2) {
+                     int Nq, int n_ktiles, float scale, float scale_log2,
+                     const int* __restrict__ kv_lo, const int* __restrict__ kv_hi,
+                     const i32x4* __restrict__ tile_sum, int Nk_arg) {
+  // (New parameters go last: inserting one before the loop's scalar arguments has
+  // been seen to change register allocation enough to add DMA waits in the loop.)
+  // Keys and queries differ in number only under interval masks.
+  const int Nk = IMASK ? Nk_arg : Nq;
   using C = DkdvCfg<D, NBUF>;
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
@@ -130,6 +168,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   __shared__ __attribute__((aligned(256))) float ll1[C::kQT], lD1[C::kQT];
   __shared__ __attribute__((aligned(256))) float ll2[C::kQT], lD2[C::kQT];
   __shared__ __attribute__((aligned(256))) float ll3[NBUF > 3 ? C::kQT : 4], lD3[NBUF > 3 ? C::kQT : 4];
+  // Interval masks: each staged tile's row intervals, lo in [0, kQT), hi in [kQT, 2kQT).
+  constexpr int kLM = IMASK ? 2 * C::kQT : 4;
+  __shared__ __attribute__((aligned(256))) int lm0[kLM], lm1[kLM], lm2[kLM], lm3[kLM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -146,9 +187,10 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int k0 = kt * C::kKeys;
   const int kw = k0 + 32 * KB * wave;  // first key of this wave
 
-  const uint32_t head_bytes = (uint32_t)N * C::kRowBytes;
-  const auto rk = make_rsrc(K + (size_t)bg * N * D, head_bytes);
-  const auto rv = make_rsrc(V + (size_t)bg * N * D, head_bytes);
+  const uint32_t q_bytes = (uint32_t)Nq * C::kRowBytes;
+  const uint32_t kv_bytes = (uint32_t)Nk * C::kRowBytes;
+  const auto rk = make_rsrc(K + (size_t)bg * Nk * D, kv_bytes);
+  const auto rv = make_rsrc(V + (size_t)bg * Nk * D, kv_bytes);
 
   // K and V rows of this wave (B operands of S = Q K^T and dP = dO V^T).
   vec8 kf[KB][D / 16], vf[KB][D / 16];
@@ -173,10 +215,30 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         dv_acc[kb][t][r] = 0.f;
       }
 
-  // Query tiles that see these keys: all of them, or (causal) from the diagonal on.
-  const int qt_first = CAUSAL ? (k0 / C::kQT) : 0;
-  const int n_qt = (N + C::kQT - 1) / C::kQT;
-  const int per_head = n_qt - qt_first;
+  // Query tiles that see these keys: all of them, or (causal) from the diagonal on,
+  // or (interval masks) the first through the last tile whose rows' intervals meet
+  // this workgroup's keys, from the per-tile summaries (min lo, max hi, max lo, min hi).
+  const int n_qt = (Nq + C::kQT - 1) / C::kQT;
+  int qt_first = CAUSAL ? (k0 / C::kQT) : 0;
+  int per_head = n_qt - qt_first;
+  if constexpr (IMASK) {
+    const int key_hi = min(Nk, k0 + C::kKeys) - 1;
+    int f = n_qt, l = -1;
+    for (int t = lane; t < n_qt; t += 64) {
+      const i32x4 sm = tile_sum[(size_t)b * n_qt + t];
+      if (sm[0] <= key_hi && sm[1] >= k0) {
+        f = min(f, t);
+        l = max(l, t);
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      f = min(f, __shfl_xor(f, off));
+      l = max(l, __shfl_xor(l, off));
+    }
+    qt_first = l >= 0 ? f : 0;
+    per_head = l >= 0 ? l - f + 1 : 0;
+  }
   const int n_iter = per_head * n_rep;
 
   // LDS-DMA offsets: chunk ch of a tile holds tile row off / kRowBytes, physical
@@ -189,31 +251,36 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int pg = (off % C::kRowBytes) / 16;
     goff[i] = row * C::kRowBytes + ((pg ^ bwd_swz<D>(row)) * 16);
   }
-  auto issue = [&](int it, uint16_t* lq, uint16_t* ld, float* ll, float* lD)
+  const uint32_t lane4 = (uint32_t)lane * 4;  // per-lane offset of the 4-byte row loads
+  auto issue = [&](int it, uint16_t* lq, uint16_t* ld, float* ll, float* lD, int* lm)
       __attribute__((always_inline)) {
     const int r = it / per_head;
     const uint32_t i0 = (uint32_t)(qt_first + it % per_head) * C::kQT;
     const size_t bh = (size_t)b * H + kvh * n_rep + r;
-    const auto rq = make_rsrc(Q + bh * N * D, head_bytes);
-    const auto rd = make_rsrc(dO + bh * N * D, head_bytes);
+    const auto rq = make_rsrc(Q + bh * Nq * D, q_bytes);
+    const auto rd = make_rsrc(dO + bh * Nq * D, q_bytes);
 #pragma unroll
     for (int i = 0; i < C::kCPW; ++i) {
       const int ch = wave * C::kCPW + i;
-      buffer_load16_lds(rq, lq + ch * 512, i0 * C::kRowBytes + goff[i]);
-      buffer_load16_lds(rd, ld + ch * 512, i0 * C::kRowBytes + goff[i]);
+      buffer_load16_lds(rq, lq + ch * 512, goff[i], i0 * C::kRowBytes);
+      buffer_load16_lds(rd, ld + ch * 512, goff[i], i0 * C::kRowBytes);
     }
-    if (wave == 0) {  // 64 rows x 4 bytes of LSE*log2(e) and D; rows >= N read zero
-      const auto rl = make_rsrc(LSE2 + bh * N, (uint32_t)N * 4);
-      const auto rD = make_rsrc(Dv + bh * N, (uint32_t)N * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)ll, 4,
-                                               (i0 + lane) * 4, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (__attribute__((address_space(3))) void*)lD, 4,
-                                               (i0 + lane) * 4, 0, 0, 0);
+    if (wave == 0) {  // 64 rows x 4 bytes of LSE*log2(e) and D; rows >= Nq read zero
+      const auto rl = make_rsrc(LSE2 + bh * Nq, (uint32_t)Nq * 4);
+      const auto rD = make_rsrc(Dv + bh * Nq, (uint32_t)Nq * 4);
+      buffer_load4_lds(rl, ll, lane4, i0 * 4);
+      buffer_load4_lds(rD, lD, lane4, i0 * 4);
+      if constexpr (IMASK) {  // and the rows' key intervals
+        const auto rlo = make_rsrc(kv_lo + (size_t)b * Nq, (uint32_t)Nq * 4);
+        const auto rhi = make_rsrc(kv_hi + (size_t)b * Nq, (uint32_t)Nq * 4);
+        buffer_load4_lds(rlo, lm, lane4, i0 * 4);
+        buffer_load4_lds(rhi, lm + C::kQT, lane4, i0 * 4);
+      }
     }
   };
-  // Per-wave outstanding loads of one tile (wave 0 also loads LSE and D).
-  const int loads_per_tile = 2 * C::kCPW + (wave == 0 ? 2 : 0);
-  (void)loads_per_tile;
+  // Outstanding loads per staged tile: 2 * kCPW per wave, and wave 0 also loads LSE
+  // and D (and the two interval arrays).
+  constexpr int kW0 = IMASK ? 4 : 2;
 
   // LDS read offsets (bytes in a tile), loop-invariant per lane.
   //  row-wise (A operand of S and dP): row 32qb + l32, logical granule 2c + hi
@@ -248,8 +315,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   //   transposed Q/dO reads         | softmax-JVP arithmetic
   //                                 | dV, dK MFMAs
   auto compute_tile_fenced = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
-                          const float* lD) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_c)::value;
+                          const float* lD, const int* lm) __attribute__((always_inline)) {
+    constexpr int MM = decltype(mask_c)::value;  // 0 none, 1 causal, 2 intervals
 #pragma unroll
     for (int qb = 0; qb < C::kQT / 32; ++qb) {
       // -- operand requests for S and dP
@@ -260,10 +327,15 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         ad[c] = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
       }
       f32x4 lse4[4], d4[4];  // rows 32qb + 8g + 4hi + 0..3 for register group g
+      i32x4 lo4[4], hi4[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         lse4[g] = *(const f32x4*)&ll[32 * qb + 8 * g + 4 * hi];
         d4[g] = *(const f32x4*)&lD[32 * qb + 8 * g + 4 * hi];
+        if constexpr (MM == 2) {
+          lo4[g] = *(const i32x4*)&lm[32 * qb + 8 * g + 4 * hi];
+          hi4[g] = *(const i32x4*)&lm[C::kQT + 32 * qb + 8 * g + 4 * hi];
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       // -- S = Q K^T, dP = dO V^T (lane = key, register r = query row 8(r/4)+4hi+r%4)
@@ -310,7 +382,11 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g + e;
               float pv = fast_exp2(fmaf(s[kb][r], scale_log2, -lse4[g][e]));
-              if (MASK && key > i0 + ql + e) pv = 0.f;
+              if constexpr (MM == 1) {
+                if (key > i0 + ql + e) pv = 0.f;
+              } else if constexpr (MM == 2) {
+                if (key < lo4[g][e] || key > hi4[g][e]) pv = 0.f;
+              }
               p8[4 * g2 + e] = pv;
               d8[4 * g2 + e] = pv * (dp[kb][r] - d4[g][e]);
             }
@@ -331,8 +407,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
   };
   auto compute_tile_wide = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
-                          const float* lD) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_c)::value;
+                          const float* lD, const int* lm) __attribute__((always_inline)) {
+    constexpr int MM = decltype(mask_c)::value;  // 0 none, 1 causal, 2 intervals
     constexpr int NQB = C::kQT / 32;
     // S = Q K^T, dP = dO V^T (lane = key, register r = query row 8(r/4)+4hi+r%4)
     f32x16 s[NQB][KB], dp[NQB][KB];
@@ -372,11 +448,20 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             const int ql = 32 * qb + 16 * cq + 8 * g2 + 4 * hi;  // local row of register 8cq+4g2
             const f32x4 lse4 = *(const f32x4*)&ll[ql];
             const f32x4 d4 = *(const f32x4*)&lD[ql];
+            i32x4 lo4 = {}, hi4 = {};
+            if constexpr (MM == 2) {
+              lo4 = *(const i32x4*)&lm[ql];
+              hi4 = *(const i32x4*)&lm[C::kQT + ql];
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 8 * cq + 4 * g2 + e;
               float pv = fast_exp2(fmaf(s[qb][kb][r], scale_log2, -lse4[e]));
-              if (MASK && key > i0 + ql + e) pv = 0.f;
+              if constexpr (MM == 1) {
+                if (key > i0 + ql + e) pv = 0.f;
+              } else if constexpr (MM == 2) {
+                if (key < lo4[e] || key > hi4[e]) pv = 0.f;
+              }
               p8[4 * g2 + e] = pv;
               d8[4 * g2 + e] = pv * (dp[qb][kb][r] - d4[e]);
             }
@@ -451,8 +536,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
   };
   auto jvp = [&](auto mask_c, int i0, int qb, const RowOps& o, const f32x16& s, const f32x16& dp,
-                 vec8 (&pp)[2], vec8 (&ps)[2]) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_c)::value;
+                 vec8 (&pp)[2], vec8 (&ps)[2], const int* lm) __attribute__((always_inline)) {
+    constexpr int MM = decltype(mask_c)::value;  // 0 none, 1 causal, 2 intervals
     const int key = kw + l32;
 #pragma unroll
     for (int cq = 0; cq < 2; ++cq) {
@@ -461,11 +546,20 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       for (int g2 = 0; g2 < 2; ++g2) {
         const int g = 2 * cq + g2;
         const int ql = 32 * qb + 8 * g + 4 * hi;
+        i32x4 lo4 = {}, hi4 = {};  // the rows' key intervals (interval masks only)
+        if constexpr (MM == 2) {
+          lo4 = *(const i32x4*)&lm[ql];
+          hi4 = *(const i32x4*)&lm[C::kQT + ql];
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           float pv = fast_exp2(fmaf(s[r], scale_log2, -o.lse4[g][e]));
-          if (MASK && key > i0 + ql + e) pv = 0.f;
+          if constexpr (MM == 1) {
+            if (key > i0 + ql + e) pv = 0.f;
+          } else if constexpr (MM == 2) {
+            if (key < lo4[e] || key > hi4[e]) pv = 0.f;
+          }
           p8[4 * g2 + e] = pv;
           d8[4 * g2 + e] = pv * (dp[r] - o.d4[g][e]);
         }
@@ -499,7 +593,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
   };
   auto compute_tile_pipe = [&](auto mask_c, int i0, const char* qb_, const char* db_,
-                               const float* ll, const float* lD) __attribute__((always_inline)) {
+                               const float* ll, const float* lD, const int* lm)
+      __attribute__((always_inline)) {
     using IC0 = std::integral_constant<int, 0>;
     RowOps r0, r1;
     TrOps t0, t1;
@@ -512,14 +607,14 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // G1(1) with J(0); block 0's transposed operands are requested here too
     read_rows(r1, 1, qb_, db_, ll, lD);
     read_tr(t0, 0, qb_, db_);
-    jvp(mask_c, i0, 0, r0, s0, dp0, pp0, ps0);
+    jvp(mask_c, i0, 0, r0, s0, dp0, pp0, ps0, lm);
     g1(r1, s1, dp1);
     interleave16(std::integral_constant<int, 24>{}, std::integral_constant<int, 16>{},
                  std::integral_constant<int, 2>{}, std::integral_constant<int, 7>{});
     __builtin_amdgcn_sched_barrier(0);
     // G2(0) with J(1); block 1's transposed operands
     read_tr(t1, 1, qb_, db_);
-    jvp(mask_c, i0, 1, r1, s1, dp1, pp1, ps1);
+    jvp(mask_c, i0, 1, r1, s1, dp1, pp1, ps1, lm);
     g2(t0, pp0, ps0);
     interleave16(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
                  std::integral_constant<int, 2>{}, std::integral_constant<int, 8>{});
@@ -529,64 +624,86 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     (void)IC0{};
   };
   auto compute_tile = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
-                          const float* lD) __attribute__((always_inline)) {
+                          const float* lD, const int* lm) __attribute__((always_inline)) {
     if constexpr (KB == 1) {
-      if constexpr (OSATTN_DKDV_PIPE) compute_tile_pipe(mask_c, i0, qb_, db_, ll, lD);
-      else compute_tile_fenced(mask_c, i0, qb_, db_, ll, lD);
+      if constexpr (OSATTN_DKDV_PIPE) compute_tile_pipe(mask_c, i0, qb_, db_, ll, lD, lm);
+      else compute_tile_fenced(mask_c, i0, qb_, db_, ll, lD, lm);
     } else {
-      compute_tile_wide(mask_c, i0, qb_, db_, ll, lD);
+      compute_tile_wide(mask_c, i0, qb_, db_, ll, lD, lm);
     }
   };
-  auto compute = [&](int it, const char* qb_, const char* db_, const float* ll, const float* lD)
-      __attribute__((always_inline)) {
-    const int i0 = (qt_first + it % per_head) * C::kQT;
+  using M0 = std::integral_constant<int, 0>;
+  using M1 = std::integral_constant<int, 1>;
+  using M2 = std::integral_constant<int, 2>;
+  auto compute = [&](int it, const char* qb_, const char* db_, const float* ll, const float* lD,
+                     const int* lm) __attribute__((always_inline)) {
+    const int tq = qt_first + it % per_head;
+    const int i0 = tq * C::kQT;
+    if constexpr (IMASK) {
+      // Skip the tile if no row's interval meets this wave's keys; mask it unless every
+      // row sees all of them.
+      const i32x4 sm = tile_sum[(size_t)b * n_qt + tq];
+      const int kw_last = kw + 32 * KB - 1;
+      if (sm[0] > kw_last || sm[1] < kw) return;
+      if (sm[2] <= kw && sm[3] >= kw_last) compute_tile(M0{}, i0, qb_, db_, ll, lD, lm);
+      else compute_tile(M2{}, i0, qb_, db_, ll, lD, lm);
+      return;
+    }
     if (CAUSAL && i0 + C::kQT - 1 < kw) return;  // every key of this wave is after every row
     // Causal: only tiles whose first row precedes this wave's last key need the mask.
     if (CAUSAL && i0 < kw + 32 * KB - 1)
-      compute_tile(std::true_type{}, i0, qb_, db_, ll, lD);
+      compute_tile(M1{}, i0, qb_, db_, ll, lD, lm);
     else
-      compute_tile(std::false_type{}, i0, qb_, db_, ll, lD);
+      compute_tile(M0{}, i0, qb_, db_, ll, lD, lm);
   };
 
   auto stage = [&](auto sc, auto fn) __attribute__((always_inline)) {
     constexpr int S = decltype(sc)::value;
-    if constexpr (S == 0) fn(lq0, ld0, ll0, lD0);
-    else if constexpr (S == 1) fn(lq1, ld1, ll1, lD1);
-    else if constexpr (S == 2) fn(lq2, ld2, ll2, lD2);
-    else fn(lq3, ld3, ll3, lD3);
+    // The interval arrays only exist for interval masks (elsewhere they must not be
+    // referenced at all, or the compiler stops telling the stages' LDS apart).
+    int* const m0 = IMASK ? lm0 : nullptr;
+    int* const m1 = IMASK ? lm1 : nullptr;
+    int* const m2 = IMASK ? lm2 : nullptr;
+    int* const m3 = IMASK ? lm3 : nullptr;
+    if constexpr (S == 0) fn(lq0, ld0, ll0, lD0, m0);
+    else if constexpr (S == 1) fn(lq1, ld1, ll1, lD1, m1);
+    else if constexpr (S == 2) fn(lq2, ld2, ll2, lD2, m2);
+    else fn(lq3, ld3, ll3, lD3, m3);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  if (0 < n_iter) stage(I0{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd) { issue(0, a, d, l, dd); });
+  if (0 < n_iter)
+    stage(I0{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) { issue(0, a, d, l, dd, mm); });
   if (NBUF > 2 && 1 < n_iter)
-    stage(I1{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd) { issue(1, a, d, l, dd); });
+    stage(I1{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) { issue(1, a, d, l, dd, mm); });
   if (NBUF > 3 && 2 < n_iter)
-    stage(I2{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd) { issue(2, a, d, l, dd); });
+    stage(I2{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) { issue(2, a, d, l, dd, mm); });
 
   auto step = [&](auto sc, int it) __attribute__((always_inline)) {
     constexpr int S = decltype(sc)::value;
     constexpr int SN = (S + NBUF - 1) % NBUF;  // receives tile it + NBUF - 1
     // Tile `it` has landed once at most the loads of the tiles issued after it
     // (up to NBUF - 2 of them) are outstanding.
-    constexpr int kPer = 2 * C::kCPW;  // loads per tile and wave (+2 on wave 0)
+    constexpr int kPer = 2 * C::kCPW;  // loads per tile and wave (+kW0 on wave 0)
     const int ahead = min(NBUF - 2, n_iter - 1 - it);
     if (NBUF > 3 && ahead >= 2) {
-      if (wave == 0) wait_vmcnt<2 * (kPer + 2)>();
+      if (wave == 0) wait_vmcnt<2 * (kPer + kW0)>();
       else wait_vmcnt<2 * kPer>();
     } else if (NBUF > 2 && ahead >= 1) {
-      if (wave == 0) wait_vmcnt<kPer + 2>();
+      if (wave == 0) wait_vmcnt<kPer + kW0>();
       else wait_vmcnt<kPer>();
     } else {
       wait_vmcnt<0>();
     }
     block_barrier();
     if (it + NBUF - 1 < n_iter)
-      stage(std::integral_constant<int, SN>{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd) {
-        issue(it + NBUF - 1, a, d, l, dd);
-      });
-    stage(sc, [&](uint16_t* a, uint16_t* d, float* l, float* dd) {
-      compute(it, (const char*)a, (const char*)d, l, dd);
+      stage(std::integral_constant<int, SN>{},
+            [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) {
+              issue(it + NBUF - 1, a, d, l, dd, mm);
+            });
+    stage(sc, [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) {
+      compute(it, (const char*)a, (const char*)d, l, dd, mm);
     });
   };
   for (int it = 0; it < n_iter; it += NBUF) {
@@ -602,9 +719,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int key = kw + 32 * kb + l32;
-    if (key < N) {
-      uint16_t* dkp = dK + ((size_t)bg * N + key) * D;
-      uint16_t* dvp = dV + ((size_t)bg * N + key) * D;
+    if (key < Nk) {
+      uint16_t* dkp = dK + ((size_t)bg * Nk + key) * D;
+      uint16_t* dvp = dV + ((size_t)bg * Nk + key) * D;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -643,14 +760,16 @@ struct DqCfg {
   static_assert(kCPW >= 1 && kChunks % kNW == 0, "tile must split evenly over the waves");
 };
 
-template <typename T, int D, int NBUF, bool CAUSAL>
+template <typename T, int D, int NBUF, bool CAUSAL, bool IMASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                    const float* __restrict__ LSE2, const float* __restrict__ Dv,
-                   uint16_t* __restrict__ dQ, int H, int Hkv, int N, int n_qtiles, float scale,
-                   float scale_log2) {
+                   uint16_t* __restrict__ dQ, int H, int Hkv, int Nq, int n_qtiles,
+                   float scale, float scale_log2, const int* __restrict__ kv_lo,
+                   const int* __restrict__ kv_hi, int Nk_arg) {
+  const int Nk = IMASK ? Nk_arg : Nq;  // keys differ from queries only under interval masks
   using C = DqCfg<D, NBUF>;
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
@@ -681,11 +800,12 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int wrow0 = q0 + 32 * wave;
   const int row = wrow0 + l32;
 
-  const uint32_t head_bytes = (uint32_t)N * C::kRowBytes;
-  const auto rq = make_rsrc(Q + (size_t)bh * N * D, head_bytes);
-  const auto rdo = make_rsrc(dO + (size_t)bh * N * D, head_bytes);
-  const auto rk = make_rsrc(K + (size_t)(b * Hkv + kvh) * N * D, head_bytes);
-  const auto rv = make_rsrc(V + (size_t)(b * Hkv + kvh) * N * D, head_bytes);
+  const uint32_t q_bytes = (uint32_t)Nq * C::kRowBytes;
+  const uint32_t kv_bytes = (uint32_t)Nk * C::kRowBytes;
+  const auto rq = make_rsrc(Q + (size_t)bh * Nq * D, q_bytes);
+  const auto rdo = make_rsrc(dO + (size_t)bh * Nq * D, q_bytes);
+  const auto rk = make_rsrc(K + (size_t)(b * Hkv + kvh) * Nk * D, kv_bytes);
+  const auto rv = make_rsrc(V + (size_t)(b * Hkv + kvh) * Nk * D, kv_bytes);
 
   // Q and dO rows of this lane (B operands of S^T = K Q^T and dP^T = V dO^T).
   vec8 qf[D / 16], df[D / 16];
@@ -697,8 +817,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       df[c] = as_vec8<T>(buffer_load16(rdo, rowoff + (16 * c + 8 * hi) * 2));
     }
   }
-  const float lse2 = row < N ? LSE2[(size_t)bh * N + row] : 0.f;
-  const float drow = row < N ? Dv[(size_t)bh * N + row] : 0.f;
+  const float lse2 = row < Nq ? LSE2[(size_t)bh * Nq + row] : 0.f;
+  const float drow = row < Nq ? Dv[(size_t)bh * Nq + row] : 0.f;
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -706,8 +826,49 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
 
-  int n_kt = (N + C::kBC - 1) / C::kBC;
+  int kt0 = 0;  // first key tile of the loop
+  int n_kt = (Nk + C::kBC - 1) / C::kBC;
   if (CAUSAL) n_kt = min(n_kt, (q0 + C::kRows + C::kBC - 1) / C::kBC);
+
+  // Interval masks (as in the forward): this row's keys lo .. hi (empty: lo = Nk,
+  // hi = -1), the wave's union and intersection of its rows' intervals, and the
+  // workgroup's tile range.
+  int lo_r = 0, hi_r = 0, w_lo = 0, w_hi = 0, w_maxlo = 0, w_minhi = 0;
+  if constexpr (IMASK) {
+    __shared__ int wg_bounds[2 * C::kNW];
+    lo_r = Nk;
+    hi_r = -1;
+    if (row < Nq) {
+      lo_r = max(kv_lo[(size_t)b * Nq + row], 0);
+      hi_r = min(kv_hi[(size_t)b * Nq + row], Nk - 1);
+      if (lo_r > hi_r) {
+        lo_r = Nk;
+        hi_r = -1;
+      }
+    }
+    w_lo = w_maxlo = lo_r;
+    w_hi = w_minhi = hi_r;
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+      w_lo = min(w_lo, __shfl_xor(w_lo, off));
+      w_hi = max(w_hi, __shfl_xor(w_hi, off));
+      w_maxlo = max(w_maxlo, __shfl_xor(w_maxlo, off));
+      w_minhi = min(w_minhi, __shfl_xor(w_minhi, off));
+    }
+    if (lane == 0) {
+      wg_bounds[2 * wave] = w_lo;
+      wg_bounds[2 * wave + 1] = w_hi;
+    }
+    __syncthreads();
+    int g_lo = Nk, g_hi = -1;
+#pragma unroll
+    for (int w = 0; w < C::kNW; ++w) {
+      g_lo = min(g_lo, wg_bounds[2 * w]);
+      g_hi = max(g_hi, wg_bounds[2 * w + 1]);
+    }
+    kt0 = g_hi >= g_lo ? g_lo / C::kBC : 0;
+    n_kt = g_hi >= g_lo ? g_hi / C::kBC + 1 - kt0 : 0;
+  }
 
   uint32_t goff[C::kCPW];
 #pragma unroll
@@ -718,7 +879,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     goff[i] = r * C::kRowBytes + ((pg ^ bwd_swz<D>(r)) * 16);
   }
   auto issue = [&](int kt, uint16_t* lk, uint16_t* lv) __attribute__((always_inline)) {
-    const uint32_t base = (uint32_t)kt * C::kBC * C::kRowBytes;
+    const uint32_t base = (uint32_t)(kt0 + kt) * C::kBC * C::kRowBytes;
 #pragma unroll
     for (int i = 0; i < C::kCPW; ++i) {
       const int ch = wave * C::kCPW + i;
@@ -743,9 +904,11 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
 
   auto compute = [&](int kt, const char* kbase, const char* vbase) __attribute__((always_inline)) {
-    const int k0 = kt * C::kBC;
+    const int k0 = (kt0 + kt) * C::kBC;
     if (CAUSAL && k0 > wrow0 + 31) return;  // every key of the tile is after every row
-    const bool need_mask = (k0 + C::kBC > N) || (CAUSAL && k0 + C::kBC - 1 > wrow0);
+    if (IMASK && (k0 > w_hi || k0 + C::kBC - 1 < w_lo)) return;  // no row of the wave sees it
+    const bool need_mask = (k0 + C::kBC > Nk) || (CAUSAL && k0 + C::kBC - 1 > wrow0) ||
+                           (IMASK && !(k0 >= w_maxlo && k0 + C::kBC - 1 <= w_minhi));
 #pragma unroll
     for (int kb = 0; kb < C::kBC / 32; ++kb) {
       // S^T = K Q^T, dP^T = V dO^T (lane = query row, register = key)
@@ -768,7 +931,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         float pv = fast_exp2(fmaf(s[r], scale_log2, -lse2));
         if (need_mask) {
           const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= N || (CAUSAL && key > row)) pv = 0.f;
+          if (key >= Nk || (CAUSAL && key > row) || (IMASK && (key < lo_r || key > hi_r))) pv = 0.f;
         }
         dsv[r] = pv * (dp[r] - drow);
       }
@@ -830,8 +993,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       if (kt + 3 < n_kt) step(std::integral_constant<int, 3>{}, kt + 3);
   }
 
-  if (row < N) {
-    uint16_t* qp = dQ + ((size_t)bh * N + row) * D;
+  if (row < Nq) {
+    uint16_t* qp = dQ + ((size_t)bh * Nq + row) * D;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -850,7 +1013,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 template <typename E, int D>
 static hipError_t preprocess_t(const BwdArgs& a) {
   constexpr int kTPR = D / (16 / sizeof(E));
-  const long long rows = (long long)a.B * a.H * a.N;
+  const long long rows = (long long)a.B * a.H * a.N;  // query rows
   const long long blocks = (rows + (256 / kTPR) - 1) / (256 / kTPR);
   hipLaunchKernelGGL((bwd_preprocess_kernel<E, D>), dim3((unsigned)blocks), dim3(256), 0,
                      (hipStream_t)a.stream, (const E*)a.o, (const E*)a.dO, a.lse, a.dvec, a.lse2,
@@ -858,10 +1021,20 @@ static hipError_t preprocess_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_preprocess(const BwdArgs& a) {
+static hipError_t preprocess_dt(const BwdArgs& a) {
   if (a.dtype == 0) return a.d == 64 ? preprocess_t<float, 64>(a) : preprocess_t<float, 128>(a);
   if (a.dtype == 1) return a.d == 64 ? preprocess_t<_Float16, 64>(a) : preprocess_t<_Float16, 128>(a);
   return a.d == 64 ? preprocess_t<__bf16, 64>(a) : preprocess_t<__bf16, 128>(a);
+}
+
+hipError_t launch_bwd_preprocess(const BwdArgs& a) {
+  hipError_t e = preprocess_dt(a);
+  if (e != hipSuccess || !a.kv_lo) return e;
+  const int n_qt = (a.N + 63) / 64;
+  hipLaunchKernelGGL(mask_tiles_kernel, dim3((unsigned)n_qt, (unsigned)a.B), dim3(64), 0,
+                     (hipStream_t)a.stream, a.kv_lo, a.kv_hi, (i32x4*)a.tile_sum, a.N,
+                     a.Nk ? a.Nk : a.N, n_qt);
+  return hipGetLastError();
 }
 
 #ifndef OSATTN_BWD_NBUF
@@ -871,19 +1044,21 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a) {
 #define OSATTN_DKDV_NBUF 4
 #endif
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool IMASK>
 static hipError_t bwd_t(const BwdArgs& a) {
   constexpr int NB = OSATTN_BWD_NBUF;
   constexpr int NBK = OSATTN_DKDV_NBUF;
   const float sl2 = a.scale * kLog2e;
+  const int Nk = a.Nk ? a.Nk : a.N;
   if (a.stages & kStageDkdv) {
     using C = DkdvCfg<D, NBK>;
-    const int n_kt = (a.N + C::kKeys - 1) / C::kKeys;
+    const int n_kt = (Nk + C::kKeys - 1) / C::kKeys;
     const long long blocks = (long long)n_kt * a.B * a.Hkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NBK, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0,
-                       (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse2, a.dvec,
-                       (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.Hkv, a.N, n_kt, a.scale, sl2);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NBK, CAUSAL, IMASK>), dim3((unsigned)blocks),
+                       dim3(256), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse2,
+                       a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.Hkv, a.N, n_kt,
+                       a.scale, sl2, a.kv_lo, a.kv_hi, (const i32x4*)a.tile_sum, Nk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -891,18 +1066,20 @@ static hipError_t bwd_t(const BwdArgs& a) {
     using C = DqCfg<D, NB>;
     const int n_qt = (a.N + C::kRows - 1) / C::kRows;
     const long long blocks = (long long)n_qt * a.B * a.H;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, NB, CAUSAL>), dim3((unsigned)blocks), dim3(512), 0,
-                       (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse2, a.dvec,
-                       (uint16_t*)a.dq, a.H, a.Hkv, a.N, n_qt, a.scale, sl2);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, NB, CAUSAL, IMASK>), dim3((unsigned)blocks),
+                       dim3(512), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse2,
+                       a.dvec, (uint16_t*)a.dq, a.H, a.Hkv, a.N, n_qt, a.scale, sl2,
+                       a.kv_lo, a.kv_hi, Nk);
   }
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t bwd_dt(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? bwd_t<T, 64, true>(a) : bwd_t<T, 64, false>(a);
-  return a.causal ? bwd_t<T, 128, true>(a) : bwd_t<T, 128, false>(a);
+  if (a.kv_lo) return a.d == 64 ? bwd_t<T, 64, false, true>(a) : bwd_t<T, 128, false, true>(a);
+  if (a.d == 64) return a.causal ? bwd_t<T, 64, true, false>(a) : bwd_t<T, 64, false, false>(a);
+  return a.causal ? bwd_t<T, 128, true, false>(a) : bwd_t<T, 128, false, false>(a);
 }
 
 hipError_t launch_bwd_mfma(const BwdArgs& a) {

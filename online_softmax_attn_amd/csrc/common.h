@@ -20,6 +20,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -136,11 +137,23 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane i of the wave
-// writes lds_chunk + 16*i (lds_chunk is wave-uniform and 16-byte aligned).
+// writes lds_chunk + 16*i (lds_chunk is wave-uniform and 16-byte aligned).  The
+// global offset is voff (per lane) + soff (wave-uniform, a scalar register): keeping
+// the per-lane part loop-invariant and the tile base scalar leaves no short-lived
+// address VGPR behind the DMA (the compiler treats the address register of an LDS
+// DMA as busy until the load completes, so a reused temporary would make later
+// LDS reads into it wait for the whole DMA).
 __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_chunk,
-                                                  uint32_t off) {
+                                                  uint32_t voff, uint32_t soff = 0) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)lds_chunk, 16, off, 0, 0, 0);
+      r, (__attribute__((address_space(3))) void*)lds_chunk, 16, voff, soff, 0, 0);
+}
+
+// 4 bytes per lane into LDS (lane i writes lds + 4*i); same offset split.
+__device__ __forceinline__ void buffer_load4_lds(__amdgpu_buffer_rsrc_t r, void* lds,
+                                                 uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                           voff, soff, 0, 0);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): the fence would

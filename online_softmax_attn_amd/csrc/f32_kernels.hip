@@ -137,45 +137,56 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
 
 // dK, dV for 32 key rows of one key/value head, looping over every query row of
 // every query head in its group (single writer per key row).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    float* __restrict__ dK, float* __restrict__ dV, int H, int Hkv, int N, float scale) {
+    float* __restrict__ dK, float* __restrict__ dV, int H, int Hkv, int Nq, int Nk, float scale,
+    const int* __restrict__ kv_lo, const int* __restrict__ kv_hi) {
   __shared__ float qs[kRows * D];
   __shared__ float dos[kRows * D];
   __shared__ float lse_s[kRows];
   __shared__ float d_s[kRows];
+  __shared__ int lo_s[kRows], hi_s[kRows];
   const int lane = threadIdx.x;
   const int half = lane >> 5;
   const int bg = blockIdx.y;  // b * Hkv + kvh
   const int kvh = bg % Hkv, b = bg / Hkv;
   const int n_rep = H / Hkv;
-  const int key = blockIdx.x * kRows + (lane & 31);
-  const float* Kp = K + (size_t)bg * N * D;
-  const float* Vp = V + (size_t)bg * N * D;
+  const int key0 = blockIdx.x * kRows;
+  const int key = key0 + (lane & 31);
+  const float* Kp = K + (size_t)bg * Nk * D;
+  const float* Vp = V + (size_t)bg * Nk * D;
 
   float kr[D / 2], vr[D / 2], dk[D / 2], dv[D / 2];
 #pragma unroll
   for (int c = 0; c < D / 2; ++c) {
-    kr[c] = key < N ? Kp[(size_t)key * D + half * (D / 2) + c] : 0.f;
-    vr[c] = key < N ? Vp[(size_t)key * D + half * (D / 2) + c] : 0.f;
+    kr[c] = key < Nk ? Kp[(size_t)key * D + half * (D / 2) + c] : 0.f;
+    vr[c] = key < Nk ? Vp[(size_t)key * D + half * (D / 2) + c] : 0.f;
     dk[c] = 0.f;
     dv[c] = 0.f;
   }
   const int first_q = CAUSAL ? blockIdx.x * kRows : 0;
   for (int r = 0; r < n_rep; ++r) {
     const int bh = b * H + kvh * n_rep + r;
-    const float* Qp = Q + (size_t)bh * N * D;
-    const float* dOp = dO + (size_t)bh * N * D;
-    for (int i0 = first_q; i0 < N; i0 += kRows) {
+    const float* Qp = Q + (size_t)bh * Nq * D;
+    const float* dOp = dO + (size_t)bh * Nq * D;
+    for (int i0 = first_q; i0 < Nq; i0 += kRows) {
+      if constexpr (MASK) {
+        // Skip 32-row query tiles none of whose rows sees these 32 keys.
+        int lo, hi, w_lo, w_hi;
+        row_interval(kv_lo, kv_hi, b, Nq, Nk, i0 + (lane & 31), lo, hi);
+        wave_span(lo, hi, w_lo, w_hi);
+        if (w_hi < key0 || w_lo > key0 + kRows - 1) continue;
+      }
       __syncthreads();
-      stage_rows<D>(qs, Qp, i0, N);
-      stage_rows<D>(dos, dOp, i0, N);
+      stage_rows<D>(qs, Qp, i0, Nq);
+      stage_rows<D>(dos, dOp, i0, Nq);
       if (lane < kRows) {
         const int i = i0 + lane;
-        lse_s[lane] = i < N ? LSE[(size_t)bh * N + i] : INFINITY;
-        d_s[lane] = i < N ? Dv[(size_t)bh * N + i] : 0.f;
+        lse_s[lane] = i < Nq ? LSE[(size_t)bh * Nq + i] : INFINITY;
+        d_s[lane] = i < Nq ? Dv[(size_t)bh * Nq + i] : 0.f;
+        if constexpr (MASK) row_interval(kv_lo, kv_hi, b, Nq, Nk, i, lo_s[lane], hi_s[lane]);
       }
       __syncthreads();
       for (int ii = 0; ii < kRows; ++ii) {
@@ -184,7 +195,8 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
         s = (s + __shfl_xor(s, 32)) * scale;
         float dp = half_dot<D>(vr, dos + ii * D + half * (D / 2));
         dp = dp + __shfl_xor(dp, 32);
-        const bool masked = (i >= N) || (CAUSAL && key > i);
+        const bool masked = (i >= Nq) || (CAUSAL && key > i) ||
+                            (MASK && (key < lo_s[ii] || key > hi_s[ii]));
         const float p = masked ? 0.f : expf(s - lse_s[ii]);
         const float ds = p * (dp - d_s[ii]);
         const float* qrow = qs + ii * D + half * (D / 2);
@@ -197,21 +209,22 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
       }
     }
   }
-  if (key < N) {
+  if (key < Nk) {
 #pragma unroll
     for (int c = 0; c < D / 2; ++c) {
-      dK[(size_t)bg * N * D + (size_t)key * D + half * (D / 2) + c] = dk[c] * scale;
-      dV[(size_t)bg * N * D + (size_t)key * D + half * (D / 2) + c] = dv[c];
+      dK[(size_t)bg * Nk * D + (size_t)key * D + half * (D / 2) + c] = dk[c] * scale;
+      dV[(size_t)bg * Nk * D + (size_t)key * D + half * (D / 2) + c] = dv[c];
     }
   }
 }
 
 // dQ for 32 query rows, looping over the key/value tiles they see.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    float* __restrict__ dQ, int H, int Hkv, int N, float scale) {
+    float* __restrict__ dQ, int H, int Hkv, int Nq, int Nk, float scale,
+    const int* __restrict__ kv_lo, const int* __restrict__ kv_hi) {
   __shared__ float ks[kRows * D];
   __shared__ float vs[kRows * D];
   const int lane = threadIdx.x;
@@ -220,24 +233,32 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
   const int h = bh % H, b = bh / H;
   const int kvh = h / (H / Hkv);
   const int row = blockIdx.x * kRows + (lane & 31);
-  const float* Kp = K + (size_t)(b * Hkv + kvh) * N * D;
-  const float* Vp = V + (size_t)(b * Hkv + kvh) * N * D;
+  const float* Kp = K + (size_t)(b * Hkv + kvh) * Nk * D;
+  const float* Vp = V + (size_t)(b * Hkv + kvh) * Nk * D;
 
   float q[D / 2], dor[D / 2], dq[D / 2];
 #pragma unroll
   for (int c = 0; c < D / 2; ++c) {
-    q[c] = row < N ? Q[((size_t)bh * N + row) * D + half * (D / 2) + c] : 0.f;
-    dor[c] = row < N ? dO[((size_t)bh * N + row) * D + half * (D / 2) + c] : 0.f;
+    q[c] = row < Nq ? Q[((size_t)bh * Nq + row) * D + half * (D / 2) + c] : 0.f;
+    dor[c] = row < Nq ? dO[((size_t)bh * Nq + row) * D + half * (D / 2) + c] : 0.f;
     dq[c] = 0.f;
   }
-  const float lse = row < N ? LSE[(size_t)bh * N + row] : INFINITY;
-  const float dd = row < N ? Dv[(size_t)bh * N + row] : 0.f;
-  int n_keys = N;
-  if (CAUSAL) n_keys = min(N, blockIdx.x * kRows + kRows);
-  for (int k0 = 0; k0 < n_keys; k0 += kRows) {
+  const float lse = row < Nq ? LSE[(size_t)bh * Nq + row] : INFINITY;
+  const float dd = row < Nq ? Dv[(size_t)bh * Nq + row] : 0.f;
+  int k_begin = 0, k_end = Nk;
+  if (CAUSAL) k_end = min(Nk, blockIdx.x * kRows + kRows);
+  int lo = 0, hi = Nk - 1;
+  if constexpr (MASK) {
+    row_interval(kv_lo, kv_hi, b, Nq, Nk, row, lo, hi);
+    int w_lo, w_hi;
+    wave_span(lo, hi, w_lo, w_hi);
+    k_begin = w_hi >= 0 ? (w_lo / kRows) * kRows : 0;
+    k_end = w_hi >= 0 ? w_hi + 1 : 0;
+  }
+  for (int k0 = k_begin; k0 < k_end; k0 += kRows) {
     __syncthreads();
-    stage_rows<D>(ks, Kp, k0, N);
-    stage_rows<D>(vs, Vp, k0, N);
+    stage_rows<D>(ks, Kp, k0, Nk);
+    stage_rows<D>(vs, Vp, k0, Nk);
     __syncthreads();
     for (int j = 0; j < kRows; ++j) {
       const int key = k0 + j;
@@ -245,7 +266,8 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
       s = (s + __shfl_xor(s, 32)) * scale;
       float dp = half_dot<D>(dor, vs + j * D + half * (D / 2));
       dp = dp + __shfl_xor(dp, 32);
-      const bool masked = (key >= N) || (row >= N) || (CAUSAL && key > row);
+      const bool masked = (key >= Nk) || (row >= Nq) || (CAUSAL && key > row) ||
+                          (MASK && (key < lo || key > hi));
       const float p = masked ? 0.f : expf(s - lse);
       const float ds = p * (dp - dd);
       const float* krow = ks + j * D + half * (D / 2);
@@ -253,9 +275,9 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
       for (int c = 0; c < D / 2; ++c) dq[c] = fmaf(ds, krow[c], dq[c]);
     }
   }
-  if (row < N) {
+  if (row < Nq) {
 #pragma unroll
-    for (int c = 0; c < D / 2; ++c) dQ[((size_t)bh * N + row) * D + half * (D / 2) + c] = dq[c] * scale;
+    for (int c = 0; c < D / 2; ++c) dQ[((size_t)bh * Nq + row) * D + half * (D / 2) + c] = dq[c] * scale;
   }
 }
 
@@ -268,21 +290,24 @@ hipError_t fwd_f32_t(const FwdArgs& a) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool MASK>
 hipError_t bwd_f32_t(const BwdArgs& a) {
+  const int Nk = a.Nk ? a.Nk : a.N;
   if (a.stages & kStageDkdv) {
-    dim3 gk((a.N + kRows - 1) / kRows, a.B * a.Hkv);
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), gk, dim3(64), 0, (hipStream_t)a.stream,
-                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dO,
-                       a.lse, a.dvec, (float*)a.dk, (float*)a.dv, a.H, a.Hkv, a.N, a.scale);
+    dim3 gk((Nk + kRows - 1) / kRows, a.B * a.Hkv);
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL, MASK>), gk, dim3(64), 0,
+                       (hipStream_t)a.stream, (const float*)a.q, (const float*)a.k,
+                       (const float*)a.v, (const float*)a.dO, a.lse, a.dvec, (float*)a.dk,
+                       (float*)a.dv, a.H, a.Hkv, a.N, Nk, a.scale, a.kv_lo, a.kv_hi);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.stages & kStageDq) {
     dim3 gq((a.N + kRows - 1) / kRows, a.B * a.H);
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), gq, dim3(64), 0, (hipStream_t)a.stream,
-                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dO,
-                       a.lse, a.dvec, (float*)a.dq, a.H, a.Hkv, a.N, a.scale);
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL, MASK>), gq, dim3(64), 0,
+                       (hipStream_t)a.stream, (const float*)a.q, (const float*)a.k,
+                       (const float*)a.v, (const float*)a.dO, a.lse, a.dvec, (float*)a.dq, a.H,
+                       a.Hkv, a.N, Nk, a.scale, a.kv_lo, a.kv_hi);
   }
   return hipGetLastError();
 }
@@ -296,8 +321,9 @@ hipError_t launch_fwd_f32(const FwdArgs& a) {
 }
 
 hipError_t launch_bwd_f32(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? bwd_f32_t<64, true>(a) : bwd_f32_t<64, false>(a);
-  return a.causal ? bwd_f32_t<128, true>(a) : bwd_f32_t<128, false>(a);
+  if (a.kv_lo) return a.d == 64 ? bwd_f32_t<64, false, true>(a) : bwd_f32_t<128, false, true>(a);
+  if (a.d == 64) return a.causal ? bwd_f32_t<64, true, false>(a) : bwd_f32_t<64, false, false>(a);
+  return a.causal ? bwd_f32_t<128, true, false>(a) : bwd_f32_t<128, false, false>(a);
 }
 
 }  // namespace osattn

@@ -47,6 +47,11 @@ struct BwdArgs {
   int dtype;
   void* stream;
   int stages;  // bit set of kStageDkdv and kStageDq: which backward kernels to launch
+  // Interval masks (attn_bwd_masked): N is the query count, Nk the key count.
+  int Nk = 0;                  // 0: same as N
+  const int* kv_lo = nullptr;  // nullptr: no interval mask
+  const int* kv_hi = nullptr;
+  void* tile_sum = nullptr;    // workspace: per 64-row query tile, 4 int32 (see bwd kernels)
 };
 
 struct SplitArgs {

@@ -263,3 +263,38 @@ def masked(**kw):
 ], ids=lambda x: str(x))
 def test_masked_fwd_rejects(kw, code):
     assert masked(**kw) == S[code]
+
+
+def masked_bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=4, Hkv=2, Nq=3, Nk=100,
+             d=128, scale=0.125, lo=P, hi=P, dtype=2, ws=P, ws_bytes=1 << 24, stream=None)
+    a.update(kw)
+    return osa.library().attn_bwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"],
+                                         a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["Hkv"],
+                                         a["Nq"], a["Nk"], a["d"], a["scale"], a["lo"], a["hi"],
+                                         a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"do": None}, "ATTN_ERR_NULL"),
+    ({"hi": None}, "ATTN_ERR_NULL"),
+    ({"Nk": 0}, "ATTN_ERR_SHAPE"),
+    ({"d": 80}, "ATTN_ERR_HEAD_DIM"),
+    ({"H": 5}, "ATTN_ERR_GQA"),
+    ({"dtype": 4}, "ATTN_ERR_DTYPE"),
+    ({"scale": float("inf")}, "ATTN_ERR_SCALE"),
+    ({"ws": None}, "ATTN_ERR_WORKSPACE"),
+    ({"ws_bytes": 512}, "ATTN_ERR_WORKSPACE"),
+    ({"dv": P + 2}, "ATTN_ERR_ALIGN"),
+    ({"lo": P + 1}, "ATTN_ERR_ALIGN"),
+], ids=lambda x: str(x))
+def test_masked_bwd_rejects(kw, code):
+    assert masked_bwd(**kw) == S[code]
+
+
+def test_masked_bwd_workspace_bytes():
+    f = osa.library().attn_bwd_masked_workspace_bytes
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert f(2, 4, 2, 100, 300, 128, 2) == 2 * r256(2 * 4 * 100 * 4) + r256(2 * 2 * 16)
+    assert f(1, 1, 1, 1, 1, 64, 0) == 2 * 256 + 256
+    assert f(1, 4, 2, 100, 0, 128, 2) == 0

@@ -13,6 +13,16 @@ from gpu_parity import TOL_O, f64, max_abs, need_gpu, out_err, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
+def run_masked_bwd(inp, lo, hi, scale):
+    import online_softmax_attn_amd as osa
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    lo_d, hi_d = to_dev(lo), to_dev(hi)
+    o, lse = osa.attn_fwd_masked(q, k, v, lo_d, hi_d, scale=scale)
+    dq, dk, dv = osa.attn_bwd_masked(q, k, v, o, lse, do, lo_d, hi_d, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
 def run_masked(inp, lo, hi, scale):
     import online_softmax_attn_amd as osa
     q, k, v = (to_dev(inp[n]) for n in ("q", "k", "v"))
@@ -130,3 +140,90 @@ def test_masked_full_size_sampled(case):
             err_l = max(err_l, max_abs(f64(lse[b, h])[rows], rl))
     say(f"[masked] {name} sampled o={err_o:.2e} lse={err_l:.2e}")
     assert err_o <= TOL_O[dtype] and err_l <= TOL_O[dtype]
+
+
+def check_masked_bwd(dtype, B, H, Hkv, Nq, Nk, d, kind, seed, **mk):
+    from gpu_parity import TOL_G, rel_err
+    w = S.custom(dtype, B, H, Hkv, Nq, d, False, seed_base=seed, Nk=Nk if Nk != Nq else 0)
+    inp = S.make_inputs(w, with_grad=True)
+    lo, hi = S.mask_intervals(kind, B, Nq, Nk, seed=seed, **mk)
+    o, lse, dq, dk, dv = run_masked_bwd(inp, lo, hi, w.scale)
+    ref = A.attention_backward_intervals(inp["q"], inp["k"], inp["v"], inp["do"], w.scale,
+                                         lo.numpy(), hi.numpy())
+    label = f"bwd {kind} {dtype} B{B}H{H}Hkv{Hkv}Nq{Nq}Nk{Nk}d{d} {mk}"
+    compare(o, lse, ref["o"], ref["lse"], dtype, label)
+    errs = {}
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        g = f64(t)
+        assert np.all(np.isfinite(g)), name
+        # A gradient that is exactly zero in real arithmetic (every row sees one key)
+        # is checked in absolute terms, as the unmasked parity tests do at N = 1.
+        zero = not np.any(ref[name])
+        errs[name] = rel_err(g, ref[name], floor=1.0 if zero else 1e-2)
+    say(f"[masked]   grads {', '.join(f'{k}={v:.2e}' for k, v in errs.items())}")
+    for name, e in errs.items():
+        assert e <= TOL_G[dtype], errs
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", MASKS, ids=lambda m: m[0] + "_" + "_".join(f"{k}{v}" for k, v in m[1].items()))
+@pytest.mark.parametrize("shape", [(1, 2, 1, 1, 1), (2, 4, 2, 200, 200), (1, 3, 1, 333, 333),
+                                   (1, 4, 2, 77, 300)],
+                         ids=lambda s: "B{}H{}Hkv{}Nq{}Nk{}".format(*s))
+def test_masked_bwd_small(dtype, d, mask, shape):
+    need_gpu()
+    kind, mk = mask
+    B, H, Hkv, Nq, Nk = shape
+    check_masked_bwd(dtype, B, H, Hkv, Nq, Nk, d, kind, 9900 + Nq, **mk)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked_bwd_documents(dtype, causal):
+    need_gpu()
+    lens = [[100, 3, 250, 1, 46], [400]]
+    check_masked_bwd(dtype, 2, 4, 2, 400, 400, 128, "document", 9950, doc_lens=lens, causal=causal)
+
+
+def test_masked_bwd_causal_matches_attn_bwd():
+    """The causal mask as intervals gives the causal backward's gradients."""
+    need_gpu()
+    import online_softmax_attn_amd as osa
+    from gpu_parity import TOL_G, rel_err
+    w = S.custom("bf16", 1, 4, 2, 700, 128, True, seed_base=9960)
+    inp = S.make_inputs(w, with_grad=True)
+    lo, hi = S.mask_intervals("causal", 1, 700, 700)
+    _, _, dq1, dk1, dv1 = run_masked_bwd(inp, lo, hi, w.scale)
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    o, lse = osa.attn_fwd(q, k, v, causal=True, scale=w.scale)
+    dq2, dk2, dv2 = osa.attn_bwd(q, k, v, o, lse, do, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    for a, b in ((dq1, dq2), (dk1, dk2), (dv1, dv2)):
+        assert rel_err(f64(a), f64(b)) <= TOL_G["bf16"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("case", FULL, ids=lambda c: c[0])
+def test_masked_bwd_full_size_groups(case):
+    """Full-size masked backward: two (batch, kv-head) groups against the oracle."""
+    need_gpu()
+    from gpu_parity import TOL_G, rel_err
+    name, dtype, B, H, Hkv, N, d, kind, mk = case
+    w = S.custom(dtype, B, H, Hkv, N, d, False, seed_base=9800)
+    inp = S.make_inputs(w, with_grad=True)
+    lo, hi = S.mask_intervals(kind, B, N, N, **mk)
+    o, lse, dq, dk, dv = run_masked_bwd(inp, lo, hi, w.scale)
+    groups = [(0, 0), (B - 1, Hkv - 1)]
+    ref = A.attention_backward_intervals(inp["q"], inp["k"], inp["v"], inp["do"], w.scale,
+                                         lo.numpy(), hi.numpy(), heads=groups)
+    n_rep = H // Hkv
+    for b, g in groups:
+        hs = slice(g * n_rep, (g + 1) * n_rep)
+        e = {"dq": rel_err(f64(dq[b, hs]), ref["dq"][b, hs]),
+             "dk": rel_err(f64(dk[b, g]), ref["dk"][b, g]),
+             "dv": rel_err(f64(dv[b, g]), ref["dv"][b, g]),
+             "o": out_err(f64(o[b, hs]), ref["o"][b, hs])}
+        say(f"[masked] {name} group ({b},{g}) {', '.join(f'{k}={v:.2e}' for k, v in e.items())}")
+        assert e["o"] <= TOL_O[dtype]
+        assert max(e["dq"], e["dk"], e["dv"]) <= TOL_G[dtype], e
