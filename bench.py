@@ -1,7 +1,7 @@
 """Throughput benchmark of the fused attention path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--sweep] [--decode]
+                    [--no-cpu-baseline] [--sweep] [--decode] [--masked]
 
 A step is one pass of the whole path over one batch of resident synthetic input:
 the forward kernel (O and LSE) followed by the backward (D preprocess, dK/dV
@@ -185,6 +185,8 @@ def main():
                     help="time every point of the bf16 sweep (one JSON line each)")
     ap.add_argument("--decode", action="store_true",
                     help="time the split-KV forward on the decoding workloads (one line each)")
+    ap.add_argument("--masked", action="store_true",
+                    help="time the interval-masked fwd+bwd on the masked workloads (one line each)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 512 MiB device copies (for scaling HBM counters)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -227,6 +229,10 @@ def main():
     if args.decode:
         for w in S.DECODE.values():
             print(json.dumps(run_decode(w, args, osa, torch)), flush=True)
+        return
+    if args.masked:
+        for name, (w, kind, mk) in S.MASKED.items():
+            print(json.dumps(run_masked(name, w, kind, mk, args, osa, torch)), flush=True)
         return
     w = S.WORKLOADS[args.workload] if args.workload else S.HEADLINE
     print(json.dumps(run_one(w, args, osa, torch, with_cpu=not args.no_cpu_baseline)), flush=True)
@@ -303,6 +309,58 @@ def run_decode(w, args, osa, torch):
                          "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": algo,
                          "ms": {k2: round(x, 4) for k2, x in st.items()}}}
+
+
+def run_masked(name, w, kind, mk, args, osa, torch):
+    """Interval-masked forward + backward; FLOP counted on the visible (query, key)
+    pairs only: 4*d per pair and head forward, 2.5x that backward."""
+    import synthetic as S
+
+    inp = S.make_inputs(w, with_grad=True)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    lo, hi = S.mask_intervals(kind, w.B, w.N, w.nk, **mk)
+    pairs = S.visible_pairs(lo, hi, w.nk)
+    lo, hi = lo.cuda(), hi.cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), device="cuda", dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(osa.attn_bwd_masked_workspace_bytes(w.B, w.H, w.Hkv, w.N, w.nk, w.d, q.dtype),
+                     device="cuda", dtype=torch.uint8)
+    fwd = lambda: osa.attn_fwd_masked(q, k, v, lo, hi, scale=w.scale, out=o, lse=lse)
+    bwd = lambda: osa.attn_bwd_masked(q, k, v, o, lse, do, lo, hi, scale=w.scale, dq=dq, dk=dk,
+                                      dv=dv, workspace=ws)
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    f_ms = stats([e[0].elapsed_time(e[1]) for e in ev])["mean"]
+    b_ms = stats([e[1].elapsed_time(e[2]) for e in ev])["mean"]
+    ff = 4.0 * w.H * w.d * pairs
+    bf = 2.5 * ff
+    peak = PEAK_TFLOPS[w.dtype]
+    val = (ff + bf) / ((f_ms + b_ms) * 1e-3) / 1e12
+    dense = 4.0 * w.B * w.H * w.N * w.nk * w.d
+    return {"metric": "interval-masked attention fwd+bwd TFLOP/s on visible pairs",
+            "value": round(val, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(f_ms + b_ms, 4), "higher_is_better": True,
+            "dtype": w.dtype, "data": "synthetic",
+            "config": dict(w.describe(), workload=name, mask=kind,
+                           mask_params={k2: (v2 if k2 != "doc_lens" else "per batch")
+                                        for k2, v2 in mk.items()}),
+            "visible_fraction": round(pairs * w.H / (dense / (4.0 * w.d)), 4),
+            "fwd": {"ms": round(f_ms, 4), "tflops": round(ff / (f_ms * 1e-3) / 1e12, 2),
+                    "frac_peak": round(ff / (f_ms * 1e-3) / 1e12 / peak, 4)},
+            "bwd": {"ms": round(b_ms, 4), "tflops": round(bf / (b_ms * 1e-3) / 1e12, 2),
+                    "frac_peak": round(bf / (b_ms * 1e-3) / 1e12 / peak, 4)}}
 
 
 def stats(xs):

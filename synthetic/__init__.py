@@ -222,3 +222,21 @@ def mask_intervals(kind: str, B: int, Nq: int, Nk: int, seed: int = 0, **kw):
     lo = lo.to(torch.int32).expand(B, Nq).contiguous()
     hi = hi.to(torch.int32).expand(B, Nq).contiguous()
     return lo, hi
+
+
+# Masked workloads (interval masks): a 4096-key causal sliding window on the GQA shape,
+# and packed documents of mixed lengths (causal within each document).
+MASKED = {
+    "sliding4096_bf16_gqa": (custom("bf16", 1, 32, 8, 16384, 128, False, seed_base=7000),
+                             "sliding", {"left": 4095, "causal": True}),
+    "documents_bf16": (custom("bf16", 4, 16, 16, 8192, 128, False, seed_base=7100), "document",
+                       {"doc_lens": [[3000, 2000, 3192], [8192], [1, 4095, 4096], [100] * 81 + [92]],
+                        "causal": True}),
+}
+
+
+def visible_pairs(kv_lo, kv_hi, Nk: int) -> int:
+    """Number of (query, key) pairs an interval mask leaves visible, over the batch."""
+    lo = kv_lo.to(torch.int64).clamp(min=0)
+    hi = kv_hi.to(torch.int64).clamp(max=Nk - 1)
+    return int((hi - lo + 1).clamp(min=0).sum())
