@@ -18,6 +18,7 @@ import numpy as np
 import oracle.attention as A
 import oracle.brute as BR
 import oracle.online_walk as W
+import oracle.rowsoftmax as RS
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fa2_worked_example.json")
 
@@ -488,6 +489,113 @@ def pin_intervals_finite_differences(seed=34, h=1e-6):
     return worst
 
 
+# --- row softmax, log-softmax, cross-entropy ---------------------------------------
+
+def _fd_rows(f, x, h=1e-6):
+    """Central differences of the scalar f(x) with respect to every entry of x."""
+    g = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        g[idx] = (f(xp) - f(xm)) / (2 * h)
+    return g
+
+
+def pin_row_softmax_fd(seed=40):
+    """Softmax and log-softmax backward against central differences of <g, f(x)>."""
+    r = np.random.default_rng(seed)
+    x, g = r.standard_normal((3, 7)) * 2, r.standard_normal((3, 7))
+    e1 = np.max(np.abs(RS.softmax_backward(RS.softmax(x), g)
+                       - _fd_rows(lambda z: float(np.sum(g * RS.softmax(z))), x)))
+    e2 = np.max(np.abs(RS.log_softmax_backward(RS.log_softmax(x), g)
+                       - _fd_rows(lambda z: float(np.sum(g * RS.log_softmax(z))), x)))
+    return max(e1, e2)
+
+
+def pin_row_xent_fd(seed=41):
+    """Cross-entropy loss gradient against central differences of sum(dloss * loss)."""
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((4, 9)) * 3
+    t = np.array([2, 0, 8, 5])
+    dl = r.standard_normal(4)
+    g = RS.cross_entropy_backward(x, t, dl)
+    fd = _fd_rows(lambda z: float(np.sum(dl * RS.cross_entropy(z, t)[0])), x)
+    return float(np.max(np.abs(g - fd)))
+
+
+def pin_row_xent_three_routes(seed=42):
+    """The page's three routes to the logits gradient agree: p - y directly, the
+    softmax JVP with dL/dS = -y/p, and the log-softmax backward with dL/dY = -y."""
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((5, 6))
+    t = r.integers(0, 6, 5)
+    y = np.zeros_like(x)
+    y[np.arange(5), t] = 1.0
+    p = RS.softmax(x)
+    a = RS.cross_entropy_backward(x, t, np.ones(5))
+    b = RS.softmax_backward(p, -y / p)
+    c = RS.log_softmax_backward(RS.log_softmax(x), -y)
+    return max(np.max(np.abs(a - b)), np.max(np.abs(a - c)))
+
+
+def pin_row_invariants(seed=43):
+    """Rows of P sum to 1, softmax-backward rows sum to 0, exp(log-softmax) = softmax,
+    adding a constant to a row changes nothing, and the loss of a row equals
+    -log p_t; an ignored row (t < 0) has loss 0 and zero gradient."""
+    r = np.random.default_rng(seed)
+    x, g = r.standard_normal((4, 11)) * 4, r.standard_normal((4, 11))
+    p = RS.softmax(x)
+    t = np.array([3, -1, 10, 0])
+    loss, lse = RS.cross_entropy(x, t)
+    gx = RS.cross_entropy_backward(x, t, np.ones(4))
+    errs = [np.max(np.abs(p.sum(-1) - 1)),
+            np.max(np.abs(RS.softmax_backward(p, g).sum(-1))),
+            np.max(np.abs(np.exp(RS.log_softmax(x)) - p)),
+            np.max(np.abs(RS.softmax(x + 7.5) - p)),
+            np.max(np.abs(RS.log_softmax(x - 3.0) - RS.log_softmax(x))),
+            abs(loss[1]), np.max(np.abs(gx[1])),
+            np.max(np.abs(loss[[0, 2, 3]] + np.log(p[[0, 2, 3], t[[0, 2, 3]]])))]
+    return float(max(errs))
+
+
+def pin_row_torch_library(seed=44):
+    """Second opinion: torch CPU softmax, log_softmax and cross_entropy in float64 with
+    autograd (reduction 'none', ignore_index -1)."""
+    import torch
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((6, 13)) * 2
+    g = r.standard_normal((6, 13))
+    t = np.array([1, 12, -1, 0, 7, 7])
+    dl = r.standard_normal(6)
+    err = 0.0
+    for fn, ofn, bfn in ((torch.softmax, RS.softmax, RS.softmax_backward),
+                         (torch.log_softmax, RS.log_softmax, RS.log_softmax_backward)):
+        tx = torch.tensor(x, requires_grad=True)
+        out = fn(tx, dim=-1)
+        out.backward(torch.tensor(g))
+        err = max(err, np.max(np.abs(out.detach().numpy() - ofn(x))),
+                  np.max(np.abs(tx.grad.numpy() - bfn(ofn(x), g))))
+    tx = torch.tensor(x, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(tx, torch.tensor(t), reduction="none", ignore_index=-1)
+    loss.backward(torch.tensor(dl))
+    l_o, _ = RS.cross_entropy(x, t)
+    err = max(err, np.max(np.abs(loss.detach().numpy() - l_o)),
+              np.max(np.abs(tx.grad.numpy() - RS.cross_entropy_backward(x, t, dl))))
+    return float(err)
+
+
+def pin_row_large_logits(seed=45):
+    """Logits near 1e4 (exp overflows without the max): the stable forms stay finite
+    and equal those of the shifted row."""
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((2, 8))
+    big = x + 1e4
+    errs = [np.max(np.abs(RS.softmax(big) - RS.softmax(x))),
+            np.max(np.abs(RS.logsumexp(big) - 1e4 - RS.logsumexp(x)))]
+    return float(max(errs)) if np.all(np.isfinite(RS.softmax(big))) else np.inf
+
+
 ALL_PINS = {
     "worked_example_walk": (pin_worked_example_walk, 1e-12),
     "worked_example_scores": (pin_worked_example_scores, 0.0),
@@ -530,4 +638,10 @@ ALL_PINS = {
     "intervals_brute": (pin_intervals_brute, 1e-13),
     "intervals_wide_window": (pin_intervals_wide_window, 1e-13),
     "intervals_finite_differences": (pin_intervals_finite_differences, 1e-7),
+    "row_softmax_fd": (pin_row_softmax_fd, 1e-8),
+    "row_xent_fd": (pin_row_xent_fd, 1e-7),
+    "row_xent_three_routes": (pin_row_xent_three_routes, 1e-14),
+    "row_invariants": (pin_row_invariants, 1e-13),
+    "row_torch_library": (pin_row_torch_library, 1e-12),
+    "row_large_logits": (pin_row_large_logits, 1e-9),
 }

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as A
+import oracle.rowsoftmax as RS
 import oracle_pins as P
 
 
@@ -108,6 +109,37 @@ def _bad_merge(o_parts, lse_parts, how):
     if how == "mean":
         return np.mean(o_parts, axis=0), m + np.log(z)
     return np.sum(w[..., None] * o_parts, axis=0) / z[..., None], m
+
+
+ROW_MUTANTS = {
+    "row_softmax_bwd_no_dot": ("softmax_backward", lambda y, dy: np.asarray(y) * np.asarray(dy)),
+    "row_logsoftmax_bwd_sign": ("log_softmax_backward",
+                                lambda y, dy: np.asarray(dy) + np.exp(y) * np.sum(dy, -1, keepdims=True)),
+    "row_xent_grad_no_onehot": ("cross_entropy_backward",
+                                lambda x, t, dl: RS.softmax(x) * np.asarray(dl)[:, None]),
+    "row_xent_loss_no_lse": ("cross_entropy", lambda x, t: _xent_no_lse(x, t)),
+    "row_softmax_no_max": ("softmax", lambda x: _softmax_no_max(x)),
+}
+
+
+def _xent_no_lse(x, t):
+    x = np.asarray(x, float)
+    t = np.asarray(t)
+    live = t >= 0
+    zt = np.where(live, x[np.arange(x.shape[0]), np.where(live, t, 0)], 0.0)
+    return np.where(live, -zt, 0.0), np.zeros(x.shape[0])
+
+
+def _softmax_no_max(x):
+    e = np.exp(np.asarray(x, float))
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+@pytest.mark.parametrize("mutant", sorted(ROW_MUTANTS))
+def test_row_mutant_is_caught(mutant, monkeypatch):
+    target, repl = ROW_MUTANTS[mutant]
+    monkeypatch.setattr(RS, target, repl)
+    assert _failing_pins(), f"no pin caught mutant {mutant}"
 
 
 def _failing_pins():
