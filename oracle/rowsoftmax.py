@@ -13,8 +13,9 @@ What it computes (softmax-backward page on shreyansh26.github.io):
     ("LogSoftmax Backward");
   * cross-entropy with logits against a class index t: logsumexp(z) - z_t per row,
     and its gradient (softmax(z) - onehot(t)) times the row's upstream gradient
-    ("Cross-Entropy With Logits").  A negative target marks an ignored row: loss 0,
-    zero gradient (a reading; the page's plain version has no ignored labels).
+    ("Cross-Entropy With Logits").  A target outside 0 .. cols-1 (negative, such as
+    -100, or too large) marks an ignored row: loss 0, zero gradient (a reading; the
+    page's plain version has no ignored labels).
 Rows are independent; x is [rows, cols].
 """
 
@@ -62,23 +63,28 @@ def log_softmax_backward(y, dy):
     return dy - np.exp(y) * np.sum(dy, axis=-1, keepdims=True)
 
 
+def _live(t, cols):
+    return (t >= 0) & (t < cols)
+
+
 def cross_entropy(x, t):
-    """Per-row loss logsumexp(x) - x_t, and the row logsumexp; rows with t < 0 give 0."""
+    """Per-row loss logsumexp(x) - x_t, and the row logsumexp; ignored rows give 0."""
     x = _f64(x)
     t = np.asarray(t, dtype=np.int64)
     lse = logsumexp(x)
-    live = t >= 0
+    live = _live(t, x.shape[-1])
     zt = np.where(live, x[np.arange(x.shape[0]), np.where(live, t, 0)], 0.0)
     return np.where(live, lse - zt, 0.0), lse
 
 
 def cross_entropy_backward(x, t, dloss):
-    """dlogits = dloss_row * (softmax(x) - onehot(t)); zero for rows with t < 0."""
+    """dlogits = dloss_row * (softmax(x) - onehot(t)); zero for ignored rows."""
     x = _f64(x)
     t = np.asarray(t, dtype=np.int64)
+    live = _live(t, x.shape[-1])
     g = softmax(x)
-    rows = np.nonzero(t >= 0)[0]
+    rows = np.nonzero(live)[0]
     g[rows, t[rows]] -= 1.0
     g *= _f64(dloss)[:, None]
-    g[t < 0] = 0.0
+    g[~live] = 0.0
     return g

@@ -542,19 +542,24 @@ def pin_row_xent_three_routes(seed=42):
 def pin_row_invariants(seed=43):
     """Rows of P sum to 1, softmax-backward rows sum to 0, exp(log-softmax) = softmax,
     adding a constant to a row changes nothing, and the loss of a row equals
-    -log p_t; an ignored row (t < 0) has loss 0 and zero gradient."""
+    -log p_t; an ignored row (target outside 0 .. cols-1) has loss 0 and zero gradient."""
     r = np.random.default_rng(seed)
     x, g = r.standard_normal((4, 11)) * 4, r.standard_normal((4, 11))
     p = RS.softmax(x)
     t = np.array([3, -1, 10, 0])
     loss, lse = RS.cross_entropy(x, t)
     gx = RS.cross_entropy_backward(x, t, np.ones(4))
+    t_big = np.array([3, 11, -100, 0])  # 11 = cols: outside the classes, ignored too
+    loss_b, _ = RS.cross_entropy(x, t_big)
+    gx_b = RS.cross_entropy_backward(x, t_big, np.ones(4))
     errs = [np.max(np.abs(p.sum(-1) - 1)),
             np.max(np.abs(RS.softmax_backward(p, g).sum(-1))),
             np.max(np.abs(np.exp(RS.log_softmax(x)) - p)),
             np.max(np.abs(RS.softmax(x + 7.5) - p)),
             np.max(np.abs(RS.log_softmax(x - 3.0) - RS.log_softmax(x))),
             abs(loss[1]), np.max(np.abs(gx[1])),
+            np.max(np.abs(loss_b[1:3])), np.max(np.abs(gx_b[1:3])),
+            np.max(np.abs(loss_b[[0, 3]] - loss[[0, 3]])), np.max(np.abs(gx_b[[0, 3]] - gx[[0, 3]])),
             np.max(np.abs(loss[[0, 2, 3]] + np.log(p[[0, 2, 3], t[[0, 2, 3]]])))]
     return float(max(errs))
 
