@@ -49,6 +49,7 @@ CSRC = os.path.join(ROOT, "online_softmax_attn_amd", "csrc")
 FWD_SOURCES = [os.path.join(CSRC, f) for f in ("fwd_mfma.hip", "common.h")]
 BWD_SOURCES = [os.path.join(CSRC, f) for f in ("bwd_mfma.hip", "common.h")]
 F32_SOURCES = [os.path.join(CSRC, "f32_kernels.hip")]
+ROW_SOURCES = [os.path.join(CSRC, f) for f in ("rowsoftmax.hip", "common.h")]
 
 
 def kernel_source_sha(paths) -> str:
@@ -99,18 +100,44 @@ def _counter_means(folder: str, counter: str):
 
 
 def _pick(means, short):
-    hits = [v for n, v in means.items() if short in n]
+    keys = short if isinstance(short, (list, tuple)) else [short]
+    hits = [v for n, v in means.items() if any(k in n for k in keys)]
     if not hits:
         raise SystemExit(f"no dispatch of {short} in the counter output")
     return sum(hits) / len(hits)
 
 
-def write_traffic(folders, workload_name):
+# How a kernel's element type shows in a rocprofv3 name (mangled or demangled).
+_TYPE_TOKENS = {"bf16": ("IDF16b", "<__bf16"), "fp16": ("IDF16_", "<_Float16"),
+                "fp32": ("If", "<float")}
+
+
+def row_kernel_table(w):
+    """The forward and backward launch of a row workload, with the substrings that
+    pick their dispatches out of a counter run (kernel template and element type)."""
+    fb, bb = row_bytes(w)
+    if w.op == "xent":
+        bases = (("xent_fwd_kernel",), ("xent_bwd_kernel",))
+    else:
+        bases = (("rs_fwd_reg", "rs_fwd_stream"), ("rs_bwd_reg", "rs_bwd_stream"))
+    out = []
+    for base, nbytes in zip(bases, (fb, bb)):
+        out.append({"name": f"{'/'.join(base)}<{w.dtype}>", "bytes": nbytes, "sources": ROW_SOURCES,
+                    "match": [b + t for b in base for t in _TYPE_TOKENS[w.dtype]]})
+    return out
+
+
+def write_traffic(folders, workload_name, rows: bool = False):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each kernel of the step by
     what the same counters read for a plain copy of COPY_BYTES, and record the
-    result with the sha of each kernel's source."""
+    result with the sha of each kernel's source.  rows: the counter runs are of
+    `bench.py --rows` and every row workload is recorded."""
     import synthetic as S
-    w = S.WORKLOADS[workload_name] if workload_name else S.HEADLINE
+    if rows:
+        tables = [(w, row_kernel_table(w)) for w in S.ROWS.values()]
+    else:
+        w = S.WORKLOADS[workload_name] if workload_name else S.HEADLINE
+        tables = [(w, kernel_table(w))]
     fetch, write, cfetch, cwrite = folders
     fm, wm = _counter_means(fetch, "FETCH_SIZE"), _counter_means(write, "WRITE_SIZE")
     cf = _pick(_counter_means(cfetch, "FETCH_SIZE"), COPY_KERNEL)
@@ -123,8 +150,9 @@ def write_traffic(folders, workload_name):
                                 "WRITE_SIZE_KiB": cw, "fetch_scale": round(fetch_scale, 5),
                                 "write_scale": round(write_scale, 5)},
            "kernels": old.get("kernels", {})}
-    for kt in kernel_table(w):
-        f_kib, w_kib = _pick(fm, kt["name"]), _pick(wm, kt["name"])
+    for w, kt in ((w, kt) for w, table in tables for kt in table):
+        key = kt.get("match", kt["name"])
+        f_kib, w_kib = _pick(fm, key), _pick(wm, key)
         hbm = f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale
         ent = out["kernels"].get(kt["name"], {})
         sha = kernel_source_sha(kt["sources"])
@@ -187,6 +215,9 @@ def main():
                     help="time the split-KV forward on the decoding workloads (one line each)")
     ap.add_argument("--masked", action="store_true",
                     help="time the interval-masked fwd+bwd on the masked workloads (one line each)")
+    ap.add_argument("--rows", action="store_true",
+                    help="time row softmax / log-softmax / cross-entropy fwd+bwd on the row "
+                         "workloads (one line each)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 512 MiB device copies (for scaling HBM counters)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -195,7 +226,7 @@ def main():
     args = ap.parse_args()
 
     if args.traffic_from:
-        write_traffic(args.traffic_from, args.workload)
+        write_traffic(args.traffic_from, args.workload, rows=args.rows)
         return
 
     if args.gpus != 1:
@@ -233,6 +264,11 @@ def main():
     if args.masked:
         for name, (w, kind, mk) in S.MASKED.items():
             print(json.dumps(run_masked(name, w, kind, mk, args, osa, torch)), flush=True)
+        return
+    if args.rows:
+        for w in S.ROWS.values():
+            print(json.dumps(run_rows(w, args, osa, torch, with_cpu=not args.no_cpu_baseline)),
+                  flush=True)
         return
     w = S.WORKLOADS[args.workload] if args.workload else S.HEADLINE
     print(json.dumps(run_one(w, args, osa, torch, with_cpu=not args.no_cpu_baseline)), flush=True)
@@ -361,6 +397,106 @@ def run_masked(name, w, kind, mk, args, osa, torch):
                     "frac_peak": round(ff / (f_ms * 1e-3) / 1e12 / peak, 4)},
             "bwd": {"ms": round(b_ms, 4), "tflops": round(bf / (b_ms * 1e-3) / 1e12, 2),
                     "frac_peak": round(bf / (b_ms * 1e-3) / 1e12 / peak, 4)}}
+
+
+def row_bytes(w):
+    """Compulsory HBM bytes of the forward and the backward launch of a row workload:
+    every element read or written once (fp32 loss / lse / dloss, int32 targets)."""
+    el = w.rows * w.cols * w.elem_bytes()
+    if w.op == "xent":
+        return el + w.rows * (4 + 8), 2 * el + w.rows * 12
+    return 2 * el, 3 * el
+
+
+def row_cpu_baseline(w, inp, n_rows: int):
+    """Time the fp64 oracle's forward + backward on the first n_rows rows."""
+    import numpy as np
+
+    import oracle.rowsoftmax as R
+    x = inp["x"][:n_rows].double().numpy()
+    t0 = time.perf_counter()
+    if w.op == "xent":
+        t = inp["targets"][:n_rows].numpy().astype(np.int64)
+        R.cross_entropy(x, t)
+        R.cross_entropy_backward(x, t, inp["dloss"][:n_rows].numpy())
+    else:
+        log = w.op == "log_softmax"
+        y = R.log_softmax(x) if log else R.softmax(x)
+        dy = inp["dy"][:n_rows].double().numpy()
+        (R.log_softmax_backward if log else R.softmax_backward)(y, dy)
+    dt = time.perf_counter() - t0
+    fb, bb = row_bytes(w)
+    frac = n_rows / w.rows
+    return {"value": round((fb + bb) * frac / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd on the first {n_rows} of {w.rows} rows, {dt:.2f} s; "
+                      "bytes counted as for the GPU (dtype-sized elements)",
+            "seconds": round(dt, 3)}
+
+
+def run_rows(w, args, osa, torch, with_cpu: bool):
+    """One forward and one backward launch per step on a row workload; both are
+    HBM-bound, so the roofline is compulsory bytes over time."""
+    import synthetic as S
+
+    inp = S.row_inputs(w)
+    x = inp["x"].cuda()
+    if w.op == "xent":
+        t, dloss = inp["targets"].cuda(), inp["dloss"].cuda()
+        loss = torch.empty(w.rows, device="cuda", dtype=torch.float32)
+        lse = torch.empty_like(loss)
+        dx = torch.empty_like(x)
+        fwd = lambda: osa.rowxent_fwd(x, t, loss=loss, lse=lse)
+        bwd = lambda: osa.rowxent_bwd(x, t, lse, dloss, out=dx)
+        names = ("xent_fwd_kernel", "xent_bwd_kernel")
+    else:
+        log = w.op == "log_softmax"
+        dy = inp["dy"].cuda()
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        fwd = lambda: osa.rowsoftmax_fwd(x, log_softmax=log, out=y)
+        bwd = lambda: osa.rowsoftmax_bwd(y, dy, log_softmax=log, out=dx)
+        names = ("rs_fwd_reg / rs_fwd_stream", "rs_bwd_reg / rs_bwd_stream")
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps * 1e3
+    f_ms = stats([e[0].elapsed_time(e[1]) for e in ev])["mean"]
+    b_ms = stats([e[1].elapsed_time(e[2]) for e in ev])["mean"]
+    fb, bb = row_bytes(w)
+    gbs = (fb + bb) / ((f_ms + b_ms) * 1e-3) / 1e9
+    f_gbs, b_gbs = fb / (f_ms * 1e-3) / 1e9, bb / (b_ms * 1e-3) / 1e9
+    kt_f, kt_b = row_kernel_table(w)
+    dom = ((names[0], f_gbs, fb, f_ms, kt_f) if f_ms >= b_ms else
+           (names[1], b_gbs, bb, b_ms, kt_b))
+    line = {"metric": f"row {w.op} fwd+bwd: compulsory HBM bytes per second",
+            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(f_ms + b_ms, 4),
+            "wall_ms_per_step": round(wall, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": w.dtype, "data": "synthetic", "config": w.describe(),
+            "fwd": {"kernel": names[0], "ms": round(f_ms, 4), "bytes": fb, "gbs": round(f_gbs, 1),
+                    "frac": round(f_gbs / HBM_PEAK_GBS, 4)},
+            "bwd": {"kernel": names[1], "ms": round(b_ms, 4), "bytes": bb, "gbs": round(b_gbs, 1),
+                    "frac": round(b_gbs / HBM_PEAK_GBS, 4)},
+            "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[1], 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dom[1] / HBM_PEAK_GBS, 4), "bytes_per_launch": dom[2],
+                         "ms": round(dom[3], 4), "traffic": traffic_of(load_traffic(), dom[4],
+                                                                       w.name)}}
+    if with_cpu:
+        n = max(1, min(w.rows, int(4e7 // w.cols)))
+        line["cpu_baseline"] = row_cpu_baseline(w, inp, n)
+    return line
 
 
 def stats(xs):

@@ -197,6 +197,38 @@ int attn_bwd_masked(const void* q, const void* k, const void* v, const void* o,
                     const int* kv_lo, const int* kv_hi, int dtype, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/*
+ * Row softmax, log-softmax and cross-entropy with logits (softmax-backward page on
+ * shreyansh26.github.io): rows of `cols` elements, row-major and contiguous, in
+ * `dtype` (fp32 statistics inside).  x, y, dy, dx, logits, dlogits: [rows][cols];
+ * targets: int32 [rows]; loss, lse, dloss: float32 [rows].
+ *
+ * rowsoftmax_fwd: y = softmax(x) per row, or log-softmax x - logsumexp(x) when
+ *   log_softmax = 1.
+ * rowsoftmax_bwd: from the forward's output y and the upstream gradient dy,
+ *   softmax:     dx = y * (dy - rowsum(dy * y))   (the row Jacobian-vector product)
+ *   log-softmax: dx = dy - exp(y) * rowsum(dy)
+ * rowxent_fwd: per-row loss logsumexp(x) - x[target] and the row logsumexp (kept
+ *   for the backward); a row whose target is outside 0 .. cols-1 is ignored (loss 0).
+ * rowxent_bwd: dlogits = dloss[row] * (softmax(x) - onehot(target)), softmax rebuilt
+ *   from the saved logsumexp; zero for ignored rows.  A mean over the batch is
+ *   dloss = 1/rows.
+ *
+ * Arrays of elements must be 16-byte aligned, int32/float32 row arrays 4-byte
+ * aligned.  Returns ATTN_OK or ATTN_ERR_NULL / _SHAPE (rows or cols < 1, rows >=
+ * 2^31, log_softmax not 0/1) / _DTYPE / _ALIGN / _LAUNCH; nothing is launched on a
+ * validation error.  Only enqueues on `stream`.
+ */
+int rowsoftmax_fwd(const void* x, void* y, long long rows, int cols, int log_softmax,
+                   int dtype, void* stream);
+int rowsoftmax_bwd(const void* y, const void* dy, void* dx, long long rows, int cols,
+                   int log_softmax, int dtype, void* stream);
+int rowxent_fwd(const void* logits, const int* targets, float* loss, float* lse,
+                long long rows, int cols, int dtype, void* stream);
+int rowxent_bwd(const void* logits, const int* targets, const float* lse,
+                const float* dloss, void* dlogits, long long rows, int cols, int dtype,
+                void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* attn_status_string(int status);
 

@@ -9,6 +9,13 @@ exception is raised.
     o, lse = attn_fwd(q, k, v, causal=False)          # q [B,H,N,d], k/v [B,Hkv,N,d]
     dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=False)
 
+Row softmax, log-softmax and cross-entropy with logits over the last dimension:
+
+    y = rowsoftmax_fwd(x, log_softmax=False)          # any shape, rows = numel / cols
+    dx = rowsoftmax_bwd(y, dy, log_softmax=False)
+    loss, lse = rowxent_fwd(logits, targets)          # logits [..., C], targets int32
+    dlogits = rowxent_bwd(logits, targets, lse, dloss)
+
 The backward's three kernels can also be enqueued one at a time with
 ``attn_bwd_preprocess``, ``attn_bwd_dkdv`` and ``attn_bwd_dq`` on a shared
 workspace (``new_bwd_workspace``).
@@ -38,6 +45,10 @@ __all__ = [
     "attn_fwd_masked",
     "attn_bwd_masked",
     "attn_bwd_masked_workspace_bytes",
+    "rowsoftmax_fwd",
+    "rowsoftmax_bwd",
+    "rowxent_fwd",
+    "rowxent_bwd",
     "status_string",
     "library",
     "library_path",
@@ -66,6 +77,7 @@ DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
             "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
             "attn_fwd_masked", "attn_bwd_masked", "attn_bwd_masked_workspace_bytes",
+            "rowsoftmax_fwd", "rowsoftmax_bwd", "rowxent_fwd", "rowxent_bwd",
             "attn_status_string")
 
 _lib = None
@@ -115,6 +127,15 @@ def library() -> ctypes.CDLL:
     lib.attn_fwd_splitkv_workspace_bytes.restype = sz
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    ll = ctypes.c_longlong
+    lib.rowsoftmax_fwd.argtypes = [vp, vp, ll, i, i, i, vp]
+    lib.rowsoftmax_fwd.restype = i
+    lib.rowsoftmax_bwd.argtypes = [vp, vp, vp, ll, i, i, i, vp]
+    lib.rowsoftmax_bwd.restype = i
+    lib.rowxent_fwd.argtypes = [vp, vp, vp, vp, ll, i, i, vp]
+    lib.rowxent_fwd.restype = i
+    lib.rowxent_bwd.argtypes = [vp, vp, vp, vp, vp, ll, i, i, vp]
+    lib.rowxent_bwd.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -401,3 +422,103 @@ def attn_bwd_masked(q, k, v, o, lse, do, kv_lo, kv_hi, scale: float | None = Non
     if st != 0:
         raise AttnError(st, "attn_bwd_masked")
     return dq, dk, dv
+
+
+def _rows_of(x):
+    if x.dim() < 1 or x.shape[-1] < 1 or x.numel() == 0:
+        raise ValueError("need at least one row of at least one element")
+    cols = x.shape[-1]
+    return x.numel() // cols, cols
+
+
+def rowsoftmax_fwd(x, log_softmax: bool = False, out=None):
+    """Softmax (or log-softmax) of every row of x over its last dimension."""
+    lib = library()
+    _check_dev("x", x)
+    if x.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    rows, cols = _rows_of(x)
+    out = torch.empty_like(x) if out is None else out
+    _check_dev("out", out, x.dtype)
+    if out.shape != x.shape:
+        raise ValueError("out has the wrong shape")
+    st = lib.rowsoftmax_fwd(x.data_ptr(), out.data_ptr(), rows, cols, int(bool(log_softmax)),
+                            DTYPE_CODES[x.dtype], _stream_handle(x.device))
+    if st != 0:
+        raise AttnError(st, "rowsoftmax_fwd")
+    return out
+
+
+def rowsoftmax_bwd(y, dy, log_softmax: bool = False, out=None):
+    """Gradient with respect to the rows' input, from the forward's output y and dy."""
+    lib = library()
+    _check_dev("y", y)
+    _check_dev("dy", dy, y.dtype)
+    if y.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {y.dtype}")
+    if dy.shape != y.shape:
+        raise ValueError("dy must have y's shape")
+    rows, cols = _rows_of(y)
+    out = torch.empty_like(y) if out is None else out
+    _check_dev("out", out, y.dtype)
+    if out.shape != y.shape:
+        raise ValueError("out has the wrong shape")
+    st = lib.rowsoftmax_bwd(y.data_ptr(), dy.data_ptr(), out.data_ptr(), rows, cols,
+                            int(bool(log_softmax)), DTYPE_CODES[y.dtype],
+                            _stream_handle(y.device))
+    if st != 0:
+        raise AttnError(st, "rowsoftmax_bwd")
+    return out
+
+
+def _check_targets(targets, rows):
+    _check_dev("targets", targets, torch.int32)
+    if targets.numel() != rows:
+        raise ValueError(f"targets must hold one int32 per row ({rows}), got {targets.numel()}")
+
+
+def rowxent_fwd(logits, targets, loss=None, lse=None):
+    """Per-row cross-entropy logsumexp(x) - x[target] (0 where the target is outside
+    0 .. C-1) and the row logsumexp, both float32 with the rows' shape."""
+    lib = library()
+    _check_dev("logits", logits)
+    if logits.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {logits.dtype}")
+    rows, cols = _rows_of(logits)
+    _check_targets(targets, rows)
+    shape = logits.shape[:-1]
+    loss = torch.empty(shape, device=logits.device, dtype=torch.float32) if loss is None else loss
+    lse = torch.empty(shape, device=logits.device, dtype=torch.float32) if lse is None else lse
+    for name, t in (("loss", loss), ("lse", lse)):
+        _check_dev(name, t, torch.float32)
+        if t.numel() != rows:
+            raise ValueError(f"{name} must hold one float32 per row")
+    st = lib.rowxent_fwd(logits.data_ptr(), targets.data_ptr(), loss.data_ptr(), lse.data_ptr(),
+                         rows, cols, DTYPE_CODES[logits.dtype], _stream_handle(logits.device))
+    if st != 0:
+        raise AttnError(st, "rowxent_fwd")
+    return loss, lse
+
+
+def rowxent_bwd(logits, targets, lse, dloss, out=None):
+    """dlogits = dloss[row] * (softmax(logits) - onehot(target)); zero for ignored rows."""
+    lib = library()
+    _check_dev("logits", logits)
+    if logits.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {logits.dtype}")
+    rows, cols = _rows_of(logits)
+    _check_targets(targets, rows)
+    for name, t in (("lse", lse), ("dloss", dloss)):
+        _check_dev(name, t, torch.float32)
+        if t.numel() != rows:
+            raise ValueError(f"{name} must hold one float32 per row")
+    out = torch.empty_like(logits) if out is None else out
+    _check_dev("out", out, logits.dtype)
+    if out.shape != logits.shape:
+        raise ValueError("out has the wrong shape")
+    st = lib.rowxent_bwd(logits.data_ptr(), targets.data_ptr(), lse.data_ptr(), dloss.data_ptr(),
+                         out.data_ptr(), rows, cols, DTYPE_CODES[logits.dtype],
+                         _stream_handle(logits.device))
+    if st != 0:
+        raise AttnError(st, "rowxent_bwd")
+    return out

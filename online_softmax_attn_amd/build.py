@@ -17,7 +17,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libosattn.so")
-SOURCES = ["api.hip", "fwd_mfma.hip", "bwd_mfma.hip", "f32_kernels.hip", "splitkv.hip"]
+SOURCES = ["api.hip", "fwd_mfma.hip", "bwd_mfma.hip", "f32_kernels.hip", "splitkv.hip",
+           "rowsoftmax.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -311,11 +311,100 @@ int attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, 
   return run_bwd_kernels(a);
 }
 
+namespace {
+
+int validate_rows(long long rows, int cols, int dtype) {
+  if (rows < 1 || cols < 1 || rows >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  return ATTN_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+
+}  // namespace
+
+int rowsoftmax_fwd(const void* x, void* y, long long rows, int cols, int log_softmax, int dtype,
+                   void* stream) {
+  if (!x || !y) return ATTN_ERR_NULL;
+  const int st = validate_rows(rows, cols, dtype);
+  if (st != ATTN_OK) return st;
+  if (log_softmax != 0 && log_softmax != 1) return ATTN_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(y)) return ATTN_ERR_ALIGN;
+  osattn::RowArgs a;
+  a.x = x;
+  a.y = y;
+  a.rows = rows;
+  a.cols = cols;
+  a.log = log_softmax;
+  a.dtype = dtype;
+  a.stream = stream;
+  return launched(osattn::launch_rowsoftmax(a, false));
+}
+
+int rowsoftmax_bwd(const void* y, const void* dy, void* dx, long long rows, int cols,
+                   int log_softmax, int dtype, void* stream) {
+  if (!y || !dy || !dx) return ATTN_ERR_NULL;
+  const int st = validate_rows(rows, cols, dtype);
+  if (st != ATTN_OK) return st;
+  if (log_softmax != 0 && log_softmax != 1) return ATTN_ERR_SHAPE;
+  if (!aligned16(y) || !aligned16(dy) || !aligned16(dx)) return ATTN_ERR_ALIGN;
+  osattn::RowArgs a;
+  a.y = (void*)y;
+  a.dy = dy;
+  a.dx = dx;
+  a.rows = rows;
+  a.cols = cols;
+  a.log = log_softmax;
+  a.dtype = dtype;
+  a.stream = stream;
+  return launched(osattn::launch_rowsoftmax(a, true));
+}
+
+int rowxent_fwd(const void* logits, const int* targets, float* loss, float* lse, long long rows,
+                int cols, int dtype, void* stream) {
+  if (!logits || !targets || !loss || !lse) return ATTN_ERR_NULL;
+  const int st = validate_rows(rows, cols, dtype);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(logits) || !aligned4(targets) || !aligned4(loss) || !aligned4(lse))
+    return ATTN_ERR_ALIGN;
+  osattn::RowArgs a;
+  a.x = logits;
+  a.targets = targets;
+  a.loss = loss;
+  a.lse_out = lse;
+  a.rows = rows;
+  a.cols = cols;
+  a.dtype = dtype;
+  a.stream = stream;
+  return launched(osattn::launch_rowxent(a, false));
+}
+
+int rowxent_bwd(const void* logits, const int* targets, const float* lse, const float* dloss,
+                void* dlogits, long long rows, int cols, int dtype, void* stream) {
+  if (!logits || !targets || !lse || !dloss || !dlogits) return ATTN_ERR_NULL;
+  const int st = validate_rows(rows, cols, dtype);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(logits) || !aligned16(dlogits) || !aligned4(targets) || !aligned4(lse) ||
+      !aligned4(dloss))
+    return ATTN_ERR_ALIGN;
+  osattn::RowArgs a;
+  a.x = logits;
+  a.targets = targets;
+  a.lse = lse;
+  a.dloss = dloss;
+  a.dx = dlogits;
+  a.rows = rows;
+  a.cols = cols;
+  a.dtype = dtype;
+  a.stream = stream;
+  return launched(osattn::launch_rowxent(a, true));
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "null pointer argument";
-    case ATTN_ERR_SHAPE: return "invalid shape (B, H, Hkv, N must be >= 1 and fit 32-bit row indices; causal must be 0 or 1)";
+    case ATTN_ERR_SHAPE: return "invalid shape (sizes must be >= 1 and fit 32-bit row indices; flags must be 0 or 1)";
     case ATTN_ERR_HEAD_DIM: return "unsupported head dimension (d must be 64 or 128)";
     case ATTN_ERR_GQA: return "H is not a multiple of Hkv";
     case ATTN_ERR_DTYPE: return "unsupported dtype";

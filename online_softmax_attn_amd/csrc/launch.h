@@ -90,4 +90,24 @@ hipError_t launch_bwd_mfma(const BwdArgs& a);
 hipError_t launch_bwd_f32(const BwdArgs& a);
 hipError_t launch_splitkv(const SplitArgs& a);
 
+// Row softmax / log-softmax / cross-entropy (rows of `cols` elements, row-major).
+struct RowArgs {
+  const void* x = nullptr;    // forward input (softmax) or logits (cross-entropy)
+  void* y = nullptr;          // softmax / log-softmax output
+  const void* dy = nullptr;   // upstream gradient of y
+  void* dx = nullptr;         // gradient of the input
+  const int* targets = nullptr;
+  float* loss = nullptr;
+  float* lse_out = nullptr;   // cross-entropy forward: row logsumexp
+  const float* lse = nullptr; // cross-entropy backward: the saved row logsumexp
+  const float* dloss = nullptr;
+  long long rows = 0;
+  int cols = 0;
+  int log = 0;                // 1: log-softmax
+  int dtype = 0;
+  void* stream = nullptr;
+};
+hipError_t launch_rowsoftmax(const RowArgs& a, bool backward);
+hipError_t launch_rowxent(const RowArgs& a, bool backward);
+
 }  // namespace osattn

@@ -7,7 +7,8 @@ oracle upcasts the same rounded values to float64).
 
 Seeds: tensor t of workload k uses seed 1000*k + t with t = 0 (Q), 1 (K), 2 (V),
 3 (dO).  Point p of the throughput sweep uses 5000 + 10*p + t; the decoding
-workloads (fewer queries than keys) use 6000, 6100 and 6200 + t.  The GQA workload
+workloads (fewer queries than keys) use 6000, 6100 and 6200 + t, the masked ones 7000
+and 7100 + t, the row workloads 8000, 8100 and 8200 + t.  The GQA workload
 additionally scales ceil(1%) of all key rows by 8 (exact in bf16), rows picked by
 a seed-4100 permutation over the flattened (batch, kv-head, position) rows, before
 the dtype cast: those rows produce scores far above the rest and move the running
@@ -232,6 +233,65 @@ MASKED = {
     "documents_bf16": (custom("bf16", 4, 16, 16, 8192, 128, False, seed_base=7100), "document",
                        {"doc_lens": [[3000, 2000, 3192], [8192], [1, 4095, 4096], [100] * 81 + [92]],
                         "causal": True}),
+}
+
+
+# ---- row softmax / log-softmax / cross-entropy workloads ------------------------------
+@dataclass(frozen=True)
+class RowWorkload:
+    """Rows of `cols` logits.  op is "softmax", "log_softmax" or "xent"."""
+    name: str
+    op: str
+    dtype: str
+    rows: int
+    cols: int
+    seed: int
+    std: float = 1.0          # logits are std * N(0, 1)
+    ignore_frac: float = 0.0  # xent: fraction of rows whose target is -100 (ignored)
+
+    def elem_bytes(self) -> int:
+        return DTYPES[self.dtype].itemsize
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "op": self.op, "rows": self.rows, "cols": self.cols,
+                "dtype": self.dtype, "logit_std": self.std, "ignored_fraction": self.ignore_frac}
+
+
+IGNORE_TARGET = -100
+
+
+def row_inputs(w: RowWorkload, backward: bool = True) -> dict:
+    """CPU tensors: x [rows, cols] in the dtype; softmax ops add dy (N(0, 1), seed + 1);
+    xent adds int32 targets uniform over the classes (seed + 2), a seeded fraction of
+    them set to -100 (seed + 3), and dloss = 1 / (rows not ignored) on every row, the
+    gradient of the mean loss."""
+    dt = DTYPES[w.dtype]
+    out = {"x": (randn((w.rows, w.cols), w.seed) * w.std).to(dt).contiguous()}
+    if w.op == "xent":
+        g = torch.Generator(device="cpu").manual_seed(w.seed + 2)
+        t = torch.randint(0, w.cols, (w.rows,), generator=g)
+        if w.ignore_frac > 0:
+            g3 = torch.Generator(device="cpu").manual_seed(w.seed + 3)
+            t = torch.where(torch.rand((w.rows,), generator=g3) < w.ignore_frac,
+                            torch.full_like(t, IGNORE_TARGET), t)
+        out["targets"] = t.to(torch.int32).contiguous()
+        live = int((out["targets"] >= 0).sum())
+        out["dloss"] = torch.full((w.rows,), 1.0 / max(1, live), dtype=torch.float32)
+    elif backward:
+        out["dy"] = randn((w.rows, w.cols), w.seed + 1).to(dt).contiguous()
+    return out
+
+
+# Row workloads: cross-entropy over a 128256-class vocabulary for 8192 tokens (an LM
+# head's logits), softmax over 65536 rows of 8192 attention scores (8 heads' full
+# score matrices at N = 8192), and fp32 log-softmax over a 32000-class vocabulary.
+ROWS = {
+    "xent_bf16_T8192_V128256": RowWorkload("xent_bf16_T8192_V128256", "xent", "bf16", 8192,
+                                           128256, 8000, std=2.0, ignore_frac=0.02),
+    "softmax_bf16_R65536_C8192": RowWorkload("softmax_bf16_R65536_C8192", "softmax", "bf16",
+                                             65536, 8192, 8100),
+    "log_softmax_fp32_R8192_C32000": RowWorkload("log_softmax_fp32_R8192_C32000", "log_softmax",
+                                                 "fp32", 8192, 32000, 8200, std=2.0),
 }
 
 

@@ -24,7 +24,8 @@ S = osa.STATUS
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\**(attn_[a-z_]+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\**((?:attn|rowsoftmax|rowxent)_[a-z_]+)\s*\(",
+                                 text, flags=re.M)))
 
 
 def header_enum(name_prefix):
@@ -298,3 +299,80 @@ def test_masked_bwd_workspace_bytes():
     assert f(2, 4, 2, 100, 300, 128, 2) == 2 * r256(2 * 4 * 100 * 4) + r256(2 * 2 * 16)
     assert f(1, 1, 1, 1, 1, 64, 0) == 2 * 256 + 256
     assert f(1, 4, 2, 100, 0, 128, 2) == 0
+
+
+# ---- row softmax / log-softmax / cross-entropy --------------------------------------
+def row_call(fn, **kw):
+    lib = osa.library()
+    a = dict(x=P, y=P, dy=P, dx=P, t=P, loss=P, lse=P, dloss=P, rows=4, cols=64, log=0, dtype=2,
+             stream=None)
+    a.update(kw)
+    if fn == "rowsoftmax_fwd":
+        return lib.rowsoftmax_fwd(a["x"], a["y"], a["rows"], a["cols"], a["log"], a["dtype"],
+                                  a["stream"])
+    if fn == "rowsoftmax_bwd":
+        return lib.rowsoftmax_bwd(a["y"], a["dy"], a["dx"], a["rows"], a["cols"], a["log"],
+                                  a["dtype"], a["stream"])
+    if fn == "rowxent_fwd":
+        return lib.rowxent_fwd(a["x"], a["t"], a["loss"], a["lse"], a["rows"], a["cols"],
+                               a["dtype"], a["stream"])
+    return lib.rowxent_bwd(a["x"], a["t"], a["lse"], a["dloss"], a["dx"], a["rows"], a["cols"],
+                           a["dtype"], a["stream"])
+
+
+ROW_FNS = ("rowsoftmax_fwd", "rowsoftmax_bwd", "rowxent_fwd", "rowxent_bwd")
+ROW_INVALID = [
+    ({"rows": 0}, "ATTN_ERR_SHAPE"),
+    ({"rows": -1}, "ATTN_ERR_SHAPE"),
+    ({"rows": 1 << 31}, "ATTN_ERR_SHAPE"),
+    ({"cols": 0}, "ATTN_ERR_SHAPE"),
+    ({"cols": -3}, "ATTN_ERR_SHAPE"),
+    ({"dtype": 3}, "ATTN_ERR_DTYPE"),
+    ({"dtype": -1}, "ATTN_ERR_DTYPE"),
+]
+ROW_NULLS = {
+    "rowsoftmax_fwd": ("x", "y"),
+    "rowsoftmax_bwd": ("y", "dy", "dx"),
+    "rowxent_fwd": ("x", "t", "loss", "lse"),
+    "rowxent_bwd": ("x", "t", "lse", "dloss", "dx"),
+}
+ROW_ALIGN = {
+    "rowsoftmax_fwd": {"x": P + 8, "y": P + 2},
+    "rowsoftmax_bwd": {"y": P + 4, "dy": P + 8, "dx": P + 2},
+    "rowxent_fwd": {"x": P + 8, "t": P + 2, "loss": P + 1, "lse": P + 3},
+    "rowxent_bwd": {"x": P + 8, "dx": P + 4, "t": P + 2, "lse": P + 1, "dloss": P + 3},
+}
+
+
+@pytest.mark.parametrize("fn", ROW_FNS)
+@pytest.mark.parametrize("kw,code", ROW_INVALID)
+def test_row_rejects_sizes(fn, kw, code):
+    assert row_call(fn, **kw) == S[code]
+
+
+@pytest.mark.parametrize("fn", ROW_FNS)
+def test_row_rejects_null_and_misalignment(fn):
+    for name in ROW_NULLS[fn]:
+        assert row_call(fn, **{name: None}) == S["ATTN_ERR_NULL"], name
+    for name, addr in ROW_ALIGN[fn].items():
+        assert row_call(fn, **{name: addr}) == S["ATTN_ERR_ALIGN"], name
+
+
+@pytest.mark.parametrize("fn", ("rowsoftmax_fwd", "rowsoftmax_bwd"))
+def test_row_rejects_bad_log_flag(fn):
+    assert row_call(fn, log=2) == S["ATTN_ERR_SHAPE"]
+    assert row_call(fn, log=-1) == S["ATTN_ERR_SHAPE"]
+
+
+def test_row_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 8)
+    t = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        osa.rowsoftmax_fwd(x)
+    with pytest.raises(ValueError):
+        osa.rowsoftmax_bwd(x, x)
+    with pytest.raises(ValueError):
+        osa.rowxent_fwd(x, t)
+    with pytest.raises(ValueError):
+        osa.rowxent_bwd(x, t, t.float(), t.float())
