@@ -117,7 +117,7 @@ def row_kernel_table(w):
     pick their dispatches out of a counter run (kernel template and element type)."""
     fb, bb = row_bytes(w)
     if w.op == "xent":
-        bases = (("xent_fwd_kernel",), ("xent_bwd_kernel",))
+        bases = (("xent_fwd_kernel",), ("xent_bwd_flat", "xent_bwd_kernel"))
     else:
         bases = (("rs_fwd_reg", "rs_fwd_stream"), ("rs_bwd_reg", "rs_bwd_stream"))
     out = []
@@ -448,7 +448,7 @@ def run_rows(w, args, osa, torch, with_cpu: bool):
         dx = torch.empty_like(x)
         fwd = lambda: osa.rowxent_fwd(x, t, loss=loss, lse=lse)
         bwd = lambda: osa.rowxent_bwd(x, t, lse, dloss, out=dx)
-        names = ("xent_fwd_kernel", "xent_bwd_kernel")
+        names = ("xent_fwd_kernel", "xent_bwd_flat / xent_bwd_kernel")
     else:
         log = w.op == "log_softmax"
         dy = inp["dy"].cuda()

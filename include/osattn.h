@@ -216,7 +216,7 @@ int attn_bwd_masked(const void* q, const void* k, const void* v, const void* o,
  *
  * Arrays of elements must be 16-byte aligned, int32/float32 row arrays 4-byte
  * aligned.  Returns ATTN_OK or ATTN_ERR_NULL / _SHAPE (rows or cols < 1, rows >=
- * 2^31, log_softmax not 0/1) / _DTYPE / _ALIGN / _LAUNCH; nothing is launched on a
+ * 2^31, cols > 2^30, log_softmax not 0/1) / _DTYPE / _ALIGN / _LAUNCH; nothing is launched on a
  * validation error.  Only enqueues on `stream`.
  */
 int rowsoftmax_fwd(const void* x, void* y, long long rows, int cols, int log_softmax,

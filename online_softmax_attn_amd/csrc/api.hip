@@ -314,7 +314,8 @@ int attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, 
 namespace {
 
 int validate_rows(long long rows, int cols, int dtype) {
-  if (rows < 1 || cols < 1 || rows >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  // Element indices inside a row are 32-bit with headroom for a few strides.
+  if (rows < 1 || cols < 1 || rows >= (1LL << 31) || cols > (1 << 30)) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   return ATTN_OK;
 }

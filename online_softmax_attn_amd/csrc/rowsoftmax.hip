@@ -58,14 +58,15 @@ template <> struct Elem<__bf16> : Elem16<__bf16> {};
 template <> struct Elem<_Float16> : Elem16<_Float16> {};
 
 // ---- reductions over the TPR threads of one row ------------------------------------
-// TPR = 64: the row is one wave; otherwise the row is the whole workgroup and the
-// per-wave results meet in LDS (`sh` has one slot per wave).
+// TPR = 64: the row is one wave; otherwise the row is TPR / 64 waves of the workgroup
+// whose per-wave results meet in LDS (`sh` points at the row's TPR / 64 slots).  The
+// barriers are workgroup-wide, so every row of a workgroup must take them together.
 template <int TPR>
 __device__ __forceinline__ float row_max(float v, float* sh) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   if constexpr (TPR > 64) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = (threadIdx.x % TPR) >> 6;
     if ((threadIdx.x & 63) == 0) sh[wave] = v;
     __syncthreads();
     v = sh[0];
@@ -80,7 +81,7 @@ __device__ __forceinline__ float row_sum(float v, float* sh) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
   if constexpr (TPR > 64) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = (threadIdx.x % TPR) >> 6;
     if ((threadIdx.x & 63) == 0) sh[wave] = v;
     __syncthreads();
     v = 0.f;
@@ -112,8 +113,9 @@ __device__ __forceinline__ void online_add(float& m, float& s, float v) {
 }
 
 // ---- register kernels: softmax / log-softmax forward -------------------------------
-// Block = max(TPR, 256) threads holding 256 / TPR rows (TPR = 64) or one row.
-// Row r's chunk c of thread i is elements (c * TPR + i) * V .. + V - 1.
+// Block = max(TPR, 256) threads holding 256 / TPR rows (TPR < 256) or one row.
+// Row r's chunk c of thread i is elements (c * TPR + i) * V .. + V - 1.  A row past
+// the end (last workgroup) has no elements but still takes the barriers.
 template <typename E, int TPR, int CPT, bool LOG>
 __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void rs_fwd_reg(const E* __restrict__ X,
                                                                     E* __restrict__ Y,
@@ -121,10 +123,13 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void rs_fwd_reg(const E* __r
   using L = Elem<E>;
   constexpr int V = L::kV;
   constexpr int kRowsPerBlock = TPR >= 256 ? 1 : 256 / TPR;
-  __shared__ float sh[TPR / 64 > 0 ? TPR / 64 : 1];
+  constexpr int kWaves = (TPR > 256 ? TPR : 256) / 64;
+  __shared__ float sh_all[kWaves];
+  float* sh = sh_all + (threadIdx.x / TPR) * (TPR / 64);
   const int t = threadIdx.x % TPR;
   const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / TPR;
-  if (row >= rows) return;  // whole waves (TPR = 64) or whole blocks leave together
+  if (TPR == 64 && row >= rows) return;  // one-wave rows take no barrier
+  const int cols_r = row < rows ? cols : 0;
   const E* x = X + row * cols;
   E* y = Y + row * cols;
   u32x4 buf[CPT];
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void rs_fwd_reg(const E* __r
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int idx = (c * TPR + t) * V;
-    if (idx < cols) {
+    if (idx < cols_r) {
       buf[c] = *(const u32x4*)(x + idx);
 #pragma unroll
       for (int j = 0; j < V; ++j) m = fmaxf(m, L::get(buf[c], j));
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void rs_fwd_reg(const E* __r
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < CPT; ++c)
-    if ((c * TPR + t) * V < cols)
+    if ((c * TPR + t) * V < cols_r)
 #pragma unroll
       for (int j = 0; j < V; ++j) s += fast_exp2(fmaf(L::get(buf[c], j), kLog2e, -mb));
   s = row_sum<TPR>(s, sh);
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void rs_fwd_reg(const E* __r
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int idx = (c * TPR + t) * V;
-    if (idx < cols) {
+    if (idx < cols_r) {
       float o[V];
 #pragma unroll
       for (int j = 0; j < V; ++j) {
@@ -175,10 +180,13 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void rs_bwd_reg(const E* __r
   using L = Elem<E>;
   constexpr int V = L::kV;
   constexpr int kRowsPerBlock = TPR >= 256 ? 1 : 256 / TPR;
-  __shared__ float sh[TPR / 64 > 0 ? TPR / 64 : 1];
+  constexpr int kWaves = (TPR > 256 ? TPR : 256) / 64;
+  __shared__ float sh_all[kWaves];
+  float* sh = sh_all + (threadIdx.x / TPR) * (TPR / 64);
   const int t = threadIdx.x % TPR;
   const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / TPR;
-  if (row >= rows) return;
+  if (TPR == 64 && row >= rows) return;
+  const int cols_r = row < rows ? cols : 0;
   const E* y = Yv + row * cols;
   const E* dy = dY + row * cols;
   E* dx = dX + row * cols;
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void rs_bwd_reg(const E* __r
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int idx = (c * TPR + t) * V;
-    if (idx < cols) {
+    if (idx < cols_r) {
       by[c] = *(const u32x4*)(y + idx);
       bg[c] = *(const u32x4*)(dy + idx);
 #pragma unroll
@@ -199,7 +207,7 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void rs_bwd_reg(const E* __r
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int idx = (c * TPR + t) * V;
-    if (idx < cols) {
+    if (idx < cols_r) {
       float o[V];
 #pragma unroll
       for (int j = 0; j < V; ++j) {
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(T) void xent_fwd_kernel(const E* __restrict__ X,
   const E* x = X + row * cols;
   float m = -INFINITY, s = 0.f;
   if constexpr (VEC) {
-    // Chunk maxima first, then one rescale per chunk: fewer exponentials per element.
+    // The chunk's max first, then one rescale per chunk: fewer exponentials per element.
     for (int idx = threadIdx.x * V; idx < cols; idx += T * V) {
       const u32x4 c = *(const u32x4*)(x + idx);
       float cm = L::get(c, 0);
@@ -293,14 +301,44 @@ __global__ __launch_bounds__(T) void xent_fwd_kernel(const E* __restrict__ X,
 }
 
 // Backward: dx_j = dloss * (exp(x_j - lse) - [j == t]); zero for an ignored row.
-template <typename E, int T, bool VEC>
+// Once the row's lse, target and dloss are known the gradient is elementwise, so for
+// rows of whole 16-byte chunks the launch is flat over the chunks of all its rows, one
+// chunk per thread in address order (no loop: measured faster than a workgroup
+// walking its row); `cpr` is chunks per row.
+template <typename E>
+__global__ __launch_bounds__(256) void xent_bwd_flat(const E* __restrict__ X,
+                                                     const int* __restrict__ tgt,
+                                                     const float* __restrict__ lse,
+                                                     const float* __restrict__ dloss,
+                                                     E* __restrict__ dX, unsigned n_chunks,
+                                                     unsigned cpr) {
+  using L = Elem<E>;
+  constexpr int V = L::kV;
+  const unsigned ci = blockIdx.x * 256u + threadIdx.x;
+  if (ci >= n_chunks) return;
+  const unsigned row = ci / cpr;
+  const int j0 = (int)(ci - row * cpr) * V;
+  const int cols = (int)cpr * V;
+  const int t = tgt[row];
+  const bool live = t >= 0 && t < cols;
+  const float g = live ? dloss[row] : 0.f;
+  const float lb = lse[row] * kLog2e;
+  const u32x4 c = ((const u32x4*)X)[ci];
+  float o[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+    o[j] = g * (fast_exp2(fmaf(L::get(c, j), kLog2e, -lb)) - (j0 + j == t ? 1.f : 0.f));
+  ((u32x4*)dX)[ci] = L::pack(o);
+}
+
+// Rows of any length: a workgroup per row, one element per thread and step.
+template <typename E, int T>
 __global__ __launch_bounds__(T) void xent_bwd_kernel(const E* __restrict__ X,
                                                      const int* __restrict__ tgt,
                                                      const float* __restrict__ lse,
                                                      const float* __restrict__ dloss,
                                                      E* __restrict__ dX, int cols) {
   using L = Elem<E>;
-  constexpr int V = L::kV;
   const long long row = blockIdx.x;
   const E* x = X + row * cols;
   E* dx = dX + row * cols;
@@ -308,19 +346,8 @@ __global__ __launch_bounds__(T) void xent_bwd_kernel(const E* __restrict__ X,
   const bool live = t >= 0 && t < cols;
   const float g = live ? dloss[row] : 0.f;
   const float lb = lse[row] * kLog2e;
-  if constexpr (VEC) {
-    for (int idx = threadIdx.x * V; idx < cols; idx += T * V) {
-      const u32x4 c = *(const u32x4*)(x + idx);
-      float o[V];
-#pragma unroll
-      for (int j = 0; j < V; ++j)
-        o[j] = g * (fast_exp2(fmaf(L::get(c, j), kLog2e, -lb)) - (idx + j == t ? 1.f : 0.f));
-      *(u32x4*)(dx + idx) = L::pack(o);
-    }
-  } else {
-    for (int j = threadIdx.x; j < cols; j += T)
-      L::store1(dx + j, g * (fast_exp2(fmaf(L::load1(x + j), kLog2e, -lb)) - (j == t ? 1.f : 0.f)));
-  }
+  for (int j = threadIdx.x; j < cols; j += T)
+    L::store1(dx + j, g * (fast_exp2(fmaf(L::load1(x + j), kLog2e, -lb)) - (j == t ? 1.f : 0.f)));
 }
 
 // ---- dispatch -----------------------------------------------------------------------
@@ -349,17 +376,24 @@ bool row_aligned(int cols) {
 }
 
 // Register-kernel shape for a row of `chunks` 16-byte chunks: threads per row and
-// chunks per thread (a power of two); false if the row is too long to hold.  The
-// backward holds two rows (y and dy), so it stops at 8 chunks per thread: 16 would
-// not fit the 128 registers a lane has with 1024 threads per workgroup.
+// chunks per thread; false if the row is too long to hold.  Measured on the MI355X
+// over rows of 64 .. 8192 chunks: the forward is fastest with two chunks per thread
+// (more threads per row and one chunk each, or fewer threads and more chunks, lost
+// up to 20%), the backward with one chunk of y and dy per thread, both up to 1024
+// threads per row.  The backward holds two rows (y and dy), so it stops at 8 chunks
+// per thread: 16 would not fit the 128 registers a lane has at 1024 threads.
 bool reg_shape(long long chunks, bool backward, int& tpr, int& cpt) {
-  const int opts_tpr[] = {64, 64, 64, 256, 256, 1024, 1024, 1024};
-  const int opts_cpt[] = {1, 2, 4, 2, 4, 4, 8, 16};
-  const int n_opts = backward ? 7 : 8;
-  for (int i = 0; i < n_opts; ++i)
-    if (chunks <= (long long)opts_tpr[i] * opts_cpt[i]) {
-      tpr = opts_tpr[i];
-      cpt = opts_cpt[i];
+  static const int fwd_tpr[] = {64, 64, 128, 256, 512, 1024, 1024, 1024, 1024};
+  static const int fwd_cpt[] = {1, 2, 2, 2, 2, 2, 4, 8, 16};
+  static const int bwd_tpr[] = {64, 128, 256, 512, 1024, 1024, 1024, 1024};
+  static const int bwd_cpt[] = {1, 1, 1, 1, 1, 2, 4, 8};
+  const int* tp = backward ? bwd_tpr : fwd_tpr;
+  const int* cp = backward ? bwd_cpt : fwd_cpt;
+  const int n = backward ? 8 : 9;
+  for (int i = 0; i < n; ++i)
+    if (chunks <= (long long)tp[i] * cp[i]) {
+      tpr = tp[i];
+      cpt = cp[i];
       return true;
     }
   return false;
@@ -395,13 +429,21 @@ hipError_t softmax_dispatch(const RowArgs& a) {
     else return fwd_reg_t<E, TP, CP, LOG>(a);                                             \
   }
     OSATTN_REG_CASE(64, 1)
-    OSATTN_REG_CASE(64, 2)
-    OSATTN_REG_CASE(64, 4)
-    OSATTN_REG_CASE(256, 2)
-    OSATTN_REG_CASE(256, 4)
+    OSATTN_REG_CASE(1024, 2)
     OSATTN_REG_CASE(1024, 4)
     OSATTN_REG_CASE(1024, 8)
-    if constexpr (!BWD) { OSATTN_REG_CASE(1024, 16) }
+    if constexpr (BWD) {
+      OSATTN_REG_CASE(128, 1)
+      OSATTN_REG_CASE(256, 1)
+      OSATTN_REG_CASE(512, 1)
+      OSATTN_REG_CASE(1024, 1)
+    } else {
+      OSATTN_REG_CASE(64, 2)
+      OSATTN_REG_CASE(128, 2)
+      OSATTN_REG_CASE(256, 2)
+      OSATTN_REG_CASE(512, 2)
+      OSATTN_REG_CASE(1024, 16)
+    }
 #undef OSATTN_REG_CASE
   }
   return for_row_ranges(a.rows, 1, [&](long long r0, long long, unsigned blocks) {
@@ -417,26 +459,52 @@ hipError_t softmax_dispatch(const RowArgs& a) {
 }
 
 template <typename E, int T, bool VEC>
-hipError_t xent_t(const RowArgs& a, bool bwd) {
+hipError_t xent_fwd_t(const RowArgs& a) {
   return for_row_ranges(a.rows, 1, [&](long long r0, long long, unsigned blocks) {
-    const long long off = r0 * a.cols;
-    if (bwd)
-      hipLaunchKernelGGL((xent_bwd_kernel<E, T, VEC>), dim3(blocks), dim3(T), 0,
-                         (hipStream_t)a.stream, (const E*)a.x + off, a.targets + r0,
-                         a.lse + r0, a.dloss + r0, (E*)a.dx + off, a.cols);
-    else
-      hipLaunchKernelGGL((xent_fwd_kernel<E, T, VEC>), dim3(blocks), dim3(T), 0,
-                         (hipStream_t)a.stream, (const E*)a.x + off, a.targets + r0,
-                         a.loss + r0, a.lse_out + r0, a.cols);
+    hipLaunchKernelGGL((xent_fwd_kernel<E, T, VEC>), dim3(blocks), dim3(T), 0,
+                       (hipStream_t)a.stream, (const E*)a.x + r0 * a.cols, a.targets + r0,
+                       a.loss + r0, a.lse_out + r0, a.cols);
   });
+}
+
+template <typename E, int T>
+hipError_t xent_bwd_rows_t(const RowArgs& a) {
+  return for_row_ranges(a.rows, 1, [&](long long r0, long long, unsigned blocks) {
+    hipLaunchKernelGGL((xent_bwd_kernel<E, T>), dim3(blocks), dim3(T), 0, (hipStream_t)a.stream,
+                       (const E*)a.x + r0 * a.cols, a.targets + r0, a.lse + r0, a.dloss + r0,
+                       (E*)a.dx + r0 * a.cols, a.cols);
+  });
+}
+
+// Flat backward: whole rows per launch, at most 2^28 chunks (2^20 workgroups).
+template <typename E>
+hipError_t xent_bwd_flat_t(const RowArgs& a) {
+  const long long cpr = a.cols / Elem<E>::kV;
+  const long long rows_per_launch = ((1LL << 28) / cpr) > 0 ? (1LL << 28) / cpr : 1;
+  for (long long r0 = 0; r0 < a.rows; r0 += rows_per_launch) {
+    const long long n = a.rows - r0 < rows_per_launch ? a.rows - r0 : rows_per_launch;
+    const long long n_chunks = n * cpr;
+    hipLaunchKernelGGL((xent_bwd_flat<E>), dim3((unsigned)((n_chunks + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)a.stream, (const E*)a.x + r0 * a.cols, a.targets + r0,
+                       a.lse + r0, a.dloss + r0, (E*)a.dx + r0 * a.cols, (unsigned)n_chunks,
+                       (unsigned)cpr);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename E>
 hipError_t xent_dispatch(const RowArgs& a, bool bwd) {
-  // 256 threads per row for short rows, 1024 above 8192 elements.
+  // Forward: 256 threads per row for short rows, 1024 above 8192 elements.
   const bool vec = row_aligned<E>(a.cols);
-  if (a.cols > 8192) return vec ? xent_t<E, 1024, true>(a, bwd) : xent_t<E, 1024, false>(a, bwd);
-  return vec ? xent_t<E, 256, true>(a, bwd) : xent_t<E, 256, false>(a, bwd);
+  const bool big = a.cols > 8192;
+  if (bwd) {
+    if (vec) return xent_bwd_flat_t<E>(a);
+    return big ? xent_bwd_rows_t<E, 1024>(a) : xent_bwd_rows_t<E, 256>(a);
+  }
+  if (big) return vec ? xent_fwd_t<E, 1024, true>(a) : xent_fwd_t<E, 1024, false>(a);
+  return vec ? xent_fwd_t<E, 256, true>(a) : xent_fwd_t<E, 256, false>(a);
 }
 
 }  // namespace

@@ -327,6 +327,7 @@ ROW_INVALID = [
     ({"rows": 1 << 31}, "ATTN_ERR_SHAPE"),
     ({"cols": 0}, "ATTN_ERR_SHAPE"),
     ({"cols": -3}, "ATTN_ERR_SHAPE"),
+    ({"cols": (1 << 30) + 1}, "ATTN_ERR_SHAPE"),
     ({"dtype": 3}, "ATTN_ERR_DTYPE"),
     ({"dtype": -1}, "ATTN_ERR_DTYPE"),
 ]

@@ -101,12 +101,13 @@ def check_softmax(dtype, rows, cols, log, seed, std=1.0, neg_inf_frac=0.0, offse
     check(dx, ref_b, scale_b, dtype, label + " bwd")
 
 
-# Column counts that reach every kernel shape: register rows of 1, 2 and 4 chunks per
-# lane (one wave per row), 256- and 1024-thread rows, 16 chunks per thread (forward)
-# and the streaming kernels (rows too long to hold, and rows whose length is not a
-# whole number of 16-byte chunks).
-COLS = [1, 3, 8, 64, 100, 512, 1000, 1001, 2048, 4096, 8192, 12345, 32768, 65536, 131072,
-        200000]
+# Column counts that reach every register-kernel shape in each dtype (64 .. 1024
+# threads per row, several rows per workgroup below 256 threads, 1 .. 16 chunks of 16
+# bytes per thread; the forward and the backward pick different shapes for one row
+# length) and the streaming kernels (rows too long to hold, and rows whose length is
+# not a whole number of 16-byte chunks).
+COLS = [1, 3, 8, 64, 100, 512, 1000, 1001, 2048, 4096, 8192, 12345, 16000, 32768, 65536,
+        131072, 200000]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
