@@ -83,7 +83,7 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS-DMA addresses stay SALU
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -186,8 +186,10 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < C::kCPW; ++i) {
       const int ch = wave * C::kCPW + i;
-      buffer_load16_lds(rk, lk + ch * 512, base + goff_k[i]);
-      buffer_load16_lds(rv, lv + ch * 512, base + goff_v[i]);
+      // Tile base in the scalar offset, loop-invariant lane offsets: no vector
+      // address arithmetic per load.
+      buffer_load16_lds(rk, lk + ch * 512, goff_k[i], base);
+      buffer_load16_lds(rv, lv + ch * 512, goff_v[i], base);
     }
   };
 
@@ -247,6 +249,17 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = M::mma32(as_vec8<T>(a), qf[qb][c], s[qb][kb]);
       }
+    }
+    {  // Keep 8 K reads in flight ahead of the MFMAs that consume them (left alone, the
+       // scheduler issues two and waits for them before every pair of MFMAs).
+      constexpr int nR = D / 16 * KB, AH = 8;
+      __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
+#pragma unroll
+      for (int i = 0; i < nR - AH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x8, QB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x8, AH * QB, 0);
     }
     // ---- causal / ragged-tail mask (only on tiles that need it) ------------------------
     const bool need_mask = (k0 + C::kBC > Nk) || (CAUSAL && k0 + C::kBC - 1 > wrow0) ||
@@ -329,6 +342,16 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[qb][t] = M::mma32(a, pf[qb][c4], acc[qb][t]);
       }
+    }
+    {  // the same for the transposed V reads: 4 MFMA operands (8 reads) ahead
+      constexpr int nA = 2 * KB * (D / 32), AH = 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
+#pragma unroll
+      for (int i = 0; i < nA - AH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x8, QB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x8, AH * QB, 0);
     }
   };
 
