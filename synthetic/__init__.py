@@ -236,6 +236,29 @@ MASKED = {
 }
 
 
+# ---- fp8 (e4m3) inputs -----------------------------------------------------------------
+def fp8_quantize(x: torch.Tensor):
+    """e4m3 codes (uint8, same shape) of x / s and the per-tensor dequantisation factor
+    s = max|x| / 448 (so the largest magnitude maps to the largest e4m3 value);
+    torch's conversion rounds to nearest even."""
+    amax = float(x.abs().max())
+    descale = amax / 448.0 if amax > 0 else 1.0
+    codes = (x.float() / descale).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    return codes, descale
+
+
+def make_fp8_inputs(w: Workload) -> dict:
+    """The workload's Q, K, V (the same seeded N(0, 1) draws as make_inputs, before any
+    rounding) quantised to e4m3 per tensor: codes q8, k8, v8 and factors dq, dk, dv."""
+    out = {}
+    for name, t in (("q", 0), ("k", 1), ("v", 2)):
+        shape = w.shape_q if name == "q" else w.shape_kv
+        codes, ds = fp8_quantize(randn(shape, w.seed_base + t))
+        out[name + "8"] = codes
+        out["d" + name] = ds
+    return out
+
+
 # ---- row softmax / log-softmax / cross-entropy workloads ------------------------------
 @dataclass(frozen=True)
 class RowWorkload:

@@ -17,6 +17,7 @@ import numpy as np
 
 import oracle.attention as A
 import oracle.brute as BR
+import oracle.fp8 as F8
 import oracle.online_walk as W
 import oracle.rowsoftmax as RS
 
@@ -601,6 +602,58 @@ def pin_row_large_logits(seed=45):
     return float(max(errs)) if np.all(np.isfinite(RS.softmax(big))) else np.inf
 
 
+def pin_fp8_decode_library(seed=50):
+    """All 256 e4m3 codes against torch's float8_e4m3fn decoding (NaN codes compared
+    as NaN), and a round trip: encoding the decoded finite values with torch gives
+    back the codes (up to the sign of zero)."""
+    import torch
+    codes = np.arange(256)
+    mine = F8.decode_e4m3(codes)
+    lib = torch.tensor(codes, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    if not np.array_equal(np.isnan(mine), np.isnan(lib)):
+        return np.inf
+    fin = ~np.isnan(lib)
+    err = float(np.max(np.abs(mine[fin] - lib[fin])))
+    back = torch.tensor(mine[fin]).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(int)
+    same = (back == codes[fin]) | ((back & 0x7F) == 0) & ((codes[fin] & 0x7F) == 0)
+    return err if np.all(same) else np.inf
+
+
+def pin_fp8_decode_closed_forms():
+    """Values the format fixes: 1.0 = 0x38, 448 = 0x7E (largest), 2^-6 = 0x08 (smallest
+    normal), 2^-9 = 0x01 (smallest subnormal), 1.125 = 0x39, -2 = 0xC0, -0 = 0x80,
+    0x7F and 0xFF are NaN."""
+    want = {0x38: 1.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x39: 1.125, 0xC0: -2.0,
+            0x80: 0.0, 0x07: 7 * 2.0 ** -9, 0x77: 240.0}
+    got = F8.decode_e4m3(list(want))
+    err = float(np.max(np.abs(got - np.array(list(want.values())))))
+    nan_ok = np.isnan(F8.decode_e4m3([0x7F, 0xFF])).all() and np.isfinite(F8.decode_e4m3([0x7E, 0xFE])).all()
+    return err if nan_ok and F8.E4M3_MAX == 448.0 else np.inf
+
+
+def pin_fp8_attention_is_attention_of_decoded(seed=51):
+    """The fp8 forward equals the plain forward of the decoded, dequantised tensors
+    computed by hand here (codes drawn at random, scales chosen as powers of two so
+    the products are exact), against the pure-Python loops."""
+    r = np.random.default_rng(seed)
+    q8 = r.integers(0, 0x7F, (1, 2, 5, 4)) | (r.integers(0, 2, (1, 2, 5, 4)) << 7)
+    k8 = r.integers(0, 0x7F, (1, 1, 5, 4)) | (r.integers(0, 2, (1, 1, 5, 4)) << 7)
+    v8 = r.integers(0, 0x7F, (1, 1, 5, 4)) | (r.integers(0, 2, (1, 1, 5, 4)) << 7)
+    # keep the exponents small so that exp(scores) stays moderate
+    q8, k8, v8 = (np.where((x >> 3) & 0xF > 9, x & 0x87, x) for x in (q8, k8, v8))
+    dq, dk, dv, scale = 0.25, 0.5, 2.0, 0.125
+    o, lse = F8.attention_forward_fp8(q8, k8, v8, dq, dk, dv, scale, causal=True)
+    q = F8.decode_e4m3(q8) * dq
+    k = F8.decode_e4m3(k8) * dk
+    v = F8.decode_e4m3(v8) * dv
+    err = 0.0
+    for h in range(2):  # GQA: both query heads read the one key/value head
+        ob, lb = BR.forward(q[0, h].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), scale, True)
+        err = max(err, float(np.max(np.abs(o[0, h] - np.array(ob)))),
+                  float(np.max(np.abs(lse[0, h] - np.array(lb)))))
+    return err
+
+
 ALL_PINS = {
     "worked_example_walk": (pin_worked_example_walk, 1e-12),
     "worked_example_scores": (pin_worked_example_scores, 0.0),
@@ -649,4 +702,7 @@ ALL_PINS = {
     "row_invariants": (pin_row_invariants, 1e-13),
     "row_torch_library": (pin_row_torch_library, 1e-12),
     "row_large_logits": (pin_row_large_logits, 1e-9),
+    "fp8_decode_library": (pin_fp8_decode_library, 0.0),
+    "fp8_decode_closed_forms": (pin_fp8_decode_closed_forms, 0.0),
+    "fp8_attention_is_attention_of_decoded": (pin_fp8_attention_is_attention_of_decoded, 1e-12),
 }

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as A
+import oracle.fp8 as F8
 import oracle.rowsoftmax as RS
 import oracle_pins as P
 
@@ -139,6 +140,41 @@ def _softmax_no_max(x):
 def test_row_mutant_is_caught(mutant, monkeypatch):
     target, repl = ROW_MUTANTS[mutant]
     monkeypatch.setattr(RS, target, repl)
+    assert _failing_pins(), f"no pin caught mutant {mutant}"
+
+
+FP8_MUTANTS = {
+    # exponent bias 8 instead of 7
+    "fp8_bias_off_by_one": lambda c: _decode_bias(c, 8),
+    # subnormals read as if they had the implicit leading one
+    "fp8_subnormal_as_normal": lambda c: _decode_no_subnormal(c),
+    # the sign bit ignored
+    "fp8_no_sign": lambda c: np.abs(_ORIG_DECODE(c)),
+}
+_ORIG_DECODE = F8.decode_e4m3
+
+
+def _decode_bias(codes, bias):
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    out = np.where(e == 0, sign * np.ldexp(m / 8.0, 1 - bias), sign * np.ldexp(1.0 + m / 8.0, (e - bias).astype(np.int64)))
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def _decode_no_subnormal(codes):
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    out = sign * np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+@pytest.mark.parametrize("mutant", sorted(FP8_MUTANTS))
+def test_fp8_mutant_is_caught(mutant, monkeypatch):
+    monkeypatch.setattr(F8, "decode_e4m3", FP8_MUTANTS[mutant])
     assert _failing_pins(), f"no pin caught mutant {mutant}"
 
 
