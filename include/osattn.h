@@ -229,6 +229,29 @@ int rowxent_bwd(const void* logits, const int* targets, const float* lse,
                 const float* dloss, void* dlogits, long long rows, int cols, int dtype,
                 void* stream);
 
+/*
+ * fp8 forward (the FlashAttention-2 page's forward with 8-bit operands; ml-notes page,
+ * reduced-precision notes: low-precision products, fp32 accumulation and softmax
+ * statistics).  q, k, v are e4m3 codes (OCP 8-bit float: bias 7, subnormals, no
+ * infinity), one byte per element, q [B][H][N][d], k and v [B][Hkv][N][d]; the
+ * values they stand for are code * descale_q (resp. _k, _v).  Computes
+ *   O = softmax(scale * Q K^T) V   (causal: key j <= query i),  LSE as attn_fwd,
+ * O in bf16 [B][H][N][d], LSE fp32 [B][H][N].  The probabilities are rounded to
+ * e4m3 (times 256) for the P V product and the row sums are taken from those same
+ * rounded values, so O is a convex combination of V rows with 8-bit weights: its
+ * distance to the exact result is bounded by 2^-4 (relative) of the weighted spread
+ * of V around it, not by bf16 rounding.  d must be 128 (ATTN_ERR_HEAD_DIM).
+ * workspace: device memory of attn_fwd_fp8_workspace_bytes(B, Hkv, N, d) bytes
+ * (V transposed per head), 16-byte aligned; its contents need no initialisation.
+ * Scales and descales must be finite and > 0 (ATTN_ERR_SCALE).  Other errors as
+ * attn_fwd; only enqueues on `stream`.
+ */
+size_t attn_fwd_fp8_workspace_bytes(int B, int Hkv, int N, int d);
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int Hkv, int N, int d, float scale, float descale_q, float descale_k,
+                 float descale_v, int causal, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* attn_status_string(int status);
 

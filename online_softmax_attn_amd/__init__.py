@@ -45,6 +45,8 @@ __all__ = [
     "attn_fwd_masked",
     "attn_bwd_masked",
     "attn_bwd_masked_workspace_bytes",
+    "attn_fwd_fp8",
+    "attn_fwd_fp8_workspace_bytes",
     "rowsoftmax_fwd",
     "rowsoftmax_bwd",
     "rowxent_fwd",
@@ -77,6 +79,7 @@ DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
             "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
             "attn_fwd_masked", "attn_bwd_masked", "attn_bwd_masked_workspace_bytes",
+            "attn_fwd_fp8", "attn_fwd_fp8_workspace_bytes",
             "rowsoftmax_fwd", "rowsoftmax_bwd", "rowxent_fwd", "rowxent_bwd",
             "attn_status_string")
 
@@ -127,6 +130,10 @@ def library() -> ctypes.CDLL:
     lib.attn_fwd_splitkv_workspace_bytes.restype = sz
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_fwd_fp8.argtypes = [vp] * 5 + [i] * 5 + [f, f, f, f, i, vp, sz, vp]
+    lib.attn_fwd_fp8.restype = i
+    lib.attn_fwd_fp8_workspace_bytes.argtypes = [i] * 4
+    lib.attn_fwd_fp8_workspace_bytes.restype = sz
     ll = ctypes.c_longlong
     lib.rowsoftmax_fwd.argtypes = [vp, vp, ll, i, i, i, vp]
     lib.rowsoftmax_fwd.restype = i
@@ -522,3 +529,39 @@ def rowxent_bwd(logits, targets, lse, dloss, out=None):
     if st != 0:
         raise AttnError(st, "rowxent_bwd")
     return out
+
+
+def attn_fwd_fp8_workspace_bytes(B, Hkv, N, d=128) -> int:
+    return int(library().attn_fwd_fp8_workspace_bytes(B, Hkv, N, d))
+
+
+def attn_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float,
+                 causal: bool = False, scale: float | None = None, out=None, lse=None,
+                 workspace=None):
+    """Forward over e4m3 codes (uint8 tensors q8 [B,H,N,128], k8/v8 [B,Hkv,N,128]) with
+    per-tensor dequantisation factors; returns O (bf16) and LSE (fp32)."""
+    lib = library()
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _check_dev(name, t, torch.uint8)
+    B, H, Hkv, N, d = _dims(q8, k8)
+    if v8.shape != k8.shape:
+        raise ValueError("v8 must have k8's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty(q8.shape, device=q8.device, dtype=torch.bfloat16) if out is None else out
+    lse = torch.empty((B, H, N), device=q8.device, dtype=torch.float32) if lse is None else lse
+    _check_dev("out", out, torch.bfloat16)
+    _check_dev("lse", lse, torch.float32)
+    if out.shape != q8.shape or lse.shape != (B, H, N):
+        raise ValueError("out / lse have the wrong shape")
+    if workspace is None:
+        need = attn_fwd_fp8_workspace_bytes(B, Hkv, N, d)
+        workspace = torch.empty(max(need, 1), device=q8.device, dtype=torch.uint8)
+    _check_dev("workspace", workspace)
+    st = lib.attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), B, H, Hkv, N, d, float(scale), float(descale_q),
+                          float(descale_k), float(descale_v), int(bool(causal)),
+                          workspace.data_ptr(), _ws_bytes(workspace), _stream_handle(q8.device))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_fp8")
+    return out, lse

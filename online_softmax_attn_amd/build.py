@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libosattn.so")
 SOURCES = ["api.hip", "fwd_mfma.hip", "bwd_mfma.hip", "f32_kernels.hip", "splitkv.hip",
-           "rowsoftmax.hip"]
+           "rowsoftmax.hip", "fwd_fp8.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -401,6 +401,36 @@ int rowxent_bwd(const void* logits, const int* targets, const float* lse, const 
   return launched(osattn::launch_rowxent(a, true));
 }
 
+size_t attn_fwd_fp8_workspace_bytes(int B, int Hkv, int N, int d) {
+  if (B < 1 || Hkv < 1 || N < 1 || d != 128) return 0;
+  return round256(osattn::fp8_vt_bytes(B, Hkv, N));
+}
+
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int Hkv, int N, int d, float scale, float descale_q, float descale_k,
+                 float descale_v, int causal, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return ATTN_ERR_NULL;
+  int st = validate_sizes(B, H, Hkv, N, d, ATTN_BF16);  // output dtype
+  if (st != ATTN_OK) return st;
+  if (d != 128) return ATTN_ERR_HEAD_DIM;
+  // V^T holds one head's 128 dims x N rounded up to 128 keys, with 32-bit offsets.
+  if ((long long)128 * (N + 127) >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
+  st = validate_scale(scale);
+  if (st == ATTN_OK) st = validate_scale(descale_q);
+  if (st == ATTN_OK) st = validate_scale(descale_k);
+  if (st == ATTN_OK) st = validate_scale(descale_v);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(workspace))
+    return ATTN_ERR_ALIGN;
+  if (workspace_bytes < attn_fwd_fp8_workspace_bytes(B, Hkv, N, d)) return ATTN_ERR_WORKSPACE;
+  osattn::Fp8Args a{q, k, v, o, lse, B, H, Hkv, N, scale, descale_q, descale_k, descale_v,
+                    causal, workspace, stream};
+  return osattn::launch_fwd_fp8(a) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

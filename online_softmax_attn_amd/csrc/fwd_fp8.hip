@@ -1,0 +1,340 @@
+// Forward pass with fp8 (e4m3) Q, K, V on the gfx950 8-bit matrix cores.
+//
+// The same FlashAttention-2 forward as the bf16 kernel (FlashAttention-2 page,
+// inner-loop steps 1-5 and the final normalisation), with the products done in
+// 8-bit floats and everything else in fp32 (ml-notes page: low-precision multiply,
+// high-precision accumulate, softmax statistics in fp32):
+//  * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales): 64 head
+//    dimensions per instruction, exact products, fp32 sums.  S is then scaled by
+//    scale * dq * dk (the tensors' dequantisation factors) in the exp2 argument.
+//  * The running max is exact per tile (the page's m_new = max(m_old, rowmax)):
+//    then every probability is at most 1, and P * 256 (at most 256 < 448, the
+//    largest e4m3 value) is rounded to e4m3 for O^T += V^T P^T.  The factor 256
+//    keeps small probabilities out of the subnormal range.
+//  * The row sum l is taken by the matrix core from the same 8-bit P (a row of
+//    ones as an extra A operand), so O = Ot / l uses exactly the weights that
+//    produced Ot; the 256 cancels.  LSE = ln 2 * (m + log2 l - 8).
+//  * V^T is the A operand of the O update, with keys along each lane's bytes; a
+//    small pass writes V transposed per (batch, kv head), keys of each 64-key
+//    block in the order the probabilities sit in the registers (see vt_key), so
+//    both operands of the O update are plain 16-byte LDS reads.
+// d = 128 only.  Layouts: Q, K, V codes [B][H or Hkv][N][128] bytes, O bf16
+// [B][H][N][128], LSE fp32 [B][H][N]; the workspace holds V^T, [B][Hkv][128][Np]
+// bytes with Np = N rounded up to 128 (padding keys are zero).
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace osattn {
+
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kD = 128;       // head dimension
+constexpr int kNW = 8;        // waves per workgroup (two per SIMD)
+constexpr int kBR = kNW * 32; // query rows per workgroup
+constexpr int kBC = 128;      // keys per tile
+constexpr int kRow = 128;     // bytes per LDS row (K: a key's 128 dims; V^T: 128 keys of a dim)
+constexpr int kTile = kBC * kRow;          // 16 KB
+constexpr int kCPW = kTile / 1024 / kNW;   // 1 KB LDS-DMA chunks per wave per tensor
+
+// Key (within a 64-key block) of byte b of the P^T operand held by lane half h:
+// the S^T accumulator gives lane (row, h) keys 8g + 4h + e of each 32-key block in
+// register 4g + e; bytes 0-15 are the first block's registers, 16-31 the second's.
+__host__ __device__ constexpr int vt_key(int h, int b) {
+  return 32 * (b / 16) + 8 * ((b % 16) / 4) + 4 * h + (b % 4);
+}
+
+// 16-byte granule swizzle of 128-byte LDS rows: conflict-free 128-bit reads by 32
+// lanes on 32 consecutive rows.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// ---- V -> V^T with the block key order --------------------------------------------
+// One workgroup per (batch * kv head, 64-key block): the block's 64 x 128 bytes go
+// through LDS; thread t writes dim t / 2, block positions 32 * (t % 2) .. +31.
+__global__ __launch_bounds__(256) void vt_kernel(const uint8_t* __restrict__ V,
+                                                 uint8_t* __restrict__ Vt, int N, int Np) {
+  __shared__ uint8_t tile[64][kD + 4];
+  const int blk = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int k0 = blk * 64;
+  const int t = threadIdx.x;
+  // Load: thread t reads 32 bytes, row t / 4, bytes 32 * (t % 4) .. +31.
+  {
+    const int r = t / 4, c = 32 * (t % 4);
+    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+    if (k0 + r < N) {
+      const u32x4* src = (const u32x4*)(V + (bh * N + k0 + r) * kD + c);
+      a = src[0];
+      b = src[1];
+    }
+    uint32_t* dst = (uint32_t*)&tile[r][c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dst[i] = a[i];
+      dst[4 + i] = b[i];
+    }
+  }
+  __syncthreads();
+  const int d = t / 2, h = t % 2;
+  uint32_t w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v |= (uint32_t)tile[vt_key(h, 4 * j + e)][d] << (8 * e);
+    w[j] = v;
+  }
+  u32x4* out = (u32x4*)(Vt + (bh * kD + d) * Np + k0 + 32 * h);
+  out[0] = u32x4{w[0], w[1], w[2], w[3]};
+  out[1] = u32x4{w[4], w[5], w[6], w[7]};
+}
+
+__device__ __forceinline__ f32x16 mma8(i32x8 a, i32x8 b, f32x16 c) {
+  // e4m3 x e4m3 (format selectors 0), unit block scales (E8M0 code 127 = 2^0).
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ i32x8 lds_read32(const char* p0, const char* p1) {
+  const u32x4 a = *(const u32x4*)p0, b = *(const u32x4*)p1;
+  i32x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = (int)a[i];
+    r[4 + i] = (int)b[i];
+  }
+  return r;
+}
+
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
+                    const uint8_t* __restrict__ Vt, uint16_t* __restrict__ O,
+                    float* __restrict__ LSE, int H, int Hkv, int N, int Np, int n_qtiles,
+                    float c_log2, float dv) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lk0[kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv0[kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t lk1[kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv1[kTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  int qt = L % n_qtiles;
+  const int bh = L / n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
+  const int h = bh % H;
+  const int b = bh / H;
+  const int kvh = h / (H / Hkv);
+  const int q0 = qt * kBR;
+  const int wrow0 = q0 + wave * 32;
+  const size_t g = (size_t)b * Hkv + kvh;
+
+  const auto rq = make_rsrc(Q + (size_t)bh * N * kD, (uint32_t)N * kD);
+  const auto rk = make_rsrc(K + g * N * kD, (uint32_t)N * kD);
+  const auto rv = make_rsrc(Vt + g * kD * Np, (uint32_t)kD * Np);
+
+  // Q fragments (B operand of S^T = K Q^T): row l32, dims 64c + 32hi .. +31.
+  i32x8 qf[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t off = (uint32_t)(wrow0 + l32) * kD + 64 * c + 32 * hi;
+    const u32x4 a = buffer_load16(rq, off), bb = buffer_load16(rq, off + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qf[c][i] = (int)a[i];
+      qf[c][4 + i] = (int)bb[i];
+    }
+  }
+
+  int n_kt = (N + kBC - 1) / kBC;
+  if (CAUSAL) n_kt = min(n_kt, (q0 + kBR + kBC - 1) / kBC);
+
+  // LDS-DMA: chunk ch of a tile is LDS bytes [ch * 1024, +1024) = rows 8ch .. 8ch+7;
+  // the lane's 16 bytes are physical granule pg of its row, logical pg ^ swz(row).
+  uint32_t goff_k[kCPW], goff_v[kCPW];
+#pragma unroll
+  for (int i = 0; i < kCPW; ++i) {
+    const int off = (wave * kCPW + i) * 1024 + lane * 16;
+    const int row = off / kRow;
+    const int lg = ((off % kRow) / 16) ^ swz(row);
+    goff_k[i] = row * kRow + lg * 16;        // + tile base (k0 * 128) in the scalar offset
+    goff_v[i] = row * Np + lg * 16;          // row = dim; + tile base (k0) in the scalar offset
+  }
+  auto issue = [&](int kt, uint8_t* lk, uint8_t* lv) __attribute__((always_inline)) {
+    const uint32_t k0 = (uint32_t)kt * kBC;
+#pragma unroll
+    for (int i = 0; i < kCPW; ++i) {
+      const int ch = wave * kCPW + i;
+      buffer_load16_lds(rk, lk + ch * 1024, goff_k[i], k0 * kRow);
+      buffer_load16_lds(rv, lv + ch * 1024, goff_v[i], k0);
+    }
+  };
+
+  // LDS read offsets: row l32 of a 32-row block, logical granules 4c + 2hi, +1.
+  uint32_t aoff[2][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) aoff[c][j] = l32 * kRow + 16 * ((4 * c + 2 * hi + j) ^ swz(l32));
+
+  f32x16 acc[kD / 32], lacc;
+#pragma unroll
+  for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
+  float m_run = -1e30f;  // finite: exp2(m_old - m_new) never sees inf - inf
+  i32x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;  // e4m3 1.0 in every byte
+
+  auto compute = [&](int kt, const char* kbase, const char* vbase) __attribute__((always_inline)) {
+    const int k0 = kt * kBC;
+    if (CAUSAL && k0 > wrow0 + 31) return;  // every key after every row of the wave
+    f32x16 s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const char* base = kbase + kb * 32 * kRow;
+        s[kb] = mma8(lds_read32(base + aoff[c][0], base + aoff[c][1]), qf[c], s[kb]);
+      }
+    const bool need_mask = (k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > wrow0);
+    if (need_mask) {
+      asm volatile("");  // keep this a branch
+      const int row = wrow0 + l32;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= N || (CAUSAL && key > row)) s[kb][r] = -INFINITY;
+        }
+    }
+    // Exact running max (log2 units of the scaled scores).
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    const float m_new = fmaxf(m_run, wave_xor32_max(mx) * c_log2);
+    if (__any(m_new > m_run)) {
+      const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
+      m_run = m_new;
+    }
+    // P * 256 in e4m3, bytes in vt_key order: pf[m] covers keys 64m .. 64m+63.
+    const float bias = 8.0f - m_run;  // exp2(s*c - m + 8) = 256 * P
+    i32x8 pf[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x16& sb = s[2 * m + j / 4];
+        const int r0 = 4 * (j % 4);
+        const float p0 = fast_exp2(fmaf(sb[r0 + 0], c_log2, bias));
+        const float p1 = fast_exp2(fmaf(sb[r0 + 1], c_log2, bias));
+        const float p2 = fast_exp2(fmaf(sb[r0 + 2], c_log2, bias));
+        const float p3 = fast_exp2(fmaf(sb[r0 + 3], c_log2, bias));
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+        pf[m][j] = w;
+      }
+    // O^T += V^T P^T (dims 32t .. 32t+31), and l += sum of the same 8-bit P.
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int t = 0; t < kD / 32; ++t) {
+        const char* base = vbase + t * 32 * kRow;
+        acc[t] = mma8(lds_read32(base + aoff[m][0], base + aoff[m][1]), pf[m], acc[t]);
+      }
+      lacc = mma8(ones, pf[m], lacc);
+    }
+  };
+
+  if (0 < n_kt) issue(0, lk0, lv0);
+  auto step = [&](auto sc, int kt) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
+    uint8_t* lk = S == 0 ? lk0 : lk1;
+    uint8_t* lv = S == 0 ? lv0 : lv1;
+    uint8_t* nk = S == 0 ? lk1 : lk0;
+    uint8_t* nv = S == 0 ? lv1 : lv0;
+    wait_vmcnt<0>();
+    block_barrier();  // tile kt is in LDS; the other stage is free
+    if (kt + 1 < n_kt) issue(kt + 1, nk, nv);
+    compute(kt, (const char*)lk, (const char*)lv);
+  };
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < n_kt) step(std::integral_constant<int, 1>{}, kt + 1);
+  }
+
+  // O = Ot * dv / l; LSE = ln 2 * (m + log2 l - 8).
+  const int row = wrow0 + l32;
+  const float l = lacc[0];
+  const float inv = dv / l;
+  if (row < N) {
+    uint16_t* op = O + ((size_t)bh * N + row) * kD;
+#pragma unroll
+    for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        u32x2 w;
+        w[0] = (uint32_t)to_bits<__bf16>(acc[t][4 * gg + 0] * inv) |
+               ((uint32_t)to_bits<__bf16>(acc[t][4 * gg + 1] * inv) << 16);
+        w[1] = (uint32_t)to_bits<__bf16>(acc[t][4 * gg + 2] * inv) |
+               ((uint32_t)to_bits<__bf16>(acc[t][4 * gg + 3] * inv) << 16);
+        *(u32x2*)(op + 32 * t + 8 * gg + 4 * hi) = w;
+      }
+    if (hi == 0) LSE[(size_t)bh * N + row] = (m_run + __log2f(l) - 8.0f) * kLn2;
+  }
+}
+
+}  // namespace
+
+size_t fp8_vt_bytes(int B, int Hkv, int N) {
+  const size_t np = ((size_t)N + kBC - 1) / kBC * kBC;
+  return (size_t)B * Hkv * kD * np;
+}
+
+hipError_t launch_fwd_fp8(const Fp8Args& a) {
+  const int np = (a.N + kBC - 1) / kBC * kBC;
+  hipLaunchKernelGGL(vt_kernel, dim3((unsigned)(np / 64), (unsigned)(a.B * a.Hkv)), dim3(256), 0,
+                     (hipStream_t)a.stream, (const uint8_t*)a.v, (uint8_t*)a.workspace, a.N, np);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_qtiles = (a.N + kBR - 1) / kBR;
+  const long long blocks = (long long)n_qtiles * a.B * a.H;
+  const float c_log2 = a.scale * a.descale_q * a.descale_k * kLog2e;
+  if (a.causal)
+    hipLaunchKernelGGL(fwd_fp8_kernel<true>, dim3((unsigned)blocks), dim3(kNW * 64), 0,
+                       (hipStream_t)a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k,
+                       (const uint8_t*)a.workspace, (uint16_t*)a.o, a.lse, a.H, a.Hkv, a.N, np,
+                       n_qtiles, c_log2, a.descale_v);
+  else
+    hipLaunchKernelGGL(fwd_fp8_kernel<false>, dim3((unsigned)blocks), dim3(kNW * 64), 0,
+                       (hipStream_t)a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k,
+                       (const uint8_t*)a.workspace, (uint16_t*)a.o, a.lse, a.H, a.Hkv, a.N, np,
+                       n_qtiles, c_log2, a.descale_v);
+  return hipGetLastError();
+}
+
+}  // namespace osattn

@@ -84,6 +84,23 @@ constexpr int kStageDkdv = 1;
 constexpr int kStageDq = 2;
 
 hipError_t launch_fwd_mfma(const FwdArgs& a);
+
+// fp8 (e4m3) forward, d = 128: codes q [B][H][N][128], k, v [B][Hkv][N][128];
+// o bf16, lse fp32; workspace >= fp8_vt_bytes(B, Hkv, N) bytes (V transposed).
+struct Fp8Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Hkv, N;
+  float scale, descale_q, descale_k, descale_v;
+  int causal;
+  void* workspace;
+  void* stream;
+};
+size_t fp8_vt_bytes(int B, int Hkv, int N);
+hipError_t launch_fwd_fp8(const Fp8Args& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_preprocess(const BwdArgs& a);
 hipError_t launch_bwd_mfma(const BwdArgs& a);

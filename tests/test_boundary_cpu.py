@@ -24,7 +24,7 @@ S = osa.STATUS
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\**((?:attn|rowsoftmax|rowxent)_[a-z_]+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\**((?:attn|rowsoftmax|rowxent)_[a-z0-9_]+)\s*\(",
                                  text, flags=re.M)))
 
 
@@ -377,3 +377,46 @@ def test_row_binding_rejects_host_tensors():
         osa.rowxent_fwd(x, t)
     with pytest.raises(ValueError):
         osa.rowxent_bwd(x, t, t.float(), t.float())
+
+
+# ---- fp8 forward ----------------------------------------------------------------------
+def fp8(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Hkv=1, N=100, d=128, scale=0.125, dq=0.01,
+             dk=0.01, dv=0.01, causal=0, ws=P, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return osa.library().attn_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                      a["Hkv"], a["N"], a["d"], a["scale"], a["dq"], a["dk"],
+                                      a["dv"], a["causal"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+FP8_INVALID = [
+    ({"q": None}, "ATTN_ERR_NULL"),
+    ({"ws": None}, "ATTN_ERR_NULL"),
+    ({"N": 0}, "ATTN_ERR_SHAPE"),
+    ({"B": 0}, "ATTN_ERR_SHAPE"),
+    ({"d": 64}, "ATTN_ERR_HEAD_DIM"),
+    ({"d": 96}, "ATTN_ERR_HEAD_DIM"),
+    ({"H": 3, "Hkv": 2}, "ATTN_ERR_GQA"),
+    ({"causal": 2}, "ATTN_ERR_SHAPE"),
+    ({"scale": 0.0}, "ATTN_ERR_SCALE"),
+    ({"dq": float("nan")}, "ATTN_ERR_SCALE"),
+    ({"dk": -1.0}, "ATTN_ERR_SCALE"),
+    ({"dv": float("inf")}, "ATTN_ERR_SCALE"),
+    ({"k": P + 8}, "ATTN_ERR_ALIGN"),
+    ({"ws": P + 4}, "ATTN_ERR_ALIGN"),
+    ({"ws_bytes": 100}, "ATTN_ERR_WORKSPACE"),
+]
+
+
+@pytest.mark.parametrize("kw,code", FP8_INVALID)
+def test_fp8_rejects(kw, code):
+    assert fp8(**kw) == S[code]
+
+
+def test_fp8_workspace_bytes():
+    lib = osa.library()
+    # V transposed: B * Hkv * 128 dims * N rounded up to 128 keys, rounded to 256 bytes.
+    assert lib.attn_fwd_fp8_workspace_bytes(2, 3, 100, 128) == 2 * 3 * 128 * 128
+    assert lib.attn_fwd_fp8_workspace_bytes(1, 1, 129, 128) == 128 * 256
+    assert lib.attn_fwd_fp8_workspace_bytes(1, 1, 100, 64) == 0
+    assert osa.attn_fwd_fp8_workspace_bytes(4, 16, 8192) == 4 * 16 * 128 * 8192
