@@ -41,7 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3, "fp8": 5033.2}
 METRIC = "attention fwd/bwd TFLOP/s + % of bf16 MFMA peak, B*H=64 N=8192 d=128"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -170,6 +170,16 @@ def write_traffic(folders, workload_name, rows: bool = False):
     print(json.dumps(out, indent=1))
 
 
+def blas_threads() -> int:
+    """Threads the oracle's matrix products run on (BLAS pool), else the affinity size."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max((i.get("num_threads", 1) for i in threadpool_info()
+                        if i.get("user_api") == "blas"), default=1))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(w, inp, gpu_out, heads: int = 16):
     """Time the fp64 oracle (fwd + bwd) on `heads` query heads of the workload."""
     import numpy as np
@@ -215,6 +225,9 @@ def main():
                     help="time the split-KV forward on the decoding workloads (one line each)")
     ap.add_argument("--masked", action="store_true",
                     help="time the interval-masked fwd+bwd on the masked workloads (one line each)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the fp8 (e4m3) forward on the B4 H16 N8192 d128 shape, "
+                         "non-causal and causal (one line each)")
     ap.add_argument("--rows", action="store_true",
                     help="time row softmax / log-softmax / cross-entropy fwd+bwd on the row "
                          "workloads (one line each)")
@@ -264,6 +277,12 @@ def main():
     if args.masked:
         for name, (w, kind, mk) in S.MASKED.items():
             print(json.dumps(run_masked(name, w, kind, mk, args, osa, torch)), flush=True)
+        return
+    if args.fp8:
+        for causal in (False, True):
+            w = S.custom("bf16", 4, 16, 16, 8192, 128, causal, seed_base=34000)
+            print(json.dumps(run_fp8(w, args, osa, torch, with_cpu=not args.no_cpu_baseline)),
+                  flush=True)
         return
     if args.rows:
         for w in S.ROWS.values():
@@ -397,6 +416,61 @@ def run_masked(name, w, kind, mk, args, osa, torch):
                     "frac_peak": round(ff / (f_ms * 1e-3) / 1e12 / peak, 4)},
             "bwd": {"ms": round(b_ms, 4), "tflops": round(bf / (b_ms * 1e-3) / 1e12, 2),
                     "frac_peak": round(bf / (b_ms * 1e-3) / 1e12 / peak, 4)}}
+
+
+def run_fp8(w, args, osa, torch, with_cpu: bool):
+    """One attn_fwd_fp8 call per step (the V transpose pass and the forward kernel);
+    FLOP 4 * N^2 * d per head (halved when causal), against the dense fp8 peak."""
+    import synthetic as S
+
+    inp = S.make_fp8_inputs(w)
+    q8, k8, v8 = (inp[n].cuda() for n in ("q8", "k8", "v8"))
+    ws = torch.empty(osa.attn_fwd_fp8_workspace_bytes(w.B, w.Hkv, w.N), device="cuda",
+                     dtype=torch.uint8)
+    o = torch.empty(q8.shape, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((w.B, w.H, w.N), device="cuda", dtype=torch.float32)
+    fwd = lambda: osa.attn_fwd_fp8(q8, k8, v8, inp["dq"], inp["dk"], inp["dv"], causal=w.causal,
+                                   scale=w.scale, out=o, lse=lse, workspace=ws)
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    st = stats([e[0].elapsed_time(e[1]) for e in ev])
+    flop = w.fwd_flop()
+    tf = flop / (st["mean"] * 1e-3) / 1e12
+    line = {"metric": "fp8 (e4m3) attention forward TFLOP/s", "value": round(tf, 2),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(st["mean"], 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8-e4m3 (fp32 accumulate, bf16 out)",
+            "data": "synthetic", "config": dict(w.describe(), dtype="fp8_e4m3",
+                                                workload="fp8_e4m3_B4_H16_N8192_d128"
+                                                + ("_causal" if w.causal else "")),
+            "roofline": {"bound": "mfma", "kernel": "vt_kernel + fwd_fp8_kernel (one call)",
+                         "achieved": round(tf, 2), "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_TFLOPS["fp8"], 4), "flop_per_launch": flop,
+                         "traffic": None, "ms": {k: round(x, 4) for k, x in st.items()}}}
+    if with_cpu:
+        import numpy as np
+
+        import oracle.fp8 as F8
+        t0 = time.perf_counter()
+        sub = {n: inp[n][:1, :1].numpy() for n in ("q8", "k8", "v8")}
+        ref_o, _ = F8.attention_forward_fp8(sub["q8"], sub["k8"], sub["v8"], inp["dq"], inp["dk"],
+                                            inp["dv"], w.scale, w.causal)
+        dt = time.perf_counter() - t0
+        err = float(np.max(np.abs(o[0, 0].float().cpu().double().numpy() - ref_o[0, 0])))
+        line["cpu_baseline"] = {"value": round(flop / (w.B * w.H) / dt / 1e12, 5), "unit": "TFLOP/s",
+                                "cores": blas_threads(), "kind": "oracle",
+                                "sample": f"fp64 oracle forward (decoded fp8 inputs) on head (0,0) of "
+                                          f"{w.B * w.H}, {dt:.2f} s",
+                                "seconds": round(dt, 3), "gpu_vs_oracle_o_max_abs": err}
+    return line
 
 
 def row_bytes(w):
