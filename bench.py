@@ -482,29 +482,38 @@ def row_bytes(w):
     return 2 * el, 3 * el
 
 
-def row_cpu_baseline(w, inp, n_rows: int):
-    """Time the fp64 oracle's forward + backward on the first n_rows rows."""
+def row_cpu_baseline(w, inp, budget_s: float = 10.0):
+    """Time the fp64 oracle's forward + backward over the rows in order, in chunks of
+    about 4e7 elements, until every row is done or budget_s seconds of oracle time
+    have been spent (the conversion of each chunk to fp64 is not timed)."""
     import numpy as np
 
     import oracle.rowsoftmax as R
-    x = inp["x"][:n_rows].double().numpy()
-    t0 = time.perf_counter()
-    if w.op == "xent":
-        t = inp["targets"][:n_rows].numpy().astype(np.int64)
-        R.cross_entropy(x, t)
-        R.cross_entropy_backward(x, t, inp["dloss"][:n_rows].numpy())
-    else:
-        log = w.op == "log_softmax"
-        y = R.log_softmax(x) if log else R.softmax(x)
-        dy = inp["dy"][:n_rows].double().numpy()
-        (R.log_softmax_backward if log else R.softmax_backward)(y, dy)
-    dt = time.perf_counter() - t0
+    chunk = max(1, int(4e7 // w.cols))
+    done, dt = 0, 0.0
+    while done < w.rows and dt < budget_s:
+        n = min(chunk, w.rows - done)
+        x = inp["x"][done:done + n].double().numpy()
+        if w.op == "xent":
+            t = inp["targets"][done:done + n].numpy().astype(np.int64)
+            dl = inp["dloss"][done:done + n].numpy()
+            t0 = time.perf_counter()
+            R.cross_entropy(x, t)
+            R.cross_entropy_backward(x, t, dl)
+        else:
+            log = w.op == "log_softmax"
+            dy = inp["dy"][done:done + n].double().numpy()
+            t0 = time.perf_counter()
+            y = R.log_softmax(x) if log else R.softmax(x)
+            (R.log_softmax_backward if log else R.softmax_backward)(y, dy)
+        dt += time.perf_counter() - t0
+        done += n
     fb, bb = row_bytes(w)
-    frac = n_rows / w.rows
+    frac = done / w.rows
     return {"value": round((fb + bb) * frac / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"fp64 oracle fwd+bwd on the first {n_rows} of {w.rows} rows, {dt:.2f} s; "
-                      "bytes counted as for the GPU (dtype-sized elements)",
+            "sample": f"fp64 oracle fwd+bwd on rows 0-{done - 1} of {w.rows} (chunks of {chunk} "
+                      f"rows), {dt:.2f} s; bytes counted as for the GPU (dtype-sized elements)",
             "seconds": round(dt, 3)}
 
 
@@ -568,8 +577,7 @@ def run_rows(w, args, osa, torch, with_cpu: bool):
                          "ms": round(dom[3], 4), "traffic": traffic_of(load_traffic(), dom[4],
                                                                        w.name)}}
     if with_cpu:
-        n = max(1, min(w.rows, int(4e7 // w.cols)))
-        line["cpu_baseline"] = row_cpu_baseline(w, inp, n)
+        line["cpu_baseline"] = row_cpu_baseline(w, inp)
     return line
 
 
