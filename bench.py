@@ -180,8 +180,10 @@ def blas_threads() -> int:
         return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, inp, gpu_out, heads: int = 16):
-    """Time the fp64 oracle (fwd + bwd) on `heads` query heads of the workload."""
+def cpu_baseline(w, inp, gpu_out, heads: int = 0):
+    """Time the fp64 oracle (fwd + bwd) on `heads` query heads of the workload (by default
+    16 at N = 8192, scaled by (8192 / N)^2 so that the sample stays near 10-15 s of oracle
+    time, at least one KV group and at most 16 heads)."""
     import numpy as np
 
     import oracle.attention as A
@@ -192,7 +194,9 @@ def cpu_baseline(w, inp, gpu_out, heads: int = 16):
     except Exception:  # threadpoolctl missing: report the affinity size
         threads = len(os.sched_getaffinity(0))
     n_rep = w.H // w.Hkv
-    groups = [(0, g) for g in range(max(1, heads // n_rep))]
+    if heads <= 0:
+        heads = max(1, min(16, int(16 * (8192 / w.N) ** 2)))
+    groups = [(0, g) for g in range(min(w.Hkv, max(1, heads // n_rep)))]
     n_heads = len(groups) * n_rep
     t0 = time.perf_counter()
     ref = A.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, w.causal,
