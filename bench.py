@@ -1,7 +1,7 @@
 """Throughput benchmark of the fused attention path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--sweep] [--decode] [--masked]
+                    [--no-cpu-baseline] [--sweep] [--decode] [--masked] [--rows] [--fp8]
 
 A step is one pass of the whole path over one batch of resident synthetic input:
 the forward kernel (O and LSE) followed by the backward (D preprocess, dK/dV
@@ -24,7 +24,7 @@ flop/clk x 2.4 GHz) or HBM's 8 TB/s.  ``roofline`` repeats the entry of the
 kernel with the largest share of the step.  ``traffic`` is the HBM bytes per
 launch from committed rocprofv3 counter runs, or null once the kernel source has
 changed since they were taken.  ``cpu_baseline`` times the fp64 oracle on the
-host for a bounded sample (16 heads of the same workload).
+host for a bounded sample (16 heads of the headline workload; fewer at longer N).
 """
 
 from __future__ import annotations
@@ -180,10 +180,18 @@ def blas_threads() -> int:
         return len(os.sched_getaffinity(0))
 
 
+def baseline_groups(w, heads: int = 0):
+    """The (batch, kv head) groups of the oracle sample: `heads` query heads, by default
+    16 at N = 8192 scaled by (8192 / N)^2 so that the sample stays near 10-15 s of oracle
+    time; whole KV groups of batch 0, at least one, at most all of them."""
+    n_rep = w.H // w.Hkv
+    if heads <= 0:
+        heads = max(1, min(16, int(16 * (8192 / w.N) ** 2)))
+    return [(0, g) for g in range(min(w.Hkv, max(1, heads // n_rep)))]
+
+
 def cpu_baseline(w, inp, gpu_out, heads: int = 0):
-    """Time the fp64 oracle (fwd + bwd) on `heads` query heads of the workload (by default
-    16 at N = 8192, scaled by (8192 / N)^2 so that the sample stays near 10-15 s of oracle
-    time, at least one KV group and at most 16 heads)."""
+    """Time the fp64 oracle (fwd + bwd) on the query heads of baseline_groups."""
     import numpy as np
 
     import oracle.attention as A
@@ -194,9 +202,7 @@ def cpu_baseline(w, inp, gpu_out, heads: int = 0):
     except Exception:  # threadpoolctl missing: report the affinity size
         threads = len(os.sched_getaffinity(0))
     n_rep = w.H // w.Hkv
-    if heads <= 0:
-        heads = max(1, min(16, int(16 * (8192 / w.N) ** 2)))
-    groups = [(0, g) for g in range(min(w.Hkv, max(1, heads // n_rep)))]
+    groups = baseline_groups(w, heads)
     n_heads = len(groups) * n_rep
     t0 = time.perf_counter()
     ref = A.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, w.causal,
