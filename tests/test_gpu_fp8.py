@@ -1,10 +1,10 @@
 """GPU parity of the fp8 (e4m3) forward against the fp64 oracle on the decoded inputs.
 
 Bar (derived from the arithmetic, element by element).  The scores are exact fp8
-products summed in fp32; the probabilities P (largest 1 against the running max)
-are rounded to e4m3 after scaling by 256, and O = sum P8 v / sum P8 with the same
-P8.  With p_j = exp(s_j - max s) (so p <= 1, L = sum p = exp(LSE - max s) >= 1), each
-rounded weight is p_j (1 + delta_j) + eps_j with |delta_j| <= 2^-4 (three mantissa
+products summed in fp32; the probabilities P (formed against a running reference that
+never exceeds the row max, P * 256 <= 446) are rounded to e4m3 after scaling by 256,
+and O = sum P8 v / sum P8 with the same P8.  With p_j = exp(s_j - max s) (so p <= 1,
+L = sum p = exp(LSE - max s) >= 1), each rounded weight is p_j (1 + delta_j) + eps_j with |delta_j| <= 2^-4 (three mantissa
 bits) and |eps_j| <= 2^-18 (half the subnormal spacing 2^-9 of e4m3, over the factor
 256; earlier tiles are rescaled by factors <= 1, which only shrinks their errors).
 Then for every output element
