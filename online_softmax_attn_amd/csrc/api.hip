@@ -87,6 +87,8 @@ size_t attn_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d, int dtype) 
   return 2 * round256((size_t)B * H * N * sizeof(float));
 }
 
+// Helpers with C++ types (inside the extern "C" block, they need C++ linkage).
+extern "C++" {
 namespace {
 
 bool aligned_all(std::initializer_list<const void*> ps) {
@@ -124,6 +126,7 @@ int run_bwd_kernels(const osattn::BwdArgs& a) {
 }
 
 }  // namespace
+}  // extern "C++"
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
