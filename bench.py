@@ -236,7 +236,7 @@ def main():
     ap.add_argument("--masked", action="store_true",
                     help="time the interval-masked fwd+bwd on the masked workloads (one line each)")
     ap.add_argument("--fp8", action="store_true",
-                    help="time the fp8 (e4m3) forward on the B4 H16 N8192 d128 shape, "
+                    help="time the fp8 (e4m3) forward on the B4 H16 N8192 shape, d = 128 and 64, "
                          "non-causal and causal (one line each)")
     ap.add_argument("--rows", action="store_true",
                     help="time row softmax / log-softmax / cross-entropy fwd+bwd on the row "
@@ -289,10 +289,11 @@ def main():
             print(json.dumps(run_masked(name, w, kind, mk, args, osa, torch)), flush=True)
         return
     if args.fp8:
-        for causal in (False, True):
-            w = S.custom("bf16", 4, 16, 16, 8192, 128, causal, seed_base=34000)
-            print(json.dumps(run_fp8(w, args, osa, torch, with_cpu=not args.no_cpu_baseline)),
-                  flush=True)
+        for d in (128, 64):
+            for causal in (False, True):
+                w = S.custom("bf16", 4, 16, 16, 8192, d, causal, seed_base=34000)
+                print(json.dumps(run_fp8(w, args, osa, torch, with_cpu=not args.no_cpu_baseline)),
+                      flush=True)
         return
     if args.rows:
         for w in S.ROWS.values():
@@ -435,7 +436,7 @@ def run_fp8(w, args, osa, torch, with_cpu: bool):
 
     inp = S.make_fp8_inputs(w)
     q8, k8, v8 = (inp[n].cuda() for n in ("q8", "k8", "v8"))
-    ws = torch.empty(osa.attn_fwd_fp8_workspace_bytes(w.B, w.Hkv, w.N), device="cuda",
+    ws = torch.empty(osa.attn_fwd_fp8_workspace_bytes(w.B, w.Hkv, w.N, w.d), device="cuda",
                      dtype=torch.uint8)
     o = torch.empty(q8.shape, device="cuda", dtype=torch.bfloat16)
     lse = torch.empty((w.B, w.H, w.N), device="cuda", dtype=torch.float32)
@@ -459,7 +460,7 @@ def run_fp8(w, args, osa, torch, with_cpu: bool):
             "ms_per_step": round(st["mean"], 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "fp8-e4m3 (fp32 accumulate, bf16 out)",
             "data": "synthetic", "config": dict(w.describe(), dtype="fp8_e4m3",
-                                                workload="fp8_e4m3_B4_H16_N8192_d128"
+                                                workload=f"fp8_e4m3_B4_H16_N8192_d{w.d}"
                                                 + ("_causal" if w.causal else "")),
             "roofline": {"bound": "mfma", "kernel": "vt_kernel + fwd_fp8_kernel (one call)",
                          "achieved": round(tf, 2), "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",

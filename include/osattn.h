@@ -240,9 +240,10 @@ int rowxent_bwd(const void* logits, const int* targets, const float* lse,
  * e4m3 (times 256) for the P V product and the row sums are taken from those same
  * rounded values, so O is a convex combination of V rows with 8-bit weights: its
  * distance to the exact result is bounded by 2^-4 (relative) of the weighted spread
- * of V around it, not by bf16 rounding.  d must be 128 (ATTN_ERR_HEAD_DIM).
+ * of V around it, not by bf16 rounding.  d must be 64 or 128 (ATTN_ERR_HEAD_DIM).
  * workspace: device memory of attn_fwd_fp8_workspace_bytes(B, Hkv, N, d) bytes
- * (V transposed per head), 16-byte aligned; its contents need no initialisation.
+ * (V transposed per head: B * Hkv * d * N rounded up to 128, then to 256 bytes; 0
+ * for invalid sizes), 16-byte aligned; its contents need no initialisation.
  * Scales and descales must be finite and > 0 (ATTN_ERR_SCALE).  Other errors as
  * attn_fwd; only enqueues on `stream`.
  */

@@ -538,8 +538,8 @@ def attn_fwd_fp8_workspace_bytes(B, Hkv, N, d=128) -> int:
 def attn_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float,
                  causal: bool = False, scale: float | None = None, out=None, lse=None,
                  workspace=None):
-    """Forward over e4m3 codes (uint8 tensors q8 [B,H,N,128], k8/v8 [B,Hkv,N,128]) with
-    per-tensor dequantisation factors; returns O (bf16) and LSE (fp32)."""
+    """Forward over e4m3 codes (uint8 tensors q8 [B,H,N,d], k8/v8 [B,Hkv,N,d], d = 64 or
+    128) with per-tensor dequantisation factors; returns O (bf16) and LSE (fp32)."""
     lib = library()
     for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
         _check_dev(name, t, torch.uint8)

@@ -405,8 +405,8 @@ int rowxent_bwd(const void* logits, const int* targets, const float* lse, const 
 }
 
 size_t attn_fwd_fp8_workspace_bytes(int B, int Hkv, int N, int d) {
-  if (B < 1 || Hkv < 1 || N < 1 || d != 128) return 0;
-  return round256(osattn::fp8_vt_bytes(B, Hkv, N));
+  if (B < 1 || Hkv < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  return round256(osattn::fp8_vt_bytes(B, Hkv, N, d));
 }
 
 int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -416,9 +416,9 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
   if (!q || !k || !v || !o || !lse || !workspace) return ATTN_ERR_NULL;
   int st = validate_sizes(B, H, Hkv, N, d, ATTN_BF16);  // output dtype
   if (st != ATTN_OK) return st;
-  if (d != 128) return ATTN_ERR_HEAD_DIM;
-  // V^T holds one head's 128 dims x N rounded up to 128 keys, with 32-bit offsets.
-  if ((long long)128 * (N + 127) >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  // (d in {64, 128} is checked by validate_sizes.)  V^T holds one head's d dims x N
+  // rounded up to 128 keys, with 32-bit offsets.
+  if ((long long)d * (N + 127) >= (1LL << 31)) return ATTN_ERR_SHAPE;
   if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
   st = validate_scale(scale);
   if (st == ATTN_OK) st = validate_scale(descale_q);
@@ -429,7 +429,7 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
       !aligned16(workspace))
     return ATTN_ERR_ALIGN;
   if (workspace_bytes < attn_fwd_fp8_workspace_bytes(B, Hkv, N, d)) return ATTN_ERR_WORKSPACE;
-  osattn::Fp8Args a{q, k, v, o, lse, B, H, Hkv, N, scale, descale_q, descale_k, descale_v,
+  osattn::Fp8Args a{q, k, v, o, lse, B, H, Hkv, N, d, scale, descale_q, descale_k, descale_v,
                     causal, workspace, stream};
   return osattn::launch_fwd_fp8(a) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

@@ -22,8 +22,8 @@
 //    small pass writes V transposed per (batch, kv head), keys of each 64-key
 //    block in the order the probabilities sit in the registers (see vt_key), so
 //    both operands of the O update are plain 16-byte LDS reads.
-// d = 128 only.  Layouts: Q, K, V codes [B][H or Hkv][N][128] bytes, O bf16
-// [B][H][N][128], LSE fp32 [B][H][N]; the workspace holds V^T, [B][Hkv][128][Np]
+// d = 64 or 128.  Layouts: Q, K, V codes [B][H or Hkv][N][d] bytes, O bf16
+// [B][H][N][d], LSE fp32 [B][H][N]; the workspace holds V^T, [B][Hkv][d][Np]
 // bytes with Np = N rounded up to 128 (padding keys are zero).
 #include <type_traits>
 
@@ -36,13 +36,19 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kD = 128;       // head dimension
 constexpr int kNW = 8;        // waves per workgroup (two per SIMD)
 constexpr int kBR = kNW * 32; // query rows per workgroup
 constexpr int kBC = 128;      // keys per tile
-constexpr int kRow = 128;     // bytes per LDS row (K: a key's 128 dims; V^T: 128 keys of a dim)
-constexpr int kTile = kBC * kRow;          // 16 KB
-constexpr int kCPW = kTile / 1024 / kNW;   // 1 KB LDS-DMA chunks per wave per tensor
+constexpr int kRowV = kBC;    // bytes per LDS row of V^T (the tile's 128 keys of one dim)
+
+// Tile geometry for head dimension D (64 or 128): K rows are D bytes, V^T rows 128.
+template <int D>
+struct Fp8Cfg {
+  static constexpr int kRowK = D;               // bytes per LDS row of K (a key's dims)
+  static constexpr int kTile = kBC * D;         // bytes per K tile and per V^T tile
+  static constexpr int kCPW = kTile / 1024 / kNW;  // 1 KB LDS-DMA chunks per wave per tensor
+  static_assert(kCPW >= 1 && kTile % (1024 * kNW) == 0, "tile must split over the waves");
+};
 
 // Key (within a 64-key block) of byte b of the P^T operand held by lane half h:
 // the S^T accumulator gives lane (row, h) keys 8g + 4h + e of each 32-key block in
@@ -51,26 +57,33 @@ __host__ __device__ constexpr int vt_key(int h, int b) {
   return 32 * (b / 16) + 8 * ((b % 16) / 4) + 4 * h + (b % 4);
 }
 
-// 16-byte granule swizzle of 128-byte LDS rows: conflict-free 128-bit reads by 32
-// lanes on 32 consecutive rows.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// 16-byte granule swizzle of LDS rows of 128 bytes (two rows per 256-byte bank
+// cycle) and of 64 bytes (four rows per cycle): consecutive rows reading the same
+// logical granule land on distinct banks, so 128-bit reads by 32 lanes on 32
+// consecutive rows are conflict-free.
+template <int ROW>
+__device__ __forceinline__ int swz(int row) {
+  return ROW == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
 
 // ---- V -> V^T with the block key order --------------------------------------------
-// One workgroup per (batch * kv head, 64-key block): the block's 64 x 128 bytes go
-// through LDS; thread t writes dim t / 2, block positions 32 * (t % 2) .. +31.
+// One workgroup per (batch * kv head, 64-key block): the block's 64 x D bytes go
+// through LDS; thread t < 2D writes dim t / 2, block positions 32 * (t % 2) .. +31.
+template <int D>
 __global__ __launch_bounds__(256) void vt_kernel(const uint8_t* __restrict__ V,
                                                  uint8_t* __restrict__ Vt, int N, int Np) {
-  __shared__ uint8_t tile[64][kD + 4];
+  constexpr int kQ = D / 32;  // threads per row, 32 bytes each
+  __shared__ uint8_t tile[64][D + 4];
   const int blk = blockIdx.x;
   const size_t bh = blockIdx.y;
   const int k0 = blk * 64;
   const int t = threadIdx.x;
-  // Load: thread t reads 32 bytes, row t / 4, bytes 32 * (t % 4) .. +31.
-  {
-    const int r = t / 4, c = 32 * (t % 4);
+  // Load: thread t reads 32 bytes, row t / kQ, bytes 32 * (t % kQ) .. +31.
+  if (t < 64 * kQ) {
+    const int r = t / kQ, c = 32 * (t % kQ);
     u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
     if (k0 + r < N) {
-      const u32x4* src = (const u32x4*)(V + (bh * N + k0 + r) * kD + c);
+      const u32x4* src = (const u32x4*)(V + (bh * N + k0 + r) * D + c);
       a = src[0];
       b = src[1];
     }
@@ -82,6 +95,7 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint8_t* __restrict__ V,
     }
   }
   __syncthreads();
+  if (t >= 2 * D) return;
   const int d = t / 2, h = t % 2;
   uint32_t w[8];
 #pragma unroll
@@ -91,7 +105,7 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint8_t* __restrict__ V,
     for (int e = 0; e < 4; ++e) v |= (uint32_t)tile[vt_key(h, 4 * j + e)][d] << (8 * e);
     w[j] = v;
   }
-  u32x4* out = (u32x4*)(Vt + (bh * kD + d) * Np + k0 + 32 * h);
+  u32x4* out = (u32x4*)(Vt + (bh * D + d) * Np + k0 + 32 * h);
   out[0] = u32x4{w[0], w[1], w[2], w[3]};
   out[1] = u32x4{w[4], w[5], w[6], w[7]};
 }
@@ -112,17 +126,22 @@ __device__ __forceinline__ i32x8 lds_read32(const char* p0, const char* p1) {
   return r;
 }
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                     const uint8_t* __restrict__ Vt, uint16_t* __restrict__ O,
                     float* __restrict__ LSE, int H, int Hkv, int N, int Np, int n_qtiles,
                     float c_log2, float dv) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lk0[kTile];
-  __shared__ __attribute__((aligned(1024))) uint8_t lv0[kTile];
-  __shared__ __attribute__((aligned(1024))) uint8_t lk1[kTile];
-  __shared__ __attribute__((aligned(1024))) uint8_t lv1[kTile];
+  using C = Fp8Cfg<D>;
+  constexpr int kD = D;
+  constexpr int kRowK = C::kRowK;
+  constexpr int kCPW = C::kCPW;
+  constexpr int kNC = D / 64;  // 64-dim chunks of the score contraction
+  __shared__ __attribute__((aligned(1024))) uint8_t lk0[C::kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv0[C::kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t lk1[C::kTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t lv1[C::kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -146,9 +165,9 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K
   const auto rv = make_rsrc(Vt + g * kD * Np, (uint32_t)kD * Np);
 
   // Q fragments (B operand of S^T = K Q^T): row l32, dims 64c + 32hi .. +31.
-  i32x8 qf[2];
+  i32x8 qf[kNC];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < kNC; ++c) {
     const uint32_t off = (uint32_t)(wrow0 + l32) * kD + 64 * c + 32 * hi;
     const u32x4 a = buffer_load16(rq, off), bb = buffer_load16(rq, off + 16);
 #pragma unroll
@@ -161,33 +180,38 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K
   int n_kt = (N + kBC - 1) / kBC;
   if (CAUSAL) n_kt = min(n_kt, (q0 + kBR + kBC - 1) / kBC);
 
-  // LDS-DMA: chunk ch of a tile is LDS bytes [ch * 1024, +1024) = rows 8ch .. 8ch+7;
-  // the lane's 16 bytes are physical granule pg of its row, logical pg ^ swz(row).
+  // LDS-DMA: chunk ch of a tile is LDS bytes [ch * 1024, +1024); the lane's 16 bytes
+  // are physical granule pg of its row, logical pg ^ swz(row).
   uint32_t goff_k[kCPW], goff_v[kCPW];
 #pragma unroll
   for (int i = 0; i < kCPW; ++i) {
     const int off = (wave * kCPW + i) * 1024 + lane * 16;
-    const int row = off / kRow;
-    const int lg = ((off % kRow) / 16) ^ swz(row);
-    goff_k[i] = row * kRow + lg * 16;        // + tile base (k0 * 128) in the scalar offset
-    goff_v[i] = row * Np + lg * 16;          // row = dim; + tile base (k0) in the scalar offset
+    const int rk_ = off / kRowK;  // key row of the K tile
+    goff_k[i] = rk_ * kRowK + (((off % kRowK) / 16) ^ swz<kRowK>(rk_)) * 16;  // + k0 * D (scalar)
+    const int rv_ = off / kRowV;  // dim row of the V^T tile
+    goff_v[i] = rv_ * Np + (((off % kRowV) / 16) ^ swz<kRowV>(rv_)) * 16;     // + k0 (scalar)
   }
   auto issue = [&](int kt, uint8_t* lk, uint8_t* lv) __attribute__((always_inline)) {
     const uint32_t k0 = (uint32_t)kt * kBC;
 #pragma unroll
     for (int i = 0; i < kCPW; ++i) {
       const int ch = wave * kCPW + i;
-      buffer_load16_lds(rk, lk + ch * 1024, goff_k[i], k0 * kRow);
+      buffer_load16_lds(rk, lk + ch * 1024, goff_k[i], k0 * kRowK);
       buffer_load16_lds(rv, lv + ch * 1024, goff_v[i], k0);
     }
   };
 
-  // LDS read offsets: row l32 of a 32-row block, logical granules 4c + 2hi, +1.
-  uint32_t aoff[2][2];
+  // LDS read offsets: row l32 of a 32-row block, logical granules 4c + 2hi, +1 (K:
+  // dims 64c + 32hi .. +31; V^T: keys 64m + 32hi .. +31).
+  uint32_t koff[kNC][2], voff[2][2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int j = 0; j < 2; ++j) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) aoff[c][j] = l32 * kRow + 16 * ((4 * c + 2 * hi + j) ^ swz(l32));
+    for (int c = 0; c < kNC; ++c)
+      koff[c][j] = l32 * kRowK + 16 * ((4 * c + 2 * hi + j) ^ swz<kRowK>(l32));
+#pragma unroll
+    for (int m = 0; m < 2; ++m) voff[m][j] = l32 * kRowV + 16 * ((4 * m + 2 * hi + j) ^ swz<kRowV>(l32));
+  }
 
   f32x16 acc[kD / 32], lacc;
 #pragma unroll
@@ -213,11 +237,11 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < kNC; ++c)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const char* base = kbase + kb * 32 * kRow;
-        s[kb] = mma8(lds_read32(base + aoff[c][0], base + aoff[c][1]), qf[c], s[kb]);
+        const char* base = kbase + kb * 32 * kRowK;
+        s[kb] = mma8(lds_read32(base + koff[c][0], base + koff[c][1]), qf[c], s[kb]);
       }
     const bool need_mask = (k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > wrow0);
     if (need_mask) {
@@ -271,8 +295,8 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K
     for (int m = 0; m < 2; ++m) {
 #pragma unroll
       for (int t = 0; t < kD / 32; ++t) {
-        const char* base = vbase + t * 32 * kRow;
-        acc[t] = mma8(lds_read32(base + aoff[m][0], base + aoff[m][1]), pf[m], acc[t]);
+        const char* base = vbase + t * 32 * kRowV;
+        acc[t] = mma8(lds_read32(base + voff[m][0], base + voff[m][1]), pf[m], acc[t]);
       }
       lacc = mma8(ones, pf[m], lacc);
     }
@@ -318,31 +342,40 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K
 
 }  // namespace
 
-size_t fp8_vt_bytes(int B, int Hkv, int N) {
+size_t fp8_vt_bytes(int B, int Hkv, int N, int d) {
   const size_t np = ((size_t)N + kBC - 1) / kBC * kBC;
-  return (size_t)B * Hkv * kD * np;
+  return (size_t)B * Hkv * d * np;
 }
 
-hipError_t launch_fwd_fp8(const Fp8Args& a) {
+namespace {
+
+template <int D>
+hipError_t launch_fp8_d(const Fp8Args& a) {
   const int np = (a.N + kBC - 1) / kBC * kBC;
-  hipLaunchKernelGGL(vt_kernel, dim3((unsigned)(np / 64), (unsigned)(a.B * a.Hkv)), dim3(256), 0,
-                     (hipStream_t)a.stream, (const uint8_t*)a.v, (uint8_t*)a.workspace, a.N, np);
+  hipLaunchKernelGGL(vt_kernel<D>, dim3((unsigned)(np / 64), (unsigned)(a.B * a.Hkv)), dim3(256),
+                     0, (hipStream_t)a.stream, (const uint8_t*)a.v, (uint8_t*)a.workspace, a.N, np);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qtiles = (a.N + kBR - 1) / kBR;
   const long long blocks = (long long)n_qtiles * a.B * a.H;
   const float c_log2 = a.scale * a.descale_q * a.descale_k * kLog2e;
   if (a.causal)
-    hipLaunchKernelGGL(fwd_fp8_kernel<true>, dim3((unsigned)blocks), dim3(kNW * 64), 0,
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, true>), dim3((unsigned)blocks), dim3(kNW * 64), 0,
                        (hipStream_t)a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k,
                        (const uint8_t*)a.workspace, (uint16_t*)a.o, a.lse, a.H, a.Hkv, a.N, np,
                        n_qtiles, c_log2, a.descale_v);
   else
-    hipLaunchKernelGGL(fwd_fp8_kernel<false>, dim3((unsigned)blocks), dim3(kNW * 64), 0,
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, false>), dim3((unsigned)blocks), dim3(kNW * 64), 0,
                        (hipStream_t)a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k,
                        (const uint8_t*)a.workspace, (uint16_t*)a.o, a.lse, a.H, a.Hkv, a.N, np,
                        n_qtiles, c_log2, a.descale_v);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8Args& a) {
+  return a.d == 64 ? launch_fp8_d<64>(a) : launch_fp8_d<128>(a);
 }
 
 }  // namespace osattn

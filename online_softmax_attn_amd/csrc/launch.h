@@ -85,21 +85,21 @@ constexpr int kStageDq = 2;
 
 hipError_t launch_fwd_mfma(const FwdArgs& a);
 
-// fp8 (e4m3) forward, d = 128: codes q [B][H][N][128], k, v [B][Hkv][N][128];
-// o bf16, lse fp32; workspace >= fp8_vt_bytes(B, Hkv, N) bytes (V transposed).
+// fp8 (e4m3) forward, d = 64 or 128: codes q [B][H][N][d], k, v [B][Hkv][N][d];
+// o bf16, lse fp32; workspace >= fp8_vt_bytes(B, Hkv, N, d) bytes (V transposed).
 struct Fp8Args {
   const void* q;
   const void* k;
   const void* v;
   void* o;
   float* lse;
-  int B, H, Hkv, N;
+  int B, H, Hkv, N, d;
   float scale, descale_q, descale_k, descale_v;
   int causal;
   void* workspace;
   void* stream;
 };
-size_t fp8_vt_bytes(int B, int Hkv, int N);
+size_t fp8_vt_bytes(int B, int Hkv, int N, int d);
 hipError_t launch_fwd_fp8(const Fp8Args& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_preprocess(const BwdArgs& a);

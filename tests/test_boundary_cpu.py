@@ -394,8 +394,8 @@ FP8_INVALID = [
     ({"ws": None}, "ATTN_ERR_NULL"),
     ({"N": 0}, "ATTN_ERR_SHAPE"),
     ({"B": 0}, "ATTN_ERR_SHAPE"),
-    ({"d": 64}, "ATTN_ERR_HEAD_DIM"),
     ({"d": 96}, "ATTN_ERR_HEAD_DIM"),
+    ({"d": 32}, "ATTN_ERR_HEAD_DIM"),
     ({"H": 3, "Hkv": 2}, "ATTN_ERR_GQA"),
     ({"causal": 2}, "ATTN_ERR_SHAPE"),
     ({"scale": 0.0}, "ATTN_ERR_SCALE"),
@@ -415,8 +415,10 @@ def test_fp8_rejects(kw, code):
 
 def test_fp8_workspace_bytes():
     lib = osa.library()
-    # V transposed: B * Hkv * 128 dims * N rounded up to 128 keys, rounded to 256 bytes.
+    # V transposed: B * Hkv * d dims * N rounded up to 128 keys, rounded to 256 bytes.
     assert lib.attn_fwd_fp8_workspace_bytes(2, 3, 100, 128) == 2 * 3 * 128 * 128
     assert lib.attn_fwd_fp8_workspace_bytes(1, 1, 129, 128) == 128 * 256
-    assert lib.attn_fwd_fp8_workspace_bytes(1, 1, 100, 64) == 0
+    assert lib.attn_fwd_fp8_workspace_bytes(1, 1, 100, 64) == 64 * 128
+    assert lib.attn_fwd_fp8_workspace_bytes(1, 1, 100, 96) == 0
+    assert lib.attn_fwd_fp8_workspace_bytes(0, 1, 100, 128) == 0
     assert osa.attn_fwd_fp8_workspace_bytes(4, 16, 8192) == 4 * 16 * 128 * 8192

@@ -80,44 +80,47 @@ def bound_check(inp, causal, scale, o, lse, label, heads=None, rows=None, block=
     assert worst_o <= 0 and worst_l <= 0, (label, worst_o, worst_l)
 
 
-def case(B, H, Hkv, N, causal, seed):
-    w = S.custom("bf16", B, H, Hkv, N, 128, causal, seed_base=seed)
+def case(B, H, Hkv, N, causal, seed, d=128):
+    w = S.custom("bf16", B, H, Hkv, N, d, causal, seed_base=seed)
     return w, S.make_fp8_inputs(w)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(1, 2, 1, 1), (1, 2, 2, 77), (2, 4, 2, 300), (1, 4, 1, 1000),
                                    (1, 2, 1, 256)],
                          ids=lambda s: "B{}H{}Hkv{}N{}".format(*s))
-def test_fp8_forward(shape, causal):
+def test_fp8_forward(shape, causal, d):
     need_gpu()
     B, H, Hkv, N = shape
-    w, inp = case(B, H, Hkv, N, causal, 31000 + N)
+    w, inp = case(B, H, Hkv, N, causal, 31000 + N + d, d)
     o, lse = run_fp8(inp, causal, w.scale)
-    bound_check(inp, causal, w.scale, o, lse, f"B{B}H{H}Hkv{Hkv}N{N} causal={causal}")
+    bound_check(inp, causal, w.scale, o, lse, f"B{B}H{H}Hkv{Hkv}N{N}d{d} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_equal_value_rows(causal):
+def test_fp8_equal_value_rows(causal, d):
     """Every row of V the same vector: O is that vector whatever the weights."""
     need_gpu()
-    w, inp = case(1, 2, 1, 333, causal, 32000)
+    w, inp = case(1, 2, 1, 333, causal, 32000 + d, d)
     v8 = inp["v8"].clone()
     v8[:] = v8[:, :, :1, :]
     inp["v8"] = v8.contiguous()
     o, _ = run_fp8(inp, causal, w.scale)
     v = F8.dequantize(inp["v8"], inp["dv"])[0, 0, 0]
     err = np.abs(o - v[None, None, None, :]) - (2.0 ** -8 * np.abs(v) + 1e-6)
-    say(f"[fp8] equal V rows causal={causal}: worst excess {err.max():.2e}")
+    say(f"[fp8] equal V rows d={d} causal={causal}: worst excess {err.max():.2e}")
     assert err.max() <= 0
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_zero_query(causal):
+def test_fp8_zero_query(causal, d):
     """Q = 0: every visible key has weight exactly 1 (256 in e4m3 is exact), so O is
     the mean (the prefix mean when causal) of V and LSE = ln(number of keys)."""
     need_gpu()
-    w, inp = case(1, 2, 1, 200, causal, 33000)
+    w, inp = case(1, 2, 1, 200, causal, 33000 + d, d)
     inp["q8"] = torch.zeros_like(inp["q8"])
     o, lse = run_fp8(inp, causal, w.scale)
     v = F8.dequantize(inp["v8"], inp["dv"])[0, 0]
@@ -125,7 +128,7 @@ def test_fp8_zero_query(causal):
     mean = (np.cumsum(v, 0) / n[:, None]) if causal else np.broadcast_to(v.mean(0), v.shape)
     err_o = np.abs(o[0] - mean[None]) - (2.0 ** -8 * np.abs(mean[None]) + 1e-5 * np.abs(v).max())
     err_l = np.abs(lse[0] - np.log(n)[None]) - 1e-5 * (1 + np.log(n)[None])
-    say(f"[fp8] Q=0 causal={causal}: worst excess O {err_o.max():.2e} LSE {err_l.max():.2e}")
+    say(f"[fp8] Q=0 d={d} causal={causal}: worst excess O {err_o.max():.2e} LSE {err_l.max():.2e}")
     assert err_o.max() <= 0 and err_l.max() <= 0
 
 
