@@ -925,16 +925,21 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         s = M::mma32(as_vec8<T>(ak), qf[c], s);
         dp = M::mma32(as_vec8<T>(av), df[c], dp);
       }
+      // Masked scores become -inf (P = 0, so dS = 0) in a branch of their own: folded
+      // into the loop below, the compiler would evaluate the key tests as selects on
+      // every tile, needed or not.
+      if (need_mask) {
+        asm volatile("");  // keep this a branch
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= Nk || (CAUSAL && key > row) || (IMASK && (key < lo_r || key > hi_r)))
+            s[r] = -INFINITY;
+        }
+      }
       float dsv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(fmaf(s[r], scale_log2, -lse2));
-        if (need_mask) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= Nk || (CAUSAL && key > row) || (IMASK && (key < lo_r || key > hi_r))) pv = 0.f;
-        }
-        dsv[r] = pv * (dp[r] - drow);
-      }
+      for (int r = 0; r < 16; ++r) dsv[r] = fast_exp2(fmaf(s[r], scale_log2, -lse2)) * (dp[r] - drow);
       // dQ^T += K^T dS^T (reduction over the 32 keys of this block, 16 at a time)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
