@@ -10,7 +10,8 @@
 //     key/value head times the Nq queries (grouped-query decoding reads each K/V
 //     chunk once for the whole group); in memory these rows are contiguous,
 //     [h_local][i].  Each wave walks the chunk of keys in 32-key tiles with the FlashAttention-2 online softmax
-//     (FlashAttention-2 page, inner loop steps 1-5, exact running max per tile)
+//     (FlashAttention-2 page, inner loop steps 1-5; the running max is a reference
+//     that moves only when a tile's max exceeds it by more than 8 in log2 units)
 //     and writes the chunk's normalised output O_s = Ot / l and LSE_s = m + ln l
 //     in fp32 (LSE_s = -inf and O_s = 0 for rows that see no key of the chunk).
 //  2. splitkv_merge_kernel: one wave per query row combines the chunks,
@@ -166,36 +167,44 @@ void splitkv_partial_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
       s = M::mma32(as_vec8<T>(a), qf[c], s);
     }
     const bool need_mask = (k0 + kSplitTile > ke) || (CAUSAL && k0 + kSplitTile - 1 > Nk - Nq);
-    float x[16];
+    if (need_mask) {
+      asm volatile("");  // a branch: the key tests run only on tiles that need them
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      x[e] = s[e] * scale_log2;
-      if (need_mask) {
+      for (int e = 0; e < 16; ++e) {
         const int key = k0 + 8 * (e >> 2) + 4 * hi + (e & 3);
-        if (key >= ke || (CAUSAL && key > lim)) x[e] = -INFINITY;
+        if (key >= ke || (CAUSAL && key > lim)) s[e] = -INFINITY;
       }
     }
-    float mx = x[0];
+    // The tile's row max (log2 units).  The reference m moves to it (with the rescale
+    // of Ot and l by exp2(m_old - m_new)) only when it exceeds m by more than 8: then
+    // P <= 2^8, well inside the range of the rounded P and of l, and most tiles skip
+    // the rescale of the accumulators.  Ot / l does not depend on the reference.
+    float mx = s[0];
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
-    const float m_new = fmaxf(m_run, wave_xor32_max(mx));
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+    const float m_tile = wave_xor32_max(mx) * scale_log2;
+    if (__any(m_tile > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < D / 32; ++tt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[tt][e] *= alpha;
+    }
+    const float neg_m = -m_run;
     vec8 pf[2];
     float part = 0.f;
 #pragma unroll
     for (int c4 = 0; c4 < 2; ++c4) {
       float p[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = fast_exp2(x[8 * c4 + j] - m_new);
+      for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(s[8 * c4 + j], scale_log2, neg_m));
       pf[c4] = pack8<T>(p);
       part = sum8<T>(pf[c4], part);
     }
-    l_run = l_run * alpha + part;
-#pragma unroll
-    for (int tt = 0; tt < D / 32; ++tt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[tt][e] *= alpha;
+    l_run += part;
 #pragma unroll
     for (int c4 = 0; c4 < 2; ++c4)
 #pragma unroll
