@@ -3,8 +3,10 @@ as the fixed cases: lengths drawn around the tile edges (1, 31-33, 63-65, 127-12
 255-257, ... and arbitrary), GQA ratios 1-8, both head dims, all dtypes, causal or not,
 softmax scales from a quarter to four times 1/sqrt(d), query magnitudes up to 4 (large
 score ranges exercise the moves of the running reference max) and key outliers.  The
-split-KV forward gets its own draws of query and key counts and chunkings.  The case
-list is fixed by the seed, so a failure names a reproducible case."""
+split-KV forward gets its own draws of query and key counts and chunkings, the
+interval-masked forward and backward draws of mask kinds and query/key counts, and the
+fp8 forward draws of shapes, head dims and scales (against its derived bound).  The case
+lists are fixed by the seeds, so a failure names a reproducible case."""
 
 import numpy as np
 import pytest
@@ -79,3 +81,64 @@ def test_random_splitkv(c):
     w = S.custom(c["dtype"], c["B"], c["H"], c["Hkv"], c["Nq"], c["d"], c["causal"],
                  seed_base=70000 + 100 * c["idx"], Nk=c["Nk"])
     check_split(w, n_splits=c["n_splits"])
+
+
+def _draw_masked(n, seed):
+    r = np.random.default_rng(seed)
+    kinds = [("random", lambda: {"empty_frac": float(r.choice([0.0, 0.1, 0.3]))}),
+             ("sliding", lambda: {"left": int(r.integers(0, 300)), "right": int(r.integers(0, 50)),
+                                  "causal": bool(r.random() < 0.5)}),
+             ("prefix", lambda: {"prefix": int(r.integers(1, 400))}),
+             ("causal", lambda: {})]
+    out = []
+    for i in range(n):
+        Hkv = int(r.choice([1, 2]))
+        n_rep = int(r.choice([1, 2, 4]))
+        Nk = int(r.choice(EDGES)) if r.random() < 0.5 else int(r.integers(1, 600))
+        Nq = Nk if r.random() < 0.5 else int(r.integers(1, Nk + 1))
+        kind, mk = kinds[int(r.integers(0, len(kinds)))]
+        out.append(dict(idx=i, dtype=str(r.choice(["fp32", "fp16", "bf16"])), B=int(r.integers(1, 3)),
+                        H=Hkv * n_rep, Hkv=Hkv, Nq=Nq, Nk=Nk, d=int(r.choice([64, 128])), kind=kind,
+                        mk=mk()))
+    return out
+
+
+MASKED_CASES = _draw_masked(16, 20261204)
+
+
+@pytest.mark.parametrize("c", MASKED_CASES, ids=lambda c: (
+    f"{c['idx']}-{c['dtype']}-{c['kind']}-B{c['B']}H{c['H']}Hkv{c['Hkv']}Nq{c['Nq']}Nk{c['Nk']}d{c['d']}"))
+def test_random_masked_fwd_bwd(c):
+    need_gpu()
+    from test_gpu_masked import check_masked_bwd
+    check_masked_bwd(c["dtype"], c["B"], c["H"], c["Hkv"], c["Nq"], c["Nk"], c["d"], c["kind"],
+                     80000 + 100 * c["idx"], **c["mk"])
+
+
+def _draw_fp8(n, seed):
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(r.choice([1, 2]))
+        out.append(dict(idx=i, B=int(r.integers(1, 3)), H=Hkv * int(r.choice([1, 2, 4])), Hkv=Hkv,
+                        N=int(r.choice(EDGES)) if r.random() < 0.6 else int(r.integers(1, 700)),
+                        d=int(r.choice([64, 128])), causal=bool(r.random() < 0.5),
+                        scale_mult=float(2.0 ** r.uniform(-1, 1))))
+    return out
+
+
+FP8_CASES = _draw_fp8(12, 20261205)
+
+
+@pytest.mark.parametrize("c", FP8_CASES, ids=lambda c: (
+    f"{c['idx']}-B{c['B']}H{c['H']}Hkv{c['Hkv']}N{c['N']}d{c['d']}{'-c' if c['causal'] else ''}"
+    f"-s{c['scale_mult']:.2f}"))
+def test_random_fp8(c):
+    need_gpu()
+    from test_gpu_fp8 import bound_check, run_fp8
+    w = S.custom("bf16", c["B"], c["H"], c["Hkv"], c["N"], c["d"], c["causal"],
+                 seed_base=90000 + 100 * c["idx"])
+    inp = S.make_fp8_inputs(w)
+    scale = w.scale * c["scale_mult"]
+    o, lse = run_fp8(inp, c["causal"], scale)
+    bound_check(inp, c["causal"], scale, o, lse, f"random fp8 {c['idx']}")
