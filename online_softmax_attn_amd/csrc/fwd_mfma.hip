@@ -265,16 +265,21 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const bool need_mask = (k0 + C::kBC > Nk) || (CAUSAL && k0 + C::kBC - 1 > wrow0) ||
                            (MASK && !(k0 >= w_maxlo && k0 + C::kBC - 1 <= w_minhi));
     if (need_mask) {
+      // Element r of block kb holds key k0 + 4*hi + ko, ko a compile-time constant:
+      // each test compares that constant with a limit taken once per tile.
+      const int base = k0 + 4 * hi;
+      const int lim_n = Nk - base;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int row = wrow0 + 32 * qb + l32;
+        const int lim_c = wrow0 + 32 * qb + l32 - base;
+        const int lim_lo = MASK ? lo_r[qb] - base : 0;
+        const int lim_hi = MASK ? min(hi_r[qb] - base, lim_n - 1) : lim_n - 1;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= Nk || (CAUSAL && key > row) ||
-                (MASK && (key < lo_r[qb] || key > hi_r[qb])))
+            const int ko = kb * 32 + 8 * (r >> 2) + (r & 3);
+            if ((CAUSAL && ko > lim_c) || (MASK && ko < lim_lo) || ko > lim_hi)
               s[qb][kb][r] = -INFINITY;
           }
       }
