@@ -930,11 +930,16 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       // every tile, needed or not.
       if (need_mask) {
         asm volatile("");  // keep this a branch
+        // Key of element r: base + ko with ko a compile-time constant; the limits are
+        // taken relative to base once per block.
+        const int base = k0 + kb * 32 + 4 * hi;
+        const int lim_hi = IMASK ? min(hi_r - base, Nk - 1 - base) : Nk - 1 - base;
+        const int lim_lo = IMASK ? lo_r - base : 0;
+        const int lim_c = row - base;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= Nk || (CAUSAL && key > row) || (IMASK && (key < lo_r || key > hi_r)))
-            s[r] = -INFINITY;
+          const int ko = 8 * (r >> 2) + (r & 3);
+          if (ko > lim_hi || (CAUSAL && ko > lim_c) || (IMASK && ko < lim_lo)) s[r] = -INFINITY;
         }
       }
       float dsv[16];

@@ -246,13 +246,15 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K
     const bool need_mask = (k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > wrow0);
     if (need_mask) {
       asm volatile("");  // keep this a branch
-      const int row = wrow0 + l32;
+      // Key of element r of block kb: base + ko with ko a compile-time constant.
+      const int base = k0 + 4 * hi;
+      const int lim_n = N - 1 - base, lim_c = wrow0 + l32 - base;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= N || (CAUSAL && key > row)) s[kb][r] = -INFINITY;
+          const int ko = kb * 32 + 8 * (r >> 2) + (r & 3);
+          if (ko > lim_n || (CAUSAL && ko > lim_c)) s[kb][r] = -INFINITY;
         }
     }
     // The tile's row max (log2 units of the scaled scores) against the reference.
