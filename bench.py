@@ -253,8 +253,8 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
-              "the path shards over heads with no communication, see DESIGN.md", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (--gpus {args.gpus} requested); the path would "
+              "shard over (batch, kv-head group) pairs with no communication", file=sys.stderr)
         sys.exit(2)
 
     import torch
