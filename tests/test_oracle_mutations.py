@@ -10,6 +10,7 @@ import pytest
 
 import oracle.attention as A
 import oracle.fp8 as F8
+import oracle.online_walk as W
 import oracle.rowsoftmax as RS
 import oracle_pins as P
 
@@ -204,3 +205,63 @@ def test_mutant_is_caught(mutant, monkeypatch):
         monkeypatch.setattr(A, target, repl)
     failed = _failing_pins()
     assert failed, f"no pin caught mutant {mutant}"
+
+
+# Mistakes in the tiled walk's update (steps 4 and 5 and the final normalisation):
+# each mutant is the walk with one step changed.
+def _walk_mutant(kind):
+    def walk(q, k, v, block_rows, block_cols, scale=1.0, causal=False, trace=False):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        n, d = q.shape
+        o, lse, steps = np.empty_like(q), np.empty(n), []
+        for i in range(-(-n // block_rows)):
+            rows = np.arange(i * block_rows, min(n, (i + 1) * block_rows))
+            m, l, ot = np.full(len(rows), -np.inf), np.zeros(len(rows)), np.zeros((len(rows), d))
+            for j in range(-(-k.shape[0] // block_cols)):
+                cols = np.arange(j * block_cols, min(k.shape[0], (j + 1) * block_cols))
+                s_ij = scale * (q[rows] @ k[cols].T)
+                if causal:
+                    s_ij = np.where(cols[None, :] > rows[:, None], -np.inf, s_ij)
+                m_ij = np.max(s_ij, axis=1)
+                live = np.isfinite(m_ij)
+                pt = np.zeros_like(s_ij)
+                pt[live] = np.exp(s_ij[live] - m_ij[live, None])
+                l_ij = pt.sum(axis=1)
+                m_new = np.maximum(m, m_ij)
+                alpha = W._exp_diff(m, m_new)
+                beta = W._exp_diff(m_ij, m_new)
+                if kind == "no_alpha_on_ot":
+                    ot = ot + beta[:, None] * (pt @ v[cols])
+                    l = alpha * l + beta * l_ij
+                elif kind == "no_beta":
+                    ot = alpha[:, None] * ot + pt @ v[cols]
+                    l = alpha * l + l_ij
+                elif kind == "alpha_inverted":
+                    inv = np.where(np.isfinite(m), np.exp(m_new - np.where(np.isfinite(m), m, 0)), 0.0)
+                    ot = inv[:, None] * ot + beta[:, None] * (pt @ v[cols])
+                    l = inv * l + beta * l_ij
+                else:
+                    ot = alpha[:, None] * ot + beta[:, None] * (pt @ v[cols])
+                    l = alpha * l + beta * l_ij
+                m = m_new
+                if trace:
+                    steps.append({"i": i, "j": j, "m": m.copy(), "l": l.copy(), "Ot": ot.copy()})
+            o[rows] = ot / l[:, None]
+            lse[rows] = np.log(l) if kind == "lse_drops_max" else m + np.log(l)
+        return (o, lse, steps) if trace else (o, lse)
+    return walk
+
+
+WALK_MUTANTS = ["no_alpha_on_ot", "no_beta", "alpha_inverted", "lse_drops_max"]
+
+
+def test_walk_mutant_harness_is_the_walk(monkeypatch):
+    """With no step changed, the test's copy of the walk passes every pin."""
+    monkeypatch.setattr(W, "tiled_forward", _walk_mutant(None))
+    assert _failing_pins() == []
+
+
+@pytest.mark.parametrize("mutant", WALK_MUTANTS)
+def test_walk_mutant_is_caught(mutant, monkeypatch):
+    monkeypatch.setattr(W, "tiled_forward", _walk_mutant(mutant))
+    assert _failing_pins(), f"no pin caught mutant {mutant}"
