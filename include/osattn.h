@@ -170,8 +170,10 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
  * attn_fwd_splitkv_workspace_bytes() for the same arguments (fp32 chunk
  * outputs and logsumexps); its contents on entry do not matter.  Calls that may
  * overlap in time need distinct workspaces.  Returns ATTN_OK or a negative
- * attn_status_t (ATTN_ERR_SHAPE also for n_splits < 0 and causal with Nk < Nq);
- * on a validation error nothing is launched.
+ * attn_status_t (ATTN_ERR_SHAPE also for n_splits < 0, causal with Nk < Nq, and
+ * B * H * Nq of 2^26 rows or more, or chunkings whose launch would count 2^32
+ * work-items or more; the workspace query returns 0 for those); on a validation
+ * error nothing is launched.
  */
 size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d,
                                         int causal, int dtype, int n_splits);

@@ -245,6 +245,16 @@ int validate_split(int B, int H, int Hkv, int Nq, int Nk, int d, int causal, int
   return ATTN_OK;
 }
 
+// Both launches count their work-items in 32 bits: the chunk kernel runs
+// B * Hkv * n_splits row blocks of up to four waves, the merge one wave per row.
+bool split_grid_fits(int B, int H, int Hkv, int Nq, const SplitPlan& p) {
+  const int rows = (H / Hkv) * Nq;
+  const int nw = osattn::splitkv_waves(rows);
+  const long long n_rb = (rows + 32LL * nw - 1) / (32LL * nw);
+  return (long long)B * Hkv * p.n_splits * n_rb * nw * 64 < (1LL << 32) &&
+         (long long)B * H * Nq * 64 < (1LL << 32);
+}
+
 size_t split_workspace(int B, int H, int Nq, int d, const SplitPlan& p) {
   const size_t rows = (size_t)B * H * Nq;
   return round256((size_t)p.n_splits * rows * d * sizeof(float)) +
@@ -256,7 +266,9 @@ size_t split_workspace(int B, int H, int Nq, int d, const SplitPlan& p) {
 size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d,
                                         int causal, int dtype, int n_splits) {
   if (validate_split(B, H, Hkv, Nq, Nk, d, causal, dtype, n_splits) != ATTN_OK) return 0;
-  return split_workspace(B, H, Nq, d, split_plan(B, Hkv, H / Hkv, Nq, Nk, d, n_splits));
+  const SplitPlan p = split_plan(B, Hkv, H / Hkv, Nq, Nk, d, n_splits);
+  if (!split_grid_fits(B, H, Hkv, Nq, p)) return 0;
+  return split_workspace(B, H, Nq, d, p);
 }
 
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -268,6 +280,7 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   st = validate_scale(scale);
   if (st != ATTN_OK) return st;
   const SplitPlan p = split_plan(B, Hkv, H / Hkv, Nq, Nk, d, n_splits);
+  if (!split_grid_fits(B, H, Hkv, Nq, p)) return ATTN_ERR_SHAPE;
   if (!workspace || workspace_bytes < split_workspace(B, H, Nq, d, p)) return ATTN_ERR_WORKSPACE;
   if (!aligned_all({q, k, v, o, lse, workspace})) return ATTN_ERR_ALIGN;
   const size_t rows = (size_t)B * H * Nq;

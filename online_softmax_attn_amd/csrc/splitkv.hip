@@ -15,7 +15,7 @@
 //     and writes the chunk's normalised output O_s = Ot / l and LSE_s = m + ln l
 //     in fp32 (LSE_s = -inf and O_s = 0 for rows that see no key of the chunk).
 //  2. splitkv_merge_kernel: one wave per query row combines the chunks,
-//     LSE = ln sum_s exp(LSE_s) taken about the max, O = sum_s exp(LSE_s - LSE) O_s
+//     LSE = ln sum_s exp(LSE_s) taken about a running max, O = sum_s exp(LSE_s - LSE) O_s
 //     (the exact rescale-to-a-common-max merge of the ml-notes page and of
 //     "Phase 2" on the attnres-kernel-lab page), and writes O in the I/O dtype.
 //
@@ -282,73 +282,84 @@ void splitkv_partial_kernel(const uint16_t* __restrict__ Q, const uint16_t* __re
   }
 }
 
-// One wave per query row: merge the n_splits chunk results of that row.  The
-// chunk logsumexps are read one per lane (64 at a time) and reduced across the
-// wave; the weighted sum of the chunk outputs then streams over the chunks with
-// the weight broadcast from the lane that holds it, four chunks per iteration so
-// that their loads are in flight together.
+// One wave per query row: merge the n_splits chunk results of that row.  A chunk's
+// output row is D fp32 values, read as 16-byte pieces by D/4 lanes, so a wave reads
+// 64/(D/4) chunks side by side (lane group g takes chunks g, g + G, g + 2G, ...).
+// Every lane keeps its own online-softmax state over the chunks it reads: the max
+// m of their logsumexps, the weight sum z and the weighted sum o, each rescaled by
+// exp(m_old - m_new) when m moves (the FlashAttention-2 page's running statistics,
+// applied to chunk results).  Batches of eight chunks per lane are loaded before any
+// of them is used, so a row with up to 8G chunks costs one memory round trip; the
+// lane groups are then brought to the common max and summed across the wave.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restrict__ Opart,
-                                                            const float* __restrict__ Lpart,
-                                                            uint16_t* __restrict__ O,
-                                                            float* __restrict__ LSE,
-                                                            long long rows, int n_splits) {
-  constexpr int kCols = D / 64;  // columns per lane
-  const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+__global__ __launch_bounds__(64) void splitkv_merge_kernel(const float* __restrict__ Opart,
+                                                           const float* __restrict__ Lpart,
+                                                           uint16_t* __restrict__ O,
+                                                           float* __restrict__ LSE,
+                                                           long long rows, int n_splits) {
+  constexpr int kLanes = D / 4;        // lanes per chunk row (float4 each)
+  constexpr int kGroups = 64 / kLanes;  // chunks read side by side
+  constexpr int kBatch = 8;            // chunks per lane in flight
+  const int lane = threadIdx.x;
+  const int g = lane / kLanes;
+  const int cl = lane % kLanes;
+  const long long row = blockIdx.x;
   if (row >= rows) return;
-  // Pass 1: max and sum of exp over the chunk logsumexps.
-  float m = -INFINITY;
-  for (int s0 = 0; s0 < n_splits; s0 += 64) {
-    const int s = s0 + lane;
-    const float ls = s < n_splits ? Lpart[(long long)s * rows + row] : -INFINITY;
-    m = fmaxf(m, ls);
-  }
+  const long long stride = rows * D;  // floats between chunks of one row
+  const float* obase = Opart + row * D + 4 * cl;
+  float m = -INFINITY, z = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = g; s0 < n_splits; s0 += kGroups * kBatch) {
+    float4 v[kBatch];
+    float ls[kBatch];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  float o[kCols];
-#pragma unroll
-  for (int c = 0; c < kCols; ++c) o[c] = 0.f;
-  float z = 0.f;
-  if (m > -INFINITY) {
-    for (int s0 = 0; s0 < n_splits; s0 += 64) {
-      const int s = s0 + lane;
-      const float ls = s < n_splits ? Lpart[(long long)s * rows + row] : -INFINITY;
-      const float w_lane = ls > -INFINITY ? __expf(ls - m) : 0.f;
-      float zl = w_lane;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) zl += __shfl_xor(zl, off);
-      z += zl;
-      // Pass 2 over these (up to 64) chunks.
-      const int cnt = min(64, n_splits - s0);
-      const float* base = Opart + ((long long)s0 * rows + row) * D + kCols * lane;
-      const long long stride = rows * D;
-      int j = 0;
-      for (; j + 4 <= cnt; j += 4) {
-        float v[4][kCols];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int c = 0; c < kCols; ++c) v[u][c] = base[(j + u) * stride + c];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float w = __shfl(w_lane, j + u);
-#pragma unroll
-          for (int c = 0; c < kCols; ++c) o[c] = fmaf(w, v[u][c], o[c]);
-        }
-      }
-      for (; j < cnt; ++j) {
-        const float w = __shfl(w_lane, j);
-#pragma unroll
-        for (int c = 0; c < kCols; ++c) o[c] = fmaf(w, base[j * stride + c], o[c]);
+    for (int u = 0; u < kBatch; ++u) {
+      const int s = s0 + u * kGroups;
+      if (s < n_splits) {
+        v[u] = *reinterpret_cast<const float4*>(obase + s * stride);
+        ls[u] = Lpart[(long long)s * rows + row];
+      } else {
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        ls[u] = -INFINITY;
       }
     }
-  }
-  const float inv = z > 0.f ? 1.0f / z : 0.f;
-  uint16_t* out = O + row * D + kCols * lane;
+    float bm = ls[0];
 #pragma unroll
-  for (int c = 0; c < kCols; ++c) out[c] = to_bits<T>(o[c] * inv);
-  if (lane == 0) LSE[row] = z > 0.f ? m + __logf(z) : -INFINITY;
+    for (int u = 1; u < kBatch; ++u) bm = fmaxf(bm, ls[u]);
+    if (bm > m) {
+      const float c = m > -INFINITY ? __expf(m - bm) : 0.f;
+      o.x *= c; o.y *= c; o.z *= c; o.w *= c;
+      z *= c;
+      m = bm;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = ls[u] > -INFINITY ? __expf(ls[u] - m) : 0.f;
+      o.x = fmaf(w, v[u].x, o.x); o.y = fmaf(w, v[u].y, o.y);
+      o.z = fmaf(w, v[u].z, o.z); o.w = fmaf(w, v[u].w, o.w);
+      z += w;
+    }
+  }
+  // Bring the lane groups to the common max, then sum them.
+  float mall = m;
+#pragma unroll
+  for (int off = kLanes; off < 64; off <<= 1) mall = fmaxf(mall, __shfl_xor(mall, off));
+  const float c = m > -INFINITY ? __expf(m - mall) : 0.f;
+  o.x *= c; o.y *= c; o.z *= c; o.w *= c;
+  z *= c;
+#pragma unroll
+  for (int off = kLanes; off < 64; off <<= 1) {
+    o.x += __shfl_xor(o.x, off); o.y += __shfl_xor(o.y, off);
+    o.z += __shfl_xor(o.z, off); o.w += __shfl_xor(o.w, off);
+    z += __shfl_xor(z, off);
+  }
+  if (g == 0) {
+    const float inv = z > 0.f ? 1.0f / z : 0.f;
+    const uint32_t lo = (uint32_t)to_bits<T>(o.x * inv) | ((uint32_t)to_bits<T>(o.y * inv) << 16);
+    const uint32_t hi2 = (uint32_t)to_bits<T>(o.z * inv) | ((uint32_t)to_bits<T>(o.w * inv) << 16);
+    *reinterpret_cast<uint2*>(O + row * D + 4 * cl) = make_uint2(lo, hi2);
+  }
+  if (lane == 0) LSE[row] = z > 0.f ? mall + __logf(z) : -INFINITY;
 }
 
 template <typename T, int D, int NW, bool CAUSAL>
@@ -363,7 +374,7 @@ hipError_t splitkv_t(const SplitArgs& a) {
                      a.Nq, a.Nk, n_rb, a.n_splits, a.split_keys, rows, a.scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((splitkv_merge_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+  hipLaunchKernelGGL((splitkv_merge_kernel<T, D>), dim3((unsigned)rows), dim3(64), 0,
                      (hipStream_t)a.stream, a.o_part, a.lse_part, (uint16_t*)a.o, a.lse, rows,
                      a.n_splits);
   return hipGetLastError();

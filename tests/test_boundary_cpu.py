@@ -220,6 +220,9 @@ def split(**kw):
     ({"ws_bytes": 64}, "ATTN_ERR_WORKSPACE"),
     ({"o": P + 8}, "ATTN_ERR_ALIGN"),
     ({"ws": P + 4}, "ATTN_ERR_ALIGN"),
+    # Over 2^26 query rows: the merge's one wave per row would count 2^32 work-items.
+    ({"B": 9, "H": 1, "Hkv": 1, "Nq": (1 << 23) - 1, "Nk": 1000, "d": 64, "causal": 0,
+      "n_splits": 1, "ws_bytes": 1 << 62}, "ATTN_ERR_SHAPE"),
 ], ids=lambda x: str(x))
 def test_splitkv_rejects(kw, code):
     assert split(**kw) == S[code]
@@ -238,6 +241,9 @@ def test_splitkv_workspace_bytes():
     assert f(1, 4, 2, 1, 100, 128, 1, 0, 0) == 0       # fp32 has no split-KV kernel
     assert f(1, 4, 2, 200, 100, 128, 1, 2, 0) == 0     # causal with Nq > Nk
     assert f(1, 4, 2, 1, 100, 128, 0, 2, -2) == 0
+    # The largest row count whose merge grid fits, and the first that does not.
+    assert f(8, 1, 1, (1 << 23) - 1, 1000, 64, 0, 2, 1) > 0
+    assert f(9, 1, 1, (1 << 23) - 1, 1000, 64, 0, 2, 1) == 0
 
 
 def masked(**kw):
