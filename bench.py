@@ -282,11 +282,13 @@ def main():
         return
     if args.decode:
         for w in S.DECODE.values():
-            print(json.dumps(run_decode(w, args, osa, torch)), flush=True)
+            print(json.dumps(run_decode(w, args, osa, torch, with_cpu=not args.no_cpu_baseline)),
+                  flush=True)
         return
     if args.masked:
         for name, (w, kind, mk) in S.MASKED.items():
-            print(json.dumps(run_masked(name, w, kind, mk, args, osa, torch)), flush=True)
+            print(json.dumps(run_masked(name, w, kind, mk, args, osa, torch,
+                                        with_cpu=not args.no_cpu_baseline)), flush=True)
         return
     if args.fp8:
         for d in (128, 64):
@@ -335,7 +337,7 @@ def kernel_table(w):
     ]
 
 
-def run_decode(w, args, osa, torch):
+def run_decode(w, args, osa, torch, with_cpu: bool = False):
     """One split-KV forward (chunk kernel + merge kernel) per step on a decoding
     workload; HBM-bound, so the roofline is bytes: K and V read once, plus Q read and
     O and LSE written (the fp32 chunk results in the workspace are overhead)."""
@@ -365,7 +367,7 @@ def run_decode(w, args, osa, torch):
     e = q.element_size()
     algo = w.kv_bytes() + 2 * q.numel() * e + lse.numel() * 4
     gbs = algo / (st["mean"] * 1e-3) / 1e9
-    return {"metric": "split-KV decode forward: compulsory HBM bytes per second",
+    line = {"metric": "split-KV decode forward: compulsory HBM bytes per second",
             "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(st["mean"], 4), "higher_is_better": True,
             "dtype": w.dtype, "data": "synthetic", "config": w.describe(),
@@ -375,9 +377,34 @@ def run_decode(w, args, osa, torch):
                          "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": algo,
                          "ms": {k2: round(x, 4) for k2, x in st.items()}}}
+    if with_cpu:
+        line["cpu_baseline"] = decode_cpu_baseline(w, inp, o, algo)
+    return line
 
 
-def run_masked(name, w, kind, mk, args, osa, torch):
+def decode_cpu_baseline(w, inp, o_gpu, algo_bytes: int, budget_s: float = 10.0):
+    """Time the fp64 oracle forward over the batch entries in order (all heads of each)
+    until every entry is done or budget_s seconds have been spent; the rate is the
+    compulsory bytes of the entries done over that time, as for the GPU."""
+    import numpy as np
+
+    import oracle.attention as A
+    done, dt, err = 0, 0.0, 0.0
+    while done < w.B and dt < budget_s:
+        b = slice(done, done + 1)
+        t0 = time.perf_counter()
+        ref_o, _ = A.attention_forward(inp["q"][b], inp["k"][b], inp["v"][b], w.scale, w.causal)
+        dt += time.perf_counter() - t0
+        err = max(err, float(np.max(np.abs(o_gpu[b].float().cpu().double().numpy() - ref_o))))
+        done += 1
+    return {"value": round(algo_bytes * done / w.B / dt / 1e9, 3), "unit": "GB/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle forward on batch entries 0-{done - 1} of {w.B} (all {w.H} "
+                      f"query heads each), {dt:.2f} s; bytes counted as for the GPU",
+            "seconds": round(dt, 3), "gpu_vs_oracle_o_max_abs": err}
+
+
+def run_masked(name, w, kind, mk, args, osa, torch, with_cpu: bool = False):
     """Interval-masked forward + backward; FLOP counted on the visible (query, key)
     pairs only: 4*d per pair and head forward, 2.5x that backward."""
     import synthetic as S
@@ -415,7 +442,7 @@ def run_masked(name, w, kind, mk, args, osa, torch):
     peak = PEAK_TFLOPS[w.dtype]
     val = (ff + bf) / ((f_ms + b_ms) * 1e-3) / 1e12
     dense = 4.0 * w.B * w.H * w.N * w.nk * w.d
-    return {"metric": "interval-masked attention fwd+bwd TFLOP/s on visible pairs",
+    line = {"metric": "interval-masked attention fwd+bwd TFLOP/s on visible pairs",
             "value": round(val, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(f_ms + b_ms, 4), "higher_is_better": True,
             "dtype": w.dtype, "data": "synthetic",
@@ -427,6 +454,42 @@ def run_masked(name, w, kind, mk, args, osa, torch):
                     "frac_peak": round(ff / (f_ms * 1e-3) / 1e12 / peak, 4)},
             "bwd": {"ms": round(b_ms, 4), "tflops": round(bf / (b_ms * 1e-3) / 1e12, 2),
                     "frac_peak": round(bf / (b_ms * 1e-3) / 1e12 / peak, 4)}}
+    if with_cpu:
+        line["cpu_baseline"] = masked_cpu_baseline(w, inp, lo.cpu(), hi.cpu(), o, dq)
+    return line
+
+
+def masked_cpu_baseline(w, inp, lo, hi, o_gpu, dq_gpu, budget_s: float = 10.0):
+    """Time the fp64 oracle forward + backward under the same intervals, one KV group of
+    batch 0 at a time, until every group is done or budget_s seconds have been spent;
+    FLOP counted on the visible pairs of batch 0, as for the GPU."""
+    import numpy as np
+
+    import oracle.attention as A
+    import synthetic as S
+    n_rep = w.H // w.Hkv
+    lo_n, hi_n = lo.numpy(), hi.numpy()
+    done, dt, err_o, err_dq = 0, 0.0, 0.0, 0.0
+    while done < w.Hkv and dt < budget_s:
+        t0 = time.perf_counter()
+        ref = A.attention_backward_intervals(inp["q"], inp["k"], inp["v"], inp["do"], w.scale,
+                                             lo_n, hi_n, heads=[(0, done)])
+        dt += time.perf_counter() - t0
+        hs = slice(done * n_rep, (done + 1) * n_rep)
+        err_o = max(err_o, float(np.max(np.abs(o_gpu[0, hs].float().cpu().double().numpy()
+                                               - ref["o"][0, hs]))))
+        dq_ref = ref["dq"][0, hs]
+        err_dq = max(err_dq, float(np.max(np.abs(dq_gpu[0, hs].float().cpu().double().numpy() - dq_ref))
+                                   / max(float(np.max(np.abs(dq_ref))), 1e-300)))
+        done += 1
+    n_heads = done * n_rep
+    flop = 14.0 * w.d * S.visible_pairs(lo[:1], hi[:1], w.nk) * n_heads
+    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd on {n_heads} of {w.B * w.H} heads (b=0, kv groups "
+                      f"0-{done - 1}), {dt:.2f} s; dense S/P under the mask, FLOP counted on "
+                      f"visible pairs as for the GPU",
+            "seconds": round(dt, 3), "gpu_vs_oracle_on_sample": {"o_max_abs": err_o, "dq_rel": err_dq}}
 
 
 def run_fp8(w, args, osa, torch, with_cpu: bool):

@@ -137,3 +137,31 @@ def test_row_cpu_baseline_covers_rows_in_order():
     cb = bench.row_cpu_baseline(w, inp, budget_s=5.0)
     assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0
     assert "rows 0-63 of 64" in cb["sample"]
+
+
+def test_decode_cpu_baseline_covers_batch_in_order():
+    """Fed the oracle's own output as the 'GPU' result, the recorded error vanishes; the
+    whole batch is the sample when the budget allows."""
+    import oracle.attention as A
+    w = S.custom("bf16", 2, 4, 2, 3, 64, True, seed_base=123, Nk=200)
+    inp = S.make_inputs(w, with_grad=False)
+    ref_o, _ = A.attention_forward(inp["q"], inp["k"], inp["v"], w.scale, w.causal)
+    cb = bench.decode_cpu_baseline(w, inp, torch.from_numpy(ref_o), 1000, budget_s=5.0)
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["value"] > 0
+    assert "batch entries 0-1 of 2" in cb["sample"]
+    assert cb["gpu_vs_oracle_o_max_abs"] < 1e-6
+
+
+def test_masked_cpu_baseline_walks_groups():
+    import oracle.attention as A
+    w = S.custom("bf16", 2, 4, 2, 40, 64, False, seed_base=321, Nk=50)
+    inp = S.make_inputs(w, with_grad=True)
+    lo, hi = S.mask_intervals("sliding", w.B, w.N, w.nk, left=7, right=3, causal=False)
+    ref = A.attention_backward_intervals(inp["q"], inp["k"], inp["v"], inp["do"], w.scale,
+                                         lo.numpy(), hi.numpy())
+    o, dq = torch.from_numpy(ref["o"]), torch.from_numpy(ref["dq"])
+    cb = bench.masked_cpu_baseline(w, inp, lo, hi, o, dq, budget_s=5.0)
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0
+    assert "4 of 8 heads" in cb["sample"] and "kv groups 0-1" in cb["sample"]
+    assert cb["gpu_vs_oracle_on_sample"]["o_max_abs"] < 1e-6
+    assert cb["gpu_vs_oracle_on_sample"]["dq_rel"] < 1e-6
