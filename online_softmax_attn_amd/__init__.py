@@ -27,6 +27,7 @@ bfloat16); ``lse`` is float32 [B,H,N].  ``scale`` defaults to 1/sqrt(d).
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 import os
 
@@ -153,6 +154,28 @@ def status_string(status: int) -> str:
     return library().attn_status_string(int(status)).decode()
 
 
+def _common_device(tensors):
+    """The one device the CUDA (ROCm) tensors among `tensors` share, or None if none is."""
+    devs = {t.device for t in tensors if t.device.type == "cuda"}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on more than one device: {sorted(str(d) for d in devs)}")
+    return next(iter(devs), None)
+
+
+def _one_device(fn):
+    """Run fn with the device of its tensor arguments current: the library launches on
+    the current device, into the stream passed to it, and both must be the tensors'
+    device.  Tensors on two devices are refused before anything is enqueued."""
+    @functools.wraps(fn)
+    def call(*args, **kwargs):
+        dev = _common_device([a for a in (*args, *kwargs.values()) if isinstance(a, torch.Tensor)])
+        if dev is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.device(dev):
+            return fn(*args, **kwargs)
+    return call
+
+
 def _check_dev(name, t, dtype=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -182,6 +205,7 @@ def attn_bwd_workspace_bytes(B, H, Hkv, N, d, dtype) -> int:
     return int(library().attn_bwd_workspace_bytes(B, H, Hkv, N, d, code))
 
 
+@_one_device
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
     """O and LSE for q [B,H,N,d], k/v [B,Hkv,N,d]; enqueued on the current stream."""
     lib = library()
@@ -232,6 +256,7 @@ def _bwd_checked(q, k, v, o, lse, do, scale, dq, dk, dv, workspace):
     return (B, H, Hkv, N, d), float(scale), dq, dk, dv, workspace
 
 
+@_one_device
 def new_bwd_workspace(q, k):
     """An uninitialised device buffer of attn_bwd_workspace_bytes() for these tensors."""
     B, H, Hkv, N, d = _dims(q, k)
@@ -243,6 +268,7 @@ def _ws_bytes(ws):
     return ws.numel() * ws.element_size()
 
 
+@_one_device
 def attn_bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
              dq=None, dk=None, dv=None, workspace=None):
     """dQ, dK, dV from the forward's O and LSE; enqueued on the current stream."""
@@ -258,6 +284,7 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     return dq, dk, dv
 
 
+@_one_device
 def attn_bwd_preprocess(q, k, o, lse, do, workspace):
     """First backward kernel alone: D and LSE*log2(e) into ``workspace``.
 
@@ -278,6 +305,7 @@ def attn_bwd_preprocess(q, k, o, lse, do, workspace):
     return workspace
 
 
+@_one_device
 def attn_bwd_dkdv(q, k, v, o, lse, do, workspace, causal: bool = False,
                   scale: float | None = None, dk=None, dv=None):
     """dK/dV kernel alone, after attn_bwd_preprocess filled ``workspace``."""
@@ -293,6 +321,7 @@ def attn_bwd_dkdv(q, k, v, o, lse, do, workspace, causal: bool = False,
     return dk, dv
 
 
+@_one_device
 def attn_bwd_dq(q, k, v, o, lse, do, workspace, causal: bool = False,
                 scale: float | None = None, dq=None):
     """dQ kernel alone, after attn_bwd_preprocess filled ``workspace``."""
@@ -314,6 +343,7 @@ def attn_fwd_splitkv_workspace_bytes(B, H, Hkv, Nq, Nk, d, causal, dtype, n_spli
                                                           code, int(n_splits)))
 
 
+@_one_device
 def attn_fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, n_splits: int = 0,
                      out=None, lse=None, workspace=None):
     """Split-KV forward: q [B,H,Nq,d] against k/v [B,Hkv,Nk,d] (Nq may be much smaller
@@ -357,6 +387,7 @@ def _check_intervals(kv_lo, kv_hi, B, Nq):
             raise ValueError(f"{name} must be int32 [B, Nq] = {(B, Nq)}, got {tuple(t.shape)}")
 
 
+@_one_device
 def attn_fwd_masked(q, k, v, kv_lo, kv_hi, scale: float | None = None, out=None, lse=None):
     """Forward under per-row visible key intervals: query i of batch b sees keys
     kv_lo[b, i] .. kv_hi[b, i] (int32 [B, Nq] device tensors); k/v may be longer than q."""
@@ -393,6 +424,7 @@ def attn_bwd_masked_workspace_bytes(B, H, Hkv, Nq, Nk, d, dtype) -> int:
     return int(library().attn_bwd_masked_workspace_bytes(B, H, Hkv, Nq, Nk, d, code))
 
 
+@_one_device
 def attn_bwd_masked(q, k, v, o, lse, do, kv_lo, kv_hi, scale: float | None = None,
                     dq=None, dk=None, dv=None, workspace=None):
     """dQ, dK, dV under the same per-row key intervals as attn_fwd_masked."""
@@ -438,6 +470,7 @@ def _rows_of(x):
     return x.numel() // cols, cols
 
 
+@_one_device
 def rowsoftmax_fwd(x, log_softmax: bool = False, out=None):
     """Softmax (or log-softmax) of every row of x over its last dimension."""
     lib = library()
@@ -456,6 +489,7 @@ def rowsoftmax_fwd(x, log_softmax: bool = False, out=None):
     return out
 
 
+@_one_device
 def rowsoftmax_bwd(y, dy, log_softmax: bool = False, out=None):
     """Gradient with respect to the rows' input, from the forward's output y and dy."""
     lib = library()
@@ -484,6 +518,7 @@ def _check_targets(targets, rows):
         raise ValueError(f"targets must hold one int32 per row ({rows}), got {targets.numel()}")
 
 
+@_one_device
 def rowxent_fwd(logits, targets, loss=None, lse=None):
     """Per-row cross-entropy logsumexp(x) - x[target] (0 where the target is outside
     0 .. C-1) and the row logsumexp, both float32 with the rows' shape."""
@@ -507,6 +542,7 @@ def rowxent_fwd(logits, targets, loss=None, lse=None):
     return loss, lse
 
 
+@_one_device
 def rowxent_bwd(logits, targets, lse, dloss, out=None):
     """dlogits = dloss[row] * (softmax(logits) - onehot(target)); zero for ignored rows."""
     lib = library()
@@ -535,6 +571,7 @@ def attn_fwd_fp8_workspace_bytes(B, Hkv, N, d=128) -> int:
     return int(library().attn_fwd_fp8_workspace_bytes(B, Hkv, N, d))
 
 
+@_one_device
 def attn_fwd_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float,
                  causal: bool = False, scale: float | None = None, out=None, lse=None,
                  workspace=None):

@@ -11,6 +11,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import online_softmax_attn_amd as osa
 
@@ -428,3 +429,24 @@ def test_fp8_workspace_bytes():
     assert lib.attn_fwd_fp8_workspace_bytes(1, 1, 100, 96) == 0
     assert lib.attn_fwd_fp8_workspace_bytes(0, 1, 100, 128) == 0
     assert osa.attn_fwd_fp8_workspace_bytes(4, 16, 8192) == 4 * 16 * 128 * 8192
+
+
+def test_tensors_on_two_devices_are_refused():
+    """The binding runs each call on its tensors' device and refuses a mix of devices
+    before anything is enqueued (stand-ins with a device attribute; no GPU here)."""
+    from types import SimpleNamespace as NS
+    dev = lambda s: NS(device=torch.device(s))
+    assert osa._common_device([dev("cuda:1"), dev("cuda:1"), dev("cpu")]) == torch.device("cuda:1")
+    assert osa._common_device([dev("cpu")]) is None
+    assert osa._common_device([]) is None
+    with pytest.raises(ValueError, match="more than one device"):
+        osa._common_device([dev("cuda:0"), dev("cuda:1")])
+
+
+def test_public_calls_carry_the_device_guard():
+    for name in osa.__all__:
+        fn = getattr(osa, name)
+        if name.endswith("_bytes") or not callable(fn) or name in ("library", "status_string",
+                                                                   "AttnError", "library_path"):
+            continue
+        assert getattr(fn, "__wrapped__", None) is not None, name
