@@ -168,8 +168,10 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   __shared__ __attribute__((aligned(256))) float ll1[C::kQT], lD1[C::kQT];
   __shared__ __attribute__((aligned(256))) float ll2[C::kQT], lD2[C::kQT];
   __shared__ __attribute__((aligned(256))) float ll3[NBUF > 3 ? C::kQT : 4], lD3[NBUF > 3 ? C::kQT : 4];
-  // Interval masks: each staged tile's row intervals, lo in [0, kQT), hi in [kQT, 2kQT).
-  constexpr int kLM = IMASK ? 2 * C::kQT : 4;
+  // Interval masks: each staged tile's row intervals, lo in [0, kQT), hi in [kQT, 2kQT),
+  // then the tile's summary (min lo, max hi, max lo, min hi) at 2kQT (the DMA brings 64
+  // words: the summaries of this tile and the next 15, or zeros past the last tile).
+  constexpr int kLM = IMASK ? 2 * C::kQT + 64 : 4;
   __shared__ __attribute__((aligned(256))) int lm0[kLM], lm1[kLM], lm2[kLM], lm3[kLM];
 
   const int tid = threadIdx.x;
@@ -236,8 +238,10 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       f = min(f, __shfl_xor(f, off));
       l = max(l, __shfl_xor(l, off));
     }
-    qt_first = l >= 0 ? f : 0;
-    per_head = l >= 0 ? l - f + 1 : 0;
+    // (Equal in every lane after the reduction; read from lane 0 so that the loop's
+    // trip count and its wait choices are scalar.)
+    qt_first = __builtin_amdgcn_readfirstlane(l >= 0 ? f : 0);
+    per_head = __builtin_amdgcn_readfirstlane(l >= 0 ? l - f + 1 : 0);
   }
   const int n_iter = per_head * n_rep;
 
@@ -275,12 +279,18 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         const auto rhi = make_rsrc(kv_hi + (size_t)b * Nq, (uint32_t)Nq * 4);
         buffer_load4_lds(rlo, lm, lane4, i0 * 4);
         buffer_load4_lds(rhi, lm + C::kQT, lane4, i0 * 4);
+        // The tile's summary comes through LDS too: read from global memory in the
+        // loop, it would need a vmcnt wait that also drains the prefetches in flight.
+        // (The tile offset goes into the per-lane offset, which the buffer's range check
+        // always covers: lanes past the last summary read zero.)
+        const auto rs = make_rsrc(tile_sum + (size_t)b * n_qt, (uint32_t)n_qt * 16);
+        buffer_load4_lds(rs, lm + 2 * C::kQT, lane4 + (i0 / C::kQT) * 16, 0);
       }
     }
   };
   // Outstanding loads per staged tile: 2 * kCPW per wave, and wave 0 also loads LSE
-  // and D (and the two interval arrays).
-  constexpr int kW0 = IMASK ? 4 : 2;
+  // and D (and the two interval arrays and the tile summary).
+  constexpr int kW0 = IMASK ? 5 : 2;
 
   // LDS read offsets (bytes in a tile), loop-invariant per lane.
   //  row-wise (A operand of S and dP): row 32qb + l32, logical granule 2c + hi
@@ -642,7 +652,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     if constexpr (IMASK) {
       // Skip the tile if no row's interval meets this wave's keys; mask it unless every
       // row sees all of them.
-      const i32x4 sm = tile_sum[(size_t)b * n_qt + tq];
+      const i32x4 smv = *(const i32x4*)(lm + 2 * C::kQT);
+      const int sm[4] = {__builtin_amdgcn_readfirstlane(smv[0]), __builtin_amdgcn_readfirstlane(smv[1]),
+                         __builtin_amdgcn_readfirstlane(smv[2]), __builtin_amdgcn_readfirstlane(smv[3])};
       const int kw_last = kw + 32 * KB - 1;
       if (sm[0] > kw_last || sm[1] < kw) return;
       if (sm[2] <= kw && sm[3] >= kw_last) compute_tile(M0{}, i0, qb_, db_, ll, lD, lm);
