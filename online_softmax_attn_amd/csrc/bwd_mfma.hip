@@ -867,6 +867,12 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       w_maxlo = max(w_maxlo, __shfl_xor(w_maxlo, off));
       w_minhi = min(w_minhi, __shfl_xor(w_minhi, off));
     }
+    // Both half-waves hold the same 32 rows, so every lane now has the wave's values;
+    // read them from lane 0 so that the per-tile tests are scalar branches.
+    w_lo = __builtin_amdgcn_readfirstlane(w_lo);
+    w_hi = __builtin_amdgcn_readfirstlane(w_hi);
+    w_maxlo = __builtin_amdgcn_readfirstlane(w_maxlo);
+    w_minhi = __builtin_amdgcn_readfirstlane(w_minhi);
     if (lane == 0) {
       wg_bounds[2 * wave] = w_lo;
       wg_bounds[2 * wave + 1] = w_hi;
@@ -878,8 +884,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       g_lo = min(g_lo, wg_bounds[2 * w]);
       g_hi = max(g_hi, wg_bounds[2 * w + 1]);
     }
-    kt0 = g_hi >= g_lo ? g_lo / C::kBC : 0;
-    n_kt = g_hi >= g_lo ? g_hi / C::kBC + 1 - kt0 : 0;
+    kt0 = __builtin_amdgcn_readfirstlane(g_hi >= g_lo ? g_lo / C::kBC : 0);
+    n_kt = __builtin_amdgcn_readfirstlane(g_hi >= g_lo ? g_hi / C::kBC + 1 - kt0 : 0);
   }
 
   uint32_t goff[C::kCPW];
