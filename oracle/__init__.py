@@ -5,7 +5,7 @@ leg may import anything under ``oracle/``.  The HIP library and its Python
 binding do not import it, and it does not import them.
 
 ``oracle.attention``   the plain definition (S, P materialised), forward + backward
-``oracle.online_walk`` the pages' tiled online-softmax walk, used to pin the above
+``oracle.online_walk`` the online softmax as a fold of key-block summaries, used to pin the above
                        against the printed worked example
 ``oracle.brute``       pure-Python loops for tiny shapes (an independent pin)
 

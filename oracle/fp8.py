@@ -23,7 +23,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["decode_e4m3", "E4M3_MAX", "dequantize", "attention_forward_fp8"]
+__all__ = ["decode_e4m3", "E4M3_MAX", "dequantize", "attention_forward_fp8",
+           "attention_forward_fp8_rows"]
 
 E4M3_MAX = 448.0
 
@@ -53,3 +54,14 @@ def attention_forward_fp8(q8, k8, v8, descale_q, descale_k, descale_v, scale, ca
     k = dequantize(k8, descale_k)
     v = dequantize(v8, descale_v)
     return A.attention_forward(q, k, v, scale, causal, **kw)
+
+
+def attention_forward_fp8_rows(q8, k8, v8, descale_q, descale_k, descale_v, scale, causal, picks):
+    """O and LSE of individually picked rows (b, h, i) of the same definition: the
+    rows of ``attention_forward_fp8``, each computed against its whole key/value head
+    (for checking rows of problems too large to evaluate whole)."""
+    import oracle.attention as A
+    q = dequantize(q8, descale_q)
+    k = dequantize(k8, descale_k)
+    v = dequantize(v8, descale_v)
+    return A.attention_forward_rows(q, k, v, scale, causal, picks)

@@ -632,9 +632,10 @@ def pin_fp8_decode_closed_forms():
 
 
 def pin_fp8_attention_is_attention_of_decoded(seed=51):
-    """The fp8 forward equals the plain forward of the decoded, dequantised tensors
-    computed by hand here (codes drawn at random, scales chosen as powers of two so
-    the products are exact), against the pure-Python loops."""
+    """The fp8 forward (and its row variant, on picked rows) equals the plain forward
+    of the decoded, dequantised tensors computed by hand here (codes drawn at random,
+    scales chosen as powers of two so the products are exact), against the
+    pure-Python loops."""
     r = np.random.default_rng(seed)
     q8 = r.integers(0, 0x7F, (1, 2, 5, 4)) | (r.integers(0, 2, (1, 2, 5, 4)) << 7)
     k8 = r.integers(0, 0x7F, (1, 1, 5, 4)) | (r.integers(0, 2, (1, 1, 5, 4)) << 7)
@@ -646,11 +647,17 @@ def pin_fp8_attention_is_attention_of_decoded(seed=51):
     q = F8.decode_e4m3(q8) * dq
     k = F8.decode_e4m3(k8) * dk
     v = F8.decode_e4m3(v8) * dv
+    picks = [(0, 1, 4), (0, 0, 0), (0, 1, 2)]
+    o_r, lse_r = F8.attention_forward_fp8_rows(q8, k8, v8, dq, dk, dv, scale, True, picks)
     err = 0.0
     for h in range(2):  # GQA: both query heads read the one key/value head
         ob, lb = BR.forward(q[0, h].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), scale, True)
         err = max(err, float(np.max(np.abs(o[0, h] - np.array(ob)))),
                   float(np.max(np.abs(lse[0, h] - np.array(lb)))))
+        for n, (_, hp, i) in enumerate(picks):  # the row variant, row by row
+            if hp == h:
+                err = max(err, float(np.max(np.abs(o_r[n] - np.array(ob[i])))),
+                          abs(float(lse_r[n]) - lb[i]))
     return err
 
 

@@ -37,7 +37,7 @@ def compare(o, lse, r_o, r_lse, dtype, label):
     # Rows that see no key: LSE = -inf on both sides, O = 0.
     assert np.array_equal(np.isneginf(g_l), np.isneginf(r_lse)), label
     fin = np.isfinite(r_lse)
-    e_o, e_l = out_err(g_o, r_o), max_abs(g_l[fin], r_lse[fin])
+    e_o, e_l = out_err(g_o, r_o, dtype), max_abs(g_l[fin], r_lse[fin])
     say(f"[masked] {label} o={e_o:.2e} lse={e_l:.2e}")
     assert e_o <= TOL_O[dtype] and e_l <= TOL_O[dtype], (e_o, e_l)
 
@@ -136,7 +136,7 @@ def test_masked_full_size_sampled(case):
             ro, rl = A.attention_head_intervals(A._f64(inp["q"][b, h])[rows], A._f64(inp["k"][b, g]),
                                                 A._f64(inp["v"][b, g]), w.scale,
                                                 lo[b].numpy()[rows], hi[b].numpy()[rows])
-            err_o = max(err_o, out_err(f64(o[b, h])[rows], ro))
+            err_o = max(err_o, out_err(f64(o[b, h])[rows], ro, dtype))
             err_l = max(err_l, max_abs(f64(lse[b, h])[rows], rl))
     say(f"[masked] {name} sampled o={err_o:.2e} lse={err_l:.2e}")
     assert err_o <= TOL_O[dtype] and err_l <= TOL_O[dtype]
@@ -223,7 +223,7 @@ def test_masked_bwd_full_size_groups(case):
         e = {"dq": rel_err(f64(dq[b, hs]), ref["dq"][b, hs]),
              "dk": rel_err(f64(dk[b, g]), ref["dk"][b, g]),
              "dv": rel_err(f64(dv[b, g]), ref["dv"][b, g]),
-             "o": out_err(f64(o[b, hs]), ref["o"][b, hs])}
+             "o": out_err(f64(o[b, hs]), ref["o"][b, hs], dtype)}
         say(f"[masked] {name} group ({b},{g}) {', '.join(f'{k}={v:.2e}' for k, v in e.items())}")
         assert e["o"] <= TOL_O[dtype]
         assert max(e["dq"], e["dk"], e["dv"]) <= TOL_G[dtype], e

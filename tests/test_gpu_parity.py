@@ -1,8 +1,11 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Small and ragged shapes are compared element by element over the whole problem;
-the five named workloads run at their full sizes with rows sampled across every
-head (forward) and whole key/value groups (backward) checked against the oracle.
+Small and ragged shapes are compared element by element over the whole problem.
+The named workloads run at their full sizes: the fp32 head, the bf16 forward, the
+fp16 causal and the bf16 GQA causal workloads, and the sweep point that bench.py
+times, are compared element by element over the whole problem (forward and
+backward); the other sweep points on rows sampled across every head and one whole
+key/value group.
 """
 
 import math
@@ -12,7 +15,8 @@ import pytest
 import torch
 
 import synthetic as S
-from gpu_parity import (TOL_G, TOL_O, check_full, check_group_bwd, check_sampled_fwd, f64,
+from gpu_parity import (TOL_G, TOL_O, check_all_heads, check_full, check_group_bwd,
+                         check_sampled_fwd, f64,
                         max_abs, need_gpu, rel_err, run_bwd, run_fwd, say)
 
 pytestmark = pytest.mark.gpu
@@ -163,23 +167,39 @@ def test_workload_bf16_fwd_full():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_workload_fp16_causal():
+    """fp16 causal B2 H32 N8192 d64, every output element of the forward and the
+    backward against the oracle."""
     need_gpu()
     w = S.WORKLOADS["fp16_causal"]
     inp = S.make_inputs(w)
     outs = run_bwd(inp, True, w.scale)
-    check_sampled_fwd(inp, outs[0], outs[1], "fp16", True, w.scale, per_head=3, label=w.name)
-    check_group_bwd(inp, outs, "fp16", True, w.scale, [(0, 0), (1, 31)], label=w.name)
+    check_all_heads(inp, outs, "fp16", True, w.scale, label=w.name)
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_workload_bf16_gqa_causal():
+    """bf16 GQA causal B1 H32 Hkv8 N16384 d128 with 1% of key rows x8, every output
+    element of the forward and the backward against the oracle."""
     need_gpu()
     w = S.WORKLOADS["bf16_gqa_causal"]
     inp = S.make_inputs(w)
     outs = run_bwd(inp, True, w.scale)
-    check_sampled_fwd(inp, outs[0], outs[1], "bf16", True, w.scale, per_head=3, label=w.name)
-    check_group_bwd(inp, outs, "bf16", True, w.scale, [(0, 5)], label=w.name)
+    check_all_heads(inp, outs, "bf16", True, w.scale, label=w.name)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_workload_headline_full():
+    """The sweep point bench.py times (bf16 B4 H16 N8192 d128, non-causal), every
+    output element of the forward and the backward against the oracle."""
+    need_gpu()
+    w = S.HEADLINE
+    inp = S.make_inputs(w)
+    outs = run_bwd(inp, False, w.scale)
+    check_all_heads(inp, outs, "bf16", False, w.scale, label=w.name)
 
 
 @pytest.mark.slow

@@ -30,7 +30,7 @@ def check_split(w, n_splits=0, label=""):
     r_o, r_lse = A.attention_forward(inp["q"], inp["k"], inp["v"], w.scale, w.causal)
     g_o, g_l = f64(o), f64(lse)
     assert np.all(np.isfinite(g_o)) and np.all(np.isfinite(g_l))
-    e_o, e_l = out_err(g_o, r_o), max_abs(g_l, r_lse)
+    e_o, e_l = out_err(g_o, r_o, w.dtype), max_abs(g_l, r_lse)
     say(f"[splitkv]   errors o={e_o:.2e} lse={e_l:.2e}")
     assert e_o <= TOL_O[w.dtype] and e_l <= TOL_O[w.dtype], (e_o, e_l)
     return o, lse

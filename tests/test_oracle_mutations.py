@@ -207,61 +207,46 @@ def test_mutant_is_caught(mutant, monkeypatch):
     assert failed, f"no pin caught mutant {mutant}"
 
 
-# Mistakes in the tiled walk's update (steps 4 and 5 and the final normalisation):
-# each mutant is the walk with one step changed.
-def _walk_mutant(kind):
-    def walk(q, k, v, block_rows, block_cols, scale=1.0, causal=False, trace=False):
-        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
-        n, d = q.shape
-        o, lse, steps = np.empty_like(q), np.empty(n), []
-        for i in range(-(-n // block_rows)):
-            rows = np.arange(i * block_rows, min(n, (i + 1) * block_rows))
-            m, l, ot = np.full(len(rows), -np.inf), np.zeros(len(rows)), np.zeros((len(rows), d))
-            for j in range(-(-k.shape[0] // block_cols)):
-                cols = np.arange(j * block_cols, min(k.shape[0], (j + 1) * block_cols))
-                s_ij = scale * (q[rows] @ k[cols].T)
-                if causal:
-                    s_ij = np.where(cols[None, :] > rows[:, None], -np.inf, s_ij)
-                m_ij = np.max(s_ij, axis=1)
-                live = np.isfinite(m_ij)
-                pt = np.zeros_like(s_ij)
-                pt[live] = np.exp(s_ij[live] - m_ij[live, None])
-                l_ij = pt.sum(axis=1)
-                m_new = np.maximum(m, m_ij)
-                alpha = W._exp_diff(m, m_new)
-                beta = W._exp_diff(m_ij, m_new)
-                if kind == "no_alpha_on_ot":
-                    ot = ot + beta[:, None] * (pt @ v[cols])
-                    l = alpha * l + beta * l_ij
-                elif kind == "no_beta":
-                    ot = alpha[:, None] * ot + pt @ v[cols]
-                    l = alpha * l + l_ij
-                elif kind == "alpha_inverted":
-                    inv = np.where(np.isfinite(m), np.exp(m_new - np.where(np.isfinite(m), m, 0)), 0.0)
-                    ot = inv[:, None] * ot + beta[:, None] * (pt @ v[cols])
-                    l = inv * l + beta * l_ij
-                else:
-                    ot = alpha[:, None] * ot + beta[:, None] * (pt @ v[cols])
-                    l = alpha * l + beta * l_ij
-                m = m_new
-                if trace:
-                    steps.append({"i": i, "j": j, "m": m.copy(), "l": l.copy(), "Ot": ot.copy()})
-            o[rows] = ot / l[:, None]
-            lse[rows] = np.log(l) if kind == "lse_drops_max" else m + np.log(l)
-        return (o, lse, steps) if trace else (o, lse)
-    return walk
+# Mistakes in the block fold (the exact combination of two summaries, and the final
+# output / logsumexp): each mutant replaces one of them with a copy that has one
+# thing changed.
+def _combine_mutant(kind):
+    def combine(a, b):
+        (m1, l1, u1), (m2, l2, u2) = a, b
+        mm = np.maximum(m1, m2)
+        w1, w2 = W._weight(m1, mm), W._weight(m2, mm)
+        if kind == "running_not_rescaled":       # the earlier blocks keep their old max
+            return mm, l1 + w2 * l2, u1 + w2[:, None] * u2
+        if kind == "block_not_rescaled":         # the new block keeps its own max
+            return mm, w1 * l1 + l2, w1[:, None] * u1 + u2
+        if kind == "correction_inverted":        # exp(M - m) instead of exp(m - M)
+            inv = np.where(np.isfinite(m1), np.exp(mm - np.where(np.isfinite(m1), m1, 0)), 0.0)
+            return mm, inv * l1 + w2 * l2, inv[:, None] * u1 + w2[:, None] * u2
+        if kind == "u_not_rescaled":             # only the denominator is moved
+            return mm, w1 * l1 + w2 * l2, u1 + u2
+        return mm, w1 * l1 + w2 * l2, w1[:, None] * u1 + w2[:, None] * u2
+    return combine
 
 
-WALK_MUTANTS = ["no_alpha_on_ot", "no_beta", "alpha_inverted", "lse_drops_max"]
+def _finish_drops_max(state):
+    m, l, u = state
+    return u / l[:, None], np.log(l)
 
 
-def test_walk_mutant_harness_is_the_walk(monkeypatch):
-    """With no step changed, the test's copy of the walk passes every pin."""
-    monkeypatch.setattr(W, "tiled_forward", _walk_mutant(None))
+WALK_MUTANTS = ["running_not_rescaled", "block_not_rescaled", "correction_inverted",
+                "u_not_rescaled", "lse_drops_max"]
+
+
+def test_walk_mutant_harness_is_the_fold(monkeypatch):
+    """With nothing changed, the test's copy of the combination passes every pin."""
+    monkeypatch.setattr(W, "combine", _combine_mutant(None))
     assert _failing_pins() == []
 
 
 @pytest.mark.parametrize("mutant", WALK_MUTANTS)
 def test_walk_mutant_is_caught(mutant, monkeypatch):
-    monkeypatch.setattr(W, "tiled_forward", _walk_mutant(mutant))
+    if mutant == "lse_drops_max":
+        monkeypatch.setattr(W, "finish", _finish_drops_max)
+    else:
+        monkeypatch.setattr(W, "combine", _combine_mutant(mutant))
     assert _failing_pins(), f"no pin caught mutant {mutant}"
