@@ -14,17 +14,24 @@ kernel's extra recompute of S and dP is real work that is not counted.
 
 Timing: HIP events recorded on the stream the kernels run on (torch's current
 stream, which the binding passes to the library), around each pass of each of the
-K timed steps, after W untimed warm-up steps.  The backward is enqueued as its
-three kernels (attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq: exactly what
-attn_bwd launches) so that an event sits between every two launches.  ``kernels``
-gives each launch's mean/median/min/p90 time and its roofline: achieved = the
-algorithmic FLOP (or bytes, for the HBM-bound preprocess) per launch / mean launch
-time, against the dense bf16/fp16 MFMA peak of 2516.6 TFLOP/s (256 CUs x 4096
-flop/clk x 2.4 GHz) or HBM's 8 TB/s.  ``roofline`` repeats the entry of the
-kernel with the largest share of the step.  ``traffic`` is the HBM bytes per
-launch from committed rocprofv3 counter runs, or null once the kernel source has
-changed since they were taken.  ``cpu_baseline`` times the fp64 oracle on the
-host for a bounded sample (16 heads of the headline workload; fewer at longer N).
+K timed steps, after W untimed warm-up steps.  Between steps, outside the events, a
+512 MiB buffer is overwritten (a fill kernel) so that no step starts with the
+previous one's data in L2 or the 256 MB MALL (--no-flush turns this off).  The
+backward is enqueued as its three kernels (attn_bwd_preprocess, attn_bwd_dkdv,
+attn_bwd_dq: exactly what attn_bwd launches) so that an event sits between every
+two launches.  ``value`` and ``ms_per_step`` use the median step time (mean, min and
+p90 are reported beside it).  ``kernels`` gives each launch's mean/median/min/p90
+time and its roofline: achieved = the algorithmic FLOP (or bytes, for the HBM-bound
+preprocess) per launch / mean launch time (the figure a rocprofv3 kernel trace's
+average duration reproduces), against the dense bf16/fp16 MFMA peak of 2516.6
+TFLOP/s (256 CUs x 4096 flop/clk x 2.4 GHz) or HBM's 8 TB/s, and, for the MFMA
+kernels, against the same peak at the core clock measured during the timed steps
+(``sclk``: the current level of amdgpu's pp_dpm_sclk, read before, every 5 ms
+during, and after the timed loop).  ``roofline`` repeats the entry of the kernel
+with the largest share of the step.  ``traffic`` is the HBM bytes per launch from
+committed rocprofv3 counter runs, or null once the kernel source has changed since
+they were taken.  ``cpu_baseline`` times the fp64 oracle on the host for a bounded
+sample (16 heads of the headline workload; fewer at longer N).
 """
 
 from __future__ import annotations
@@ -229,6 +236,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not overwrite a 512 MiB buffer between timed steps")
     ap.add_argument("--sweep", action="store_true",
                     help="time every point of the bf16 sweep (one JSON line each)")
     ap.add_argument("--decode", action="store_true",
@@ -657,8 +666,104 @@ def run_rows(w, args, osa, torch, with_cpu: bool):
 
 def stats(xs):
     ys = sorted(xs)
-    return {"mean": sum(ys) / len(ys), "median": ys[len(ys) // 2], "min": ys[0],
-            "p90": ys[min(len(ys) - 1, int(math.ceil(0.9 * len(ys))) - 1)]}
+    n = len(ys)
+    med = ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+    return {"mean": sum(ys) / n, "median": med, "min": ys[0],
+            "p90": ys[min(n - 1, int(math.ceil(0.9 * n)) - 1)]}
+
+
+def sclk_path():
+    """The sysfs file that reports the GPU core clock levels with the current one
+    starred (amdgpu's pp_dpm_sclk), if exactly one GPU exposes it."""
+    import glob
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    return paths[0] if len(paths) == 1 else None
+
+
+def read_sclk_mhz(path):
+    """Current core clock in MHz from pp_dpm_sclk (the starred level), or None."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().rstrip("*").strip().lower()
+                                 .replace("mhz", ""))
+    except (OSError, ValueError, IndexError, TypeError):
+        return None
+    return None
+
+
+class ClockSampler:
+    """Reads the current core clock before, during (every `period` seconds, from a
+    thread) and after the timed region.  The clock under load is what the matrix
+    cores run at; the spec peak assumes 2.4 GHz."""
+
+    def __init__(self, period: float = 0.005):
+        import threading
+        self.path = sclk_path()
+        self.period = period
+        self.samples = []
+        self.before = self.after = None
+        self._stop = threading.Event()
+        self._thread = None
+
+    def start(self):
+        import threading
+        if not self.path:
+            return
+        self.before = read_sclk_mhz(self.path)
+
+        def run():
+            while not self._stop.is_set():
+                v = read_sclk_mhz(self.path)
+                if v is not None:
+                    self.samples.append(v)
+                self._stop.wait(self.period)
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        if self.path:
+            self.after = read_sclk_mhz(self.path)
+
+    def record(self):
+        """{'source', 'before_mhz', 'after_mhz', 'during_mhz': {median, min, max, n}}."""
+        out = {"source": self.path or "unavailable", "before_mhz": self.before,
+               "after_mhz": self.after, "during_mhz": None}
+        if self.samples:
+            st = stats(self.samples)
+            out["during_mhz"] = {"median": st["median"], "min": st["min"],
+                                 "max": max(self.samples), "n": len(self.samples)}
+        return out
+
+    def median_ghz(self):
+        return self.samples and stats(self.samples)["median"] / 1000.0 or None
+
+
+def peak_at_clock(peak_spec: float, ghz):
+    """The dense peak scaled from the spec clock (2.4 GHz) to a measured clock."""
+    return peak_spec * ghz / 2.4 if ghz else None
+
+
+FLUSH_BYTES = 512 << 20  # more than the 256 MB last-level cache (MALL) and every L2
+
+
+class CacheFlush:
+    """Overwrites a 512 MiB device buffer between timed steps, outside the timed
+    region (a fill kernel on the current stream before the step's first event), so
+    that no step starts with the previous step's data in L2 or the MALL."""
+
+    def __init__(self, torch, enabled: bool = True):
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda") if enabled else None
+        self.count = 0
+
+    def __call__(self):
+        if self.buf is not None:
+            self.count += 1
+            self.buf.fill_(self.count & 0xFF)
 
 
 def run_one(w, args, osa, torch, with_cpu: bool):
@@ -682,7 +787,11 @@ def run_one(w, args, osa, torch, with_cpu: bool):
         lambda: osa.attn_bwd_dq(q, k, v, o, lse, do, ws, dq=dq, **kw),
     ]
 
+    # Between steps (outside the timed region) a 512 MiB buffer is overwritten so that
+    # no step finds the previous step's data in L2 or the MALL.
+    flush = CacheFlush(torch, enabled=not getattr(args, "no_flush", False))
     for _ in range(args.warmup):
+        flush()
         for f in launches:
             f()
     torch.cuda.synchronize()
@@ -693,25 +802,32 @@ def run_one(w, args, osa, torch, with_cpu: bool):
     nl = len(launches)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    clock = ClockSampler()
+    clock.start()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        flush()
         ev[i][0].record(stream)
         for j, f in enumerate(launches):
             f()
             ev[i][j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock.stop()
+    ghz = clock.median_ghz()
 
     step_ms = [ev[i][0].elapsed_time(ev[i][nl]) for i in range(args.steps)]
     per_ms = [[ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)] for j in range(nl)]
     peak = PEAK_TFLOPS[w.dtype]
-    ms_step = stats(step_ms)["mean"]
+    peak_clk = peak_at_clock(peak, ghz)
+    step_st = stats(step_ms)
+    ms_step = step_st["median"]
     fwd_f, bwd_f = w.fwd_flop(), w.bwd_flop()
     value = (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
     fwd_ms = stats(per_ms[0])
     bwd_ms = stats([sum(per_ms[j][i] for j in range(1, nl)) for i in range(args.steps)])
-    fwd_tf = fwd_f / (fwd_ms["mean"] * 1e-3) / 1e12
-    bwd_tf = bwd_f / (bwd_ms["mean"] * 1e-3) / 1e12
+    fwd_tf = fwd_f / (fwd_ms["median"] * 1e-3) / 1e12
+    bwd_tf = bwd_f / (bwd_ms["median"] * 1e-3) / 1e12
     traffic = load_traffic()
 
     kernels = []
@@ -727,6 +843,8 @@ def run_one(w, args, osa, torch, with_cpu: bool):
                "traffic": traffic_of(traffic, kt, w.name),
                ("flop_per_launch" if kt["unit"] == "flop" else "bytes_per_launch"): kt["work"],
                "ms": {k2: round(x, 4) for k2, x in st.items()}}
+        if kt["bound"] == "mfma" and peak_clk:
+            ent["frac_at_measured_sclk"] = round(ach / peak_clk, 4)
         if "executed_work" in kt:
             ent["executed_flop_per_launch"] = kt["executed_work"]
             ent["executed_tflops"] = round(kt["executed_work"] / secs / 1e12, 2)
@@ -742,6 +860,8 @@ def run_one(w, args, osa, torch, with_cpu: bool):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_stats": {k2: round(x, 4) for k2, x in step_st.items()},
+        "value_basis": "median step time over the timed steps",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -749,11 +869,16 @@ def run_one(w, args, osa, torch, with_cpu: bool):
         "data": "synthetic",
         "config": dict(w.describe(), step="fwd+bwd", parallelism="single GPU"),
         "fwd": {"ms_mean": round(fwd_ms["mean"], 4), "ms_median": round(fwd_ms["median"], 4),
-                "tflops": round(fwd_tf, 2), "frac_peak": round(fwd_tf / peak, 4)},
+                "tflops": round(fwd_tf, 2), "frac_peak": round(fwd_tf / peak, 4),
+                "frac_at_measured_sclk": round(fwd_tf / peak_clk, 4) if peak_clk else None},
         "bwd": {"ms_mean": round(bwd_ms["mean"], 4), "ms_median": round(bwd_ms["median"], 4),
                 "tflops": round(bwd_tf, 2), "frac_peak": round(bwd_tf / peak, 4),
+                "frac_at_measured_sclk": round(bwd_tf / peak_clk, 4) if peak_clk else None,
                 "launches": nl - 1},
         "frac_peak_step": round(value / peak, 4),
+        "frac_peak_step_at_measured_sclk": round(value / peak_clk, 4) if peak_clk else None,
+        "sclk": dict(clock.record(), peak_at_median_tflops=round(peak_clk, 1) if peak_clk else None),
+        "cache_flush_bytes_between_steps": FLUSH_BYTES if flush.buf is not None else 0,
         "roofline": {k2: dominant[k2] for k2 in dominant if k2 != "ms"},
         "kernels": kernels,
         "wall_s_timed": round(wall, 3),

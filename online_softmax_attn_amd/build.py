@@ -26,7 +26,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-ffp-contract=fast",
     "-munsafe-fp-atomics",
     # Packed fp32 VALU instructions stay off: plain fp32 code only.
@@ -39,21 +38,41 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False, extra_flags=None, out: str = LIB, csrc: str = CSRC) -> str:
-    srcs = [os.path.join(csrc, s) for s in SOURCES]
-    fd, tmp = tempfile.mkstemp(prefix=".libosattn.", suffix=".so.tmp", dir=os.path.dirname(os.path.abspath(out)))
-    os.close(fd)
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags or []) + ["-o", tmp] + srcs
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     errs = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
     if res.returncode != 0:
-        os.unlink(tmp)
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs)
+
+
+def build(verbose: bool = False, extra_flags=None, out: str = LIB, csrc: str = CSRC,
+          jobs: int = 0) -> str:
+    """Compile every source to an object (in parallel, `jobs` at a time: default the
+    usable cores, at most 16), link them into one shared library and move it into
+    place only once the link has succeeded."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    jobs = jobs or max(1, min(16, len(os.sched_getaffinity(0)), len(SOURCES)))
+    flags = HIPCC_FLAGS + list(extra_flags or [])
+    outdir = os.path.dirname(os.path.abspath(out))
+    with tempfile.TemporaryDirectory(prefix=".osattn-build.") as objdir:
+        objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[hipcc()] + flags + ["-c", os.path.join(csrc, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(jobs) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        fd, tmp = tempfile.mkstemp(prefix=".libosattn.", suffix=".so.tmp", dir=outdir)
+        os.close(fd)
+        try:
+            _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+        except BaseException:
+            os.unlink(tmp)
+            raise
     os.replace(tmp, out)
     return out
 

@@ -60,7 +60,8 @@ def test_row_bytes():
 
 def test_stats():
     st = bench.stats([5.0, 1.0, 3.0, 2.0, 4.0, 6.0, 7.0, 8.0, 9.0, 10.0])
-    assert st["mean"] == 5.5 and st["min"] == 1.0 and st["median"] == 6.0 and st["p90"] == 9.0
+    assert st["mean"] == 5.5 and st["min"] == 1.0 and st["median"] == 5.5 and st["p90"] == 9.0
+    assert bench.stats([3.0, 1.0, 2.0])["median"] == 2.0
 
 
 def _counter_folder(path, counter, values):
@@ -165,3 +166,28 @@ def test_masked_cpu_baseline_walks_groups():
     assert "4 of 8 heads" in cb["sample"] and "kv groups 0-1" in cb["sample"]
     assert cb["gpu_vs_oracle_on_sample"]["o_max_abs"] < 1e-6
     assert cb["gpu_vs_oracle_on_sample"]["dq_rel"] < 1e-6
+
+
+def test_sclk_reading(tmp_path):
+    """The current core clock is the starred level of pp_dpm_sclk; the peak scales
+    linearly from the 2.4 GHz spec clock."""
+    p = tmp_path / "pp_dpm_sclk"
+    p.write_text("0: 500Mhz\n1: 2105Mhz *\n2: 2400Mhz\n")
+    assert bench.read_sclk_mhz(str(p)) == 2105.0
+    p.write_text("0: 500Mhz\n1: 157Mhz\n2: 2400Mhz *\n")
+    assert bench.read_sclk_mhz(str(p)) == 2400.0
+    p.write_text("garbage\n")
+    assert bench.read_sclk_mhz(str(p)) is None
+    assert bench.read_sclk_mhz(str(tmp_path / "missing")) is None
+    assert bench.peak_at_clock(2516.6, 2.1) == pytest.approx(2516.6 * 2.1 / 2.4)
+    assert bench.peak_at_clock(2516.6, None) is None
+
+
+def test_clock_sampler_without_sysfs(monkeypatch):
+    monkeypatch.setattr(bench, "sclk_path", lambda: None)
+    c = bench.ClockSampler()
+    c.start()
+    c.stop()
+    rec = c.record()
+    assert rec["source"] == "unavailable" and rec["during_mhz"] is None
+    assert not c.median_ghz()
