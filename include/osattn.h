@@ -3,9 +3,10 @@
  *
  * C ABI.  Plain device pointers and integer sizes; no C++ or framework types.
  * Every entry point only enqueues work on the given HIP stream and returns; it
- * never synchronises, never allocates device memory and keeps no global state,
- * so calls are re-entrant.  Faults inside a kernel surface at the caller's next
- * synchronisation on that stream.
+ * never synchronises and never allocates device memory.  All but one keep no
+ * global state, so calls are re-entrant; the exception, attn_bwd_noalloc, keeps its
+ * workspace in a fixed device array per GPU (see its comment).  Faults inside a
+ * kernel surface at the caller's next synchronisation on that stream.
  *
  * Operation (FlashAttention-2 page, "Standard Attention" and the FA2 inner loop;
  * ml-notes page, why scores are divided by sqrt(d)):
@@ -56,7 +57,8 @@ typedef enum {
   ATTN_ERR_SCALE = -6,     /* scale not finite or not > 0                                */
   ATTN_ERR_ALIGN = -7,     /* a tensor base address is not 16-byte aligned               */
   ATTN_ERR_WORKSPACE = -8, /* workspace NULL or smaller than attn_bwd_workspace_bytes()  */
-  ATTN_ERR_LAUNCH = -9     /* the HIP runtime rejected a kernel launch                   */
+  ATTN_ERR_LAUNCH = -9,    /* the HIP runtime rejected a kernel launch                   */
+  ATTN_ERR_SCRATCH = -10   /* attn_bwd_noalloc: problem needs more than its fixed scratch */
 } attn_status_t;
 
 /*
@@ -254,6 +256,28 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
                  int Hkv, int N, int d, float scale, float descale_q, float descale_k,
                  float descale_v, int causal, void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/*
+ * Allocation-free backward, for callers that cannot allocate device memory or hand
+ * in a workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, results and return codes as attn_bwd without
+ * the workspace: it launches the same three kernels, their workspace (D and
+ * LSE * log2(e)) placed in a fixed device array of ATTN_NOALLOC_SCRATCH_BYTES inside
+ * the library.  Each GPU the library runs on holds its own copy of that array from
+ * the library's load until the process ends; the first call on a GPU looks up its
+ * address there (with that GPU current).  The call allocates nothing (no hipMalloc,
+ * no allocating library routine).
+ * Limit: attn_bwd_workspace_bytes() <= ATTN_NOALLOC_SCRATCH_BYTES, i.e. B * H * N
+ * <= 4194304 query rows; a larger problem returns ATTN_ERR_SCRATCH and launches
+ * nothing.  The array needs no clearing (every call writes all it reads), but all
+ * calls on one GPU share it: calls that may overlap in time on the same GPU (other
+ * streams, other host threads) race, and the caller must serialise them.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                     int B, int H, int Hkv, int N, int d, float scale, int causal,
+                     int dtype, void* stream);
 
 /* A static, human-readable name for a status code. */
 const char* attn_status_string(int status);

@@ -40,6 +40,7 @@ __all__ = [
     "attn_bwd_preprocess",
     "attn_bwd_dkdv",
     "attn_bwd_dq",
+    "attn_bwd_noalloc",
     "new_bwd_workspace",
     "attn_fwd_splitkv",
     "attn_fwd_splitkv_workspace_bytes",
@@ -74,6 +75,7 @@ STATUS = {
     "ATTN_ERR_ALIGN": -7,
     "ATTN_ERR_WORKSPACE": -8,
     "ATTN_ERR_LAUNCH": -9,
+    "ATTN_ERR_SCRATCH": -10,
 }
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
@@ -82,7 +84,7 @@ EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_prepro
             "attn_fwd_masked", "attn_bwd_masked", "attn_bwd_masked_workspace_bytes",
             "attn_fwd_fp8", "attn_fwd_fp8_workspace_bytes",
             "rowsoftmax_fwd", "rowsoftmax_bwd", "rowxent_fwd", "rowxent_bwd",
-            "attn_status_string")
+            "attn_bwd_noalloc", "attn_status_string")
 
 _lib = None
 
@@ -112,6 +114,8 @@ def library() -> ctypes.CDLL:
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp,
                              ctypes.c_size_t, vp]
     lib.attn_bwd.restype = i
+    lib.attn_bwd_noalloc.argtypes = [vp] * 9 + [i, i, i, i, i, f, i, i, vp]
+    lib.attn_bwd_noalloc.restype = i
     sz = ctypes.c_size_t
     lib.attn_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
     lib.attn_bwd_preprocess.restype = i
@@ -250,6 +254,8 @@ def _bwd_checked(q, k, v, o, lse, do, scale, dq, dk, dv, workspace):
         _check_dev(name, t, q.dtype)
         if t.shape != ref.shape:
             raise ValueError(f"{name} has the wrong shape")
+    if workspace is False:  # no workspace taken (the allocation-free call)
+        return (B, H, Hkv, N, d), float(scale), dq, dk, dv, None
     if workspace is None:
         workspace = new_bwd_workspace(q, k)
     _check_dev("workspace", workspace)
@@ -281,6 +287,24 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
                       ws.data_ptr(), _ws_bytes(ws), _stream_handle(q.device))
     if st != 0:
         raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
+
+
+@_one_device
+def attn_bwd_noalloc(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
+                     dq=None, dk=None, dv=None):
+    """attn_bwd without a workspace: the library keeps it in a fixed device array per
+    GPU (B*H*N up to 4194304 query rows).  Pass dq, dk, dv to have nothing allocated
+    here either.  Calls that may overlap in time on one GPU race on that array."""
+    lib = library()
+    (B, H, Hkv, N, d), scale, dq, dk, dv, _ = _bwd_checked(q, k, v, o, lse, do, scale, dq, dk,
+                                                           dv, False)
+    st = lib.attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), B, H, Hkv, N, d, scale, int(bool(causal)),
+                              DTYPE_CODES[q.dtype], _stream_handle(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/osattn.h"
 #include "launch.h"
@@ -141,6 +142,58 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
                                      osattn::kStageDkdv | osattn::kStageDq);
   if (osattn::launch_bwd_preprocess(a) != hipSuccess) return ATTN_ERR_LAUNCH;
   return run_bwd_kernels(a);
+}
+
+// ---- allocation-free backward ---------------------------------------------------
+// The workspace of attn_bwd_noalloc lives in this fixed device array; every GPU that
+// loads the library holds its own copy until the process ends.  Host code never
+// passes the array's name to a kernel or a copy (on the host it is only a stand-in
+// for the symbol): it uses the device address looked up per device below.
+extern "C++" {
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first call
+// made with that device current and kept for the process's lifetime.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_ERR_LAUNCH;
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+}  // extern "C++"
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dO, void* dq, void* dk, void* dv, int B,
+                     int H, int Hkv, int N, int d, float scale, int causal, int dtype,
+                     void* stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  int st = validate_sizes(B, H, Hkv, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  st = validate_scale(scale);
+  if (st != ATTN_OK) return st;
+  if (causal != 0 && causal != 1) return ATTN_ERR_SHAPE;
+  if (attn_bwd_workspace_bytes(B, H, Hkv, N, d, dtype) > ATTN_NOALLOC_SCRATCH_BYTES)
+    return ATTN_ERR_SCRATCH;
+  if (!aligned_all({q, k, v, o, lse, dO, dq, dk, dv})) return ATTN_ERR_ALIGN;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != ATTN_OK) return st;
+  return attn_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dtype, ws,
+                  ATTN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int attn_bwd_preprocess(const void* o, const float* lse, const void* dO, int B, int H, int Hkv,
@@ -459,6 +512,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_ALIGN: return "tensor base address not 16-byte aligned";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_SCRATCH: return "problem too large for the allocation-free backward's fixed scratch (B*H*N > 4194304)";
     default: return "unknown status";
   }
 }

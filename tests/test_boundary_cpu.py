@@ -114,6 +114,43 @@ def test_bwd_rejects(kw, code):
     assert bwd(**kw) == S[code]
 
 
+def bwd_noalloc(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, Hkv=1, N=8, d=64,
+             scale=0.125, causal=0, dtype=2, stream=None)
+    a.update(kw)
+    return osa.library().attn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"],
+                                          a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["Hkv"],
+                                          a["N"], a["d"], a["scale"], a["causal"], a["dtype"],
+                                          a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q": None}, "ATTN_ERR_NULL"),
+    ({"dv": None}, "ATTN_ERR_NULL"),
+    ({"N": 0}, "ATTN_ERR_SHAPE"),
+    ({"causal": 2}, "ATTN_ERR_SHAPE"),
+    ({"d": 96}, "ATTN_ERR_HEAD_DIM"),
+    ({"H": 3, "Hkv": 2}, "ATTN_ERR_GQA"),
+    ({"dtype": 7}, "ATTN_ERR_DTYPE"),
+    ({"scale": float("nan")}, "ATTN_ERR_SCALE"),
+    ({"scale": 0.0}, "ATTN_ERR_SCALE"),
+    ({"dk": P + 8}, "ATTN_ERR_ALIGN"),
+    # one query row over the 4194304 the fixed scratch holds (two float32 per row)
+    ({"B": 1, "H": 1, "Hkv": 1, "N": 4194305}, "ATTN_ERR_SCRATCH"),
+    ({"B": 2, "H": 64, "Hkv": 8, "N": 32769}, "ATTN_ERR_SCRATCH"),
+])
+def test_bwd_noalloc_rejects(kw, code):
+    """Every invalid argument, and any problem larger than the fixed scratch, is
+    refused before the device is asked for anything."""
+    assert bwd_noalloc(**kw) == S[code]
+
+
+def test_noalloc_scratch_limit_matches_workspace_formula():
+    f = osa.library().attn_bwd_workspace_bytes
+    assert f(1, 1, 1, 4194304, 64, 2) == 32 << 20      # the largest problem it takes
+    assert f(1, 1, 1, 4194305, 64, 2) > 32 << 20
+
+
 def pre(**kw):
     a = dict(o=P, lse=P, do=P, B=1, H=2, Hkv=1, N=8, d=64, dtype=2, ws=P, ws_bytes=1 << 20,
              stream=None)
