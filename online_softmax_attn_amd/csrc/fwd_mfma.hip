@@ -58,7 +58,7 @@ struct FwdCfg {
 
 template <typename T, int D, int NW, int QB, int NBUF, int BC, bool CAUSAL, bool MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64)))
-__attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                      float* __restrict__ LSE, int H, int Hkv, int Nq, int Nk, int n_qtiles,
@@ -461,12 +461,48 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
 #define OSATTN_FWD_BC 128
 #endif
 
+// d = 64 has its own tile shapes: the smaller Q fragments and O accumulators leave
+// room for two 32-row blocks per wave at two waves per SIMD (every shape here runs
+// two waves per SIMD: one workgroup of 8 waves or two of 4 per CU).
+#ifndef OSATTN_FWD64_NW
+#define OSATTN_FWD64_NW 8
+#endif
+#ifndef OSATTN_FWD64C_NW
+#define OSATTN_FWD64C_NW 8
+#endif
+#ifndef OSATTN_FWD64C_QB
+#define OSATTN_FWD64C_QB 1
+#endif
+#ifndef OSATTN_FWD64C_NBUF
+#define OSATTN_FWD64C_NBUF 2
+#endif
+#ifndef OSATTN_FWD64C_BC
+#define OSATTN_FWD64C_BC 128
+#endif
+#ifndef OSATTN_FWD64_QB
+#define OSATTN_FWD64_QB 2
+#endif
+#ifndef OSATTN_FWD64_NBUF
+#define OSATTN_FWD64_NBUF 2
+#endif
+#ifndef OSATTN_FWD64_BC
+#define OSATTN_FWD64_BC 64
+#endif
+
 template <typename T, int D>
 static hipError_t launch_fwd_d(const FwdArgs& a) {
   constexpr int NW = OSATTN_FWD_NW, QB = OSATTN_FWD_QB, NB = OSATTN_FWD_NBUF, BC = OSATTN_FWD_BC;
   if (a.kv_lo) return launch_fwd_t<T, D, NW, QB, NB, BC, false, true>(a);
-  if (a.causal) return launch_fwd_t<T, D, NW, QB, NB, BC, true, false>(a);
-  return launch_fwd_t<T, D, NW, QB, NB, BC, false, false>(a);
+  if constexpr (D == 64) {
+    if (a.causal)
+      return launch_fwd_t<T, D, OSATTN_FWD64C_NW, OSATTN_FWD64C_QB, OSATTN_FWD64C_NBUF,
+                          OSATTN_FWD64C_BC, true, false>(a);
+    return launch_fwd_t<T, D, OSATTN_FWD64_NW, OSATTN_FWD64_QB, OSATTN_FWD64_NBUF,
+                        OSATTN_FWD64_BC, false, false>(a);
+  } else {
+    if (a.causal) return launch_fwd_t<T, D, NW, QB, NB, BC, true, false>(a);
+    return launch_fwd_t<T, D, NW, QB, NB, BC, false, false>(a);
+  }
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a) {
