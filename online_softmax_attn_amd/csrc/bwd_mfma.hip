@@ -180,7 +180,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  // Interval masks: K/V-head groups dealt over the XCDs (see the forward).
+  const int L = (OSATTN_XCD_GROUPS && IMASK) ? xcd_group_remap(blockIdx.x, gridDim.x, n_ktiles)
+                                             : xcd_remap(blockIdx.x, gridDim.x);
   const int kt = L % n_ktiles;
   const int bg = L / n_ktiles;  // b * Hkv + kvh
   const int kvh = bg % Hkv;
@@ -801,10 +803,13 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int L = (OSATTN_XCD_GROUPS && IMASK)
+                    ? xcd_group_remap(blockIdx.x, gridDim.x, n_qtiles * (H / Hkv))
+                    : xcd_remap(blockIdx.x, gridDim.x);
   int qt = L % n_qtiles;
   const int bh = L / n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
+  // Longest rows first (causal, and the usual interval masks: see the forward).
+  if (CAUSAL || (OSATTN_MASK_LONGEST_FIRST && IMASK)) qt = n_qtiles - 1 - qt;
   const int h = bh % H;
   const int b = bh / H;
   const int kvh = h / (H / Hkv);

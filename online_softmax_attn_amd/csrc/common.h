@@ -178,4 +178,32 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid & 7) * per + (bid >> 3);
 }
 
+// Workgroup order of the interval-masked attention kernels: 1 deals K/V-head groups to
+// the XCDs round-robin (xcd_group_remap), 0 gives each XCD one contiguous block
+// (xcd_remap, which the other kernels always use).
+#ifndef OSATTN_XCD_GROUPS
+#define OSATTN_XCD_GROUPS 1
+#endif
+// Interval-masked forward and dQ take their query tiles last-first (as causal does).
+#ifndef OSATTN_MASK_LONGEST_FIRST
+#define OSATTN_MASK_LONGEST_FIRST 1
+#endif
+
+// As xcd_remap, but over "groups" of consecutive logical tiles (a head, or the query
+// heads sharing a K/V head, with all their tiles): when the group count is a multiple of
+// 8, XCD x receives the groups g = x, x + 8, x + 16, ... (each one's tiles in order,
+// for its L2), instead of one contiguous block of groups.  Work that differs between
+// groups (packed documents of different lengths per batch entry, say) is then dealt
+// over the XCDs instead of piling onto some.  Returns the logical tile index
+// g * group_tiles + t.  Other group counts fall back to xcd_remap.
+__device__ __forceinline__ int xcd_group_remap(int bid, int nblocks, int group_tiles) {
+  const int L = xcd_remap(bid, nblocks);
+  const int groups = nblocks / group_tiles;
+  if (groups % 8 != 0 || groups * group_tiles != nblocks) return L;
+  const int per_xcd = (groups / 8) * group_tiles;  // tiles of one residue class
+  const int r = L / per_xcd;                       // = the XCD, for L from xcd_remap
+  const int w = L % per_xcd;
+  return ((w / group_tiles) * 8 + r) * group_tiles + w % group_tiles;
+}
+
 }  // namespace osattn

@@ -87,10 +87,16 @@ void fwd_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  // Interval masks can give the K/V-head groups very different amounts of work (packed
+  // documents differ per batch entry): deal the groups over the XCDs.
+  const int L = (OSATTN_XCD_GROUPS && MASK)
+                    ? xcd_group_remap(blockIdx.x, gridDim.x, n_qtiles * (H / Hkv))
+                    : xcd_remap(blockIdx.x, gridDim.x);
   int qt = L % n_qtiles;
   const int bh = L / n_qtiles;  // b * H + h
-  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
+  // Longest rows first: under a causal mask, and under interval masks, whose usual
+  // forms (causal, windows, documents) give later rows at least as many keys.
+  if (CAUSAL || (OSATTN_MASK_LONGEST_FIRST && MASK)) qt = n_qtiles - 1 - qt;
   const int h = bh % H;
   const int b = bh / H;
   const int kvh = h / (H / Hkv);
