@@ -26,8 +26,10 @@ preprocess) per launch / mean launch time (the figure a rocprofv3 kernel trace's
 average duration reproduces), against the dense bf16/fp16 MFMA peak of 2516.6
 TFLOP/s (256 CUs x 4096 flop/clk x 2.4 GHz) or HBM's 8 TB/s, and, for the MFMA
 kernels, against the same peak at the core clock measured during the timed steps
-(``sclk``: the current level of amdgpu's pp_dpm_sclk, read before, every 5 ms
-during, and after the timed loop).  ``roofline`` repeats the entry of the kernel
+(``sclk``: the current level of amdgpu's pp_dpm_sclk, read every 5 ms from the start
+of the warm-up; that level lags the load, so only samples from the timed steps taken
+at least 0.3 s after the warm-up began give the clock, and a shorter run gives no
+clock-referenced fraction).  ``roofline`` repeats the entry of the kernel
 with the largest share of the step.  ``traffic`` is the HBM bytes per launch from
 committed rocprofv3 counter runs, or null once the kernel source has changed since
 they were taken.  ``cpu_baseline`` times the fp64 oracle on the host for a bounded
@@ -693,34 +695,49 @@ def read_sclk_mhz(path):
     return None
 
 
-class ClockSampler:
-    """Reads the current core clock before, during (every `period` seconds, from a
-    thread) and after the timed region.  The clock under load is what the matrix
-    cores run at; the spec peak assumes 2.4 GHz."""
+SCLK_SETTLE_S = 0.3  # seconds of load before the sysfs clock level is taken as settled
 
-    def __init__(self, period: float = 0.005):
-        import threading
+
+class ClockSampler:
+    """Reads the current core clock (every `period` seconds, from a thread) from the
+    start of the warm-up to the end of the timed region.  The clock under load is what
+    the matrix cores run at; the spec peak assumes 2.4 GHz.  The sysfs level lags the
+    load: it climbs for a couple of hundred milliseconds after work starts while the
+    kernels already run at full speed (the same kernel timed the same at readings of
+    1200 and 2228 MHz), so only samples taken SCLK_SETTLE_S or more after the load
+    began, and inside the timed region, count as the measured clock."""
+
+    def __init__(self, period: float = 0.005, settle_s: float = SCLK_SETTLE_S):
         self.path = sclk_path()
         self.period = period
-        self.samples = []
+        self.settle_s = settle_s
+        self.samples = []  # (seconds since start, MHz)
         self.before = self.after = None
-        self._stop = threading.Event()
+        self.t_start = self.t_timed = None
+        self._stop = None
         self._thread = None
 
     def start(self):
+        """Call when the load begins (before the warm-up)."""
         import threading
+        self.t_start = time.perf_counter()
         if not self.path:
             return
         self.before = read_sclk_mhz(self.path)
+        self._stop = threading.Event()
 
         def run():
             while not self._stop.is_set():
                 v = read_sclk_mhz(self.path)
                 if v is not None:
-                    self.samples.append(v)
+                    self.samples.append((time.perf_counter() - self.t_start, v))
                 self._stop.wait(self.period)
         self._thread = threading.Thread(target=run, daemon=True)
         self._thread.start()
+
+    def mark_timed(self):
+        """Call where the timed region begins."""
+        self.t_timed = time.perf_counter() - (self.t_start or time.perf_counter())
 
     def stop(self):
         if self._thread is not None:
@@ -729,18 +746,33 @@ class ClockSampler:
         if self.path:
             self.after = read_sclk_mhz(self.path)
 
+    def timed_samples(self):
+        t0 = self.t_timed or 0.0
+        return [v for t, v in self.samples if t >= t0]
+
+    def settled_samples(self):
+        t0 = max(self.t_timed or 0.0, self.settle_s)
+        return [v for t, v in self.samples if t >= t0]
+
     def record(self):
-        """{'source', 'before_mhz', 'after_mhz', 'during_mhz': {median, min, max, n}}."""
+        """{'source', 'before_mhz', 'after_mhz', 'during_mhz': all samples of the timed
+        region, 'settled_mhz': those at least settle_s into the load (the clock used)}."""
         out = {"source": self.path or "unavailable", "before_mhz": self.before,
-               "after_mhz": self.after, "during_mhz": None}
-        if self.samples:
-            st = stats(self.samples)
-            out["during_mhz"] = {"median": st["median"], "min": st["min"],
-                                 "max": max(self.samples), "n": len(self.samples)}
+               "after_mhz": self.after, "during_mhz": None, "settled_mhz": None,
+               "settle_s": self.settle_s}
+        for key, vals in (("during_mhz", self.timed_samples()), ("settled_mhz", self.settled_samples())):
+            if vals:
+                st = stats(vals)
+                out[key] = {"median": st["median"], "min": st["min"], "max": max(vals), "n": len(vals)}
+        if out["settled_mhz"] is None and self.path:
+            out["note"] = (f"timed region ended before {self.settle_s} s of load: the sysfs level "
+                           "had not settled, so no clock-referenced fraction is given")
         return out
 
     def median_ghz(self):
-        return self.samples and stats(self.samples)["median"] / 1000.0 or None
+        """Median settled clock in GHz, or None."""
+        vals = self.settled_samples()
+        return stats(vals)["median"] / 1000.0 if vals else None
 
 
 def peak_at_clock(peak_spec: float, ghz):
@@ -790,12 +822,6 @@ def run_one(w, args, osa, torch, with_cpu: bool):
     # Between steps (outside the timed region) a 512 MiB buffer is overwritten so that
     # no step finds the previous step's data in L2 or the MALL.
     flush = CacheFlush(torch, enabled=not getattr(args, "no_flush", False))
-    for _ in range(args.warmup):
-        flush()
-        for f in launches:
-            f()
-    torch.cuda.synchronize()
-
     # Events on the stream the library launches on (the binding passes torch's
     # current stream to every call).
     stream = torch.cuda.current_stream()
@@ -804,6 +830,12 @@ def run_one(w, args, osa, torch, with_cpu: bool):
     torch.cuda.synchronize()
     clock = ClockSampler()
     clock.start()
+    for _ in range(args.warmup):
+        flush()
+        for f in launches:
+            f()
+    torch.cuda.synchronize()
+    clock.mark_timed()
     t0 = time.perf_counter()
     for i in range(args.steps):
         flush()

@@ -191,3 +191,22 @@ def test_clock_sampler_without_sysfs(monkeypatch):
     rec = c.record()
     assert rec["source"] == "unavailable" and rec["during_mhz"] is None
     assert not c.median_ghz()
+
+
+def test_clock_sampler_uses_settled_samples(monkeypatch):
+    """The clock is the median of the samples inside the timed region that were taken
+    at least settle_s after the load began; with none, no clock is claimed."""
+    monkeypatch.setattr(bench, "sclk_path", lambda: None)
+    c = bench.ClockSampler(settle_s=0.3)
+    c.samples = [(0.0, 900.0), (0.1, 1200.0), (0.2, 1500.0), (0.35, 2100.0), (0.4, 2200.0),
+                 (0.45, 2000.0)]
+    c.t_timed = 0.15
+    assert c.timed_samples() == [1500.0, 2100.0, 2200.0, 2000.0]
+    assert c.settled_samples() == [2100.0, 2200.0, 2000.0]
+    assert c.median_ghz() == pytest.approx(2.1)
+    rec = c.record()
+    assert rec["settled_mhz"]["n"] == 3 and rec["during_mhz"]["n"] == 4
+    c.t_timed = 0.5  # timed region after every sample
+    assert c.median_ghz() is None and c.record()["settled_mhz"] is None
+    c.t_timed, c.samples = 0.0, [(0.0, 900.0), (0.29, 1200.0)]  # a run shorter than settle_s
+    assert c.median_ghz() is None
