@@ -177,7 +177,7 @@ def check_group_bwd(inp, outs, dtype, causal, scale, groups, label=""):
 
 def oracle_workers() -> int:
     """Threads for whole-problem oracle checks: the host cores this process may use,
-    at most 16 (a GPU machine's CPU share)."""
+    at most 16 (the host CPU share that comes with one GPU)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
