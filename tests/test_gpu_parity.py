@@ -143,6 +143,17 @@ def test_medium_ragged_two_block_tiles():
     check_group_bwd(inp, outs, "bf16", False, w.scale, [(0, 3)], label=w.name)
 
 
+def test_medium_ragged_wide_rows_d64():
+    """d = 64 non-causal with a grid of at least one 512-row workgroup per CU (so the
+    two-block-per-wave forward runs) and a ragged last tile."""
+    need_gpu()
+    w = S.custom("bf16", 4, 16, 16, 2500, 64, False, seed_base=8400)
+    inp = S.make_inputs(w)
+    outs = run_bwd(inp, False, w.scale)
+    check_sampled_fwd(inp, outs[0], outs[1], "bf16", False, w.scale, per_head=8, label=w.name)
+    check_group_bwd(inp, outs, "bf16", False, w.scale, [(2, 9)], label=w.name)
+
+
 def test_medium_ragged_causal_fp16():
     need_gpu()
     w = S.custom("fp16", 2, 16, 16, 4477, 64, True, seed_base=8300)
