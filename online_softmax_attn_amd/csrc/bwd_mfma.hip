@@ -162,20 +162,37 @@ struct DkdvCfg {
   static_assert(kCPW >= 1 && kChunks % kNW == 0, "tile must split evenly over the waves");
 };
 
+// Persistent grid (StaticSchedule) for the causal dK/dV, whose key tiles differ in
+// length.
+#ifndef OSATTN_DKDV_PERSIST
+#define OSATTN_DKDV_PERSIST 1
+#endif
+
+// dK/dV kernel arguments.
+struct DkdvKernelArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* dO;
+  const float* LSE2;
+  const float* Dv;
+  uint16_t* dK;
+  uint16_t* dV;
+  int H, Hkv, Nq, n_ktiles;
+  float scale, scale_log2;
+  const int* kv_lo;
+  const int* kv_hi;
+  const i32x4* tile_sum;
+  int Nk;          // keys (interval masks; otherwise equal to Nq)
+  int n_jobs;  // logical tiles (key tiles x K/V heads)
+  int pad_;
+};
+
 template <typename T, int D, int NBUF, bool CAUSAL, bool IMASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                     const float* __restrict__ LSE2, const float* __restrict__ Dv,
-                     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int H, int Hkv,
-                     int Nq, int n_ktiles, float scale, float scale_log2,
-                     const int* __restrict__ kv_lo, const int* __restrict__ kv_hi,
-                     const i32x4* __restrict__ tile_sum, int Nk_arg) {
-  // (New parameters go last: inserting one before the loop's scalar arguments has
-  // been seen to change register allocation enough to add DMA waits in the loop.)
-  // Keys and queries differ in number only under interval masks.
-  const int Nk = IMASK ? Nk_arg : Nq;
+void bwd_dkdv_kernel(const DkdvKernelArgs args) {
+  constexpr bool PERSIST = OSATTN_DKDV_PERSIST && CAUSAL && !IMASK;
   using C = DkdvCfg<D, NBUF>;
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
@@ -205,579 +222,610 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Interval masks: K/V-head groups dealt over the XCDs (see the forward).
-  const int L = (OSATTN_XCD_GROUPS && IMASK) ? xcd_group_remap(blockIdx.x, gridDim.x, n_ktiles)
-                                             : xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = L % n_ktiles;
-  const int bg = L / n_ktiles;  // b * Hkv + kvh
-  const int kvh = bg % Hkv;
-  const int b = bg / Hkv;
-  const int n_rep = H / Hkv;
-  const int k0 = kt * C::kKeys;
-  const int kw = k0 + 32 * KB * wave;  // first key of this wave
-
-  const uint32_t q_bytes = (uint32_t)Nq * C::kRowBytes;
-  const uint32_t kv_bytes = (uint32_t)Nk * C::kRowBytes;
-  const auto rk = make_rsrc(K + (size_t)bg * Nk * D, kv_bytes);
-  const auto rv = make_rsrc(V + (size_t)bg * Nk * D, kv_bytes);
-
-  // K and V rows of this wave (B operands of S = Q K^T and dP = dO V^T).
-  vec8 kf[KB][D / 16], vf[KB][D / 16];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const uint32_t rowoff = (uint32_t)(kw + 32 * kb + l32) * C::kRowBytes;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      kf[kb][c] = as_vec8<T>(buffer_load16(rk, rowoff + (16 * c + 8 * hi) * 2));
-      vf[kb][c] = as_vec8<T>(buffer_load16(rv, rowoff + (16 * c + 8 * hi) * 2));
-    }
+  // Logical tile L: key tile L % n_ktiles of K/V head L / n_ktiles (the key tiles of a
+  // head longest first).  A persistent grid (causal) walks its schedule (see
+  // StaticSchedule); otherwise each workgroup runs one tile.
+  StaticSchedule sched(args.n_jobs, blockIdx.x, gridDim.x);
+  int L;
+  if constexpr (PERSIST) {
+    L = sched.next();
+  } else {
+    // Interval masks: K/V-head groups dealt over the XCDs (see the forward).
+    L = (OSATTN_XCD_GROUPS && IMASK) ? xcd_group_remap(blockIdx.x, gridDim.x, args.n_ktiles)
+                                     : xcd_remap(blockIdx.x, gridDim.x);
   }
+  while (L >= 0) {
+    // Arguments read afresh for each tile of a persistent grid (see the forward).
+    const DkdvKernelArgs a = PERSIST ? fresh_kernel_args<DkdvKernelArgs>() : args;
+    const uint16_t* __restrict__ Q = a.Q;
+    const uint16_t* __restrict__ K = a.K;
+    const uint16_t* __restrict__ V = a.V;
+    const uint16_t* __restrict__ dO = a.dO;
+    const float* __restrict__ LSE2 = a.LSE2;
+    const float* __restrict__ Dv = a.Dv;
+    uint16_t* __restrict__ dK = a.dK;
+    uint16_t* __restrict__ dV = a.dV;
+    const int H = a.H, Hkv = a.Hkv, Nq = a.Nq, n_ktiles = a.n_ktiles;
+    const float scale = a.scale, scale_log2 = a.scale_log2;
+    const int* __restrict__ kv_lo = a.kv_lo;
+    const int* __restrict__ kv_hi = a.kv_hi;
+    const i32x4* __restrict__ tile_sum = a.tile_sum;
+    // Keys and queries differ in number only under interval masks.
+    const int Nk = IMASK ? a.Nk : Nq;
+    const int kt = L % n_ktiles;
+    const int bg = L / n_ktiles;  // b * Hkv + kvh
+    const int kvh = bg % Hkv;
+    const int b = bg / Hkv;
+    const int n_rep = H / Hkv;
+    const int k0 = kt * C::kKeys;
+    const int kw = k0 + 32 * KB * wave;  // first key of this wave
 
-  f32x16 dk_acc[KB][D / 32], dv_acc[KB][D / 32];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dk_acc[kb][t][r] = 0.f;
-        dv_acc[kb][t][r] = 0.f;
-      }
+    const uint32_t q_bytes = (uint32_t)Nq * C::kRowBytes;
+    const uint32_t kv_bytes = (uint32_t)Nk * C::kRowBytes;
+    const auto rk = make_rsrc(K + (size_t)bg * Nk * D, kv_bytes);
+    const auto rv = make_rsrc(V + (size_t)bg * Nk * D, kv_bytes);
 
-  // Query tiles that see these keys: all of them, or (causal) from the diagonal on,
-  // or (interval masks) the first through the last tile whose rows' intervals meet
-  // this workgroup's keys, from the per-tile summaries (min lo, max hi, max lo, min hi).
-  const int n_qt = (Nq + C::kQT - 1) / C::kQT;
-  int qt_first = CAUSAL ? (k0 / C::kQT) : 0;
-  int per_head = n_qt - qt_first;
-  if constexpr (IMASK) {
-    const int key_hi = min(Nk, k0 + C::kKeys) - 1;
-    int f = n_qt, l = -1;
-    for (int t = lane; t < n_qt; t += 64) {
-      const i32x4 sm = tile_sum[(size_t)b * n_qt + t];
-      if (sm[0] <= key_hi && sm[1] >= k0) {
-        f = min(f, t);
-        l = max(l, t);
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      f = min(f, __shfl_xor(f, off));
-      l = max(l, __shfl_xor(l, off));
-    }
-    // (Equal in every lane after the reduction; read from lane 0 so that the loop's
-    // trip count and its wait choices are scalar.)
-    qt_first = __builtin_amdgcn_readfirstlane(l >= 0 ? f : 0);
-    per_head = __builtin_amdgcn_readfirstlane(l >= 0 ? l - f + 1 : 0);
-  }
-  const int n_iter = per_head * n_rep;
-
-  // LDS-DMA offsets: chunk ch of a tile holds tile row off / kRowBytes, physical
-  // granule pg, i.e. logical granule pg ^ swizzle(row).
-  uint32_t goff[C::kCPW];
-#pragma unroll
-  for (int i = 0; i < C::kCPW; ++i) {
-    const int off = (wave * C::kCPW + i) * 1024 + lane * 16;
-    const int row = off / C::kRowBytes;
-    const int pg = (off % C::kRowBytes) / 16;
-    goff[i] = row * C::kRowBytes + ((pg ^ bwd_swz<D>(row)) * 16);
-  }
-  const uint32_t lane4 = (uint32_t)lane * 4;  // per-lane offset of the 4-byte row loads
-  auto issue = [&](int it, uint16_t* lq, uint16_t* ld, float* ll, float* lD, int* lm)
-      __attribute__((always_inline)) {
-    const int r = it / per_head;
-    const uint32_t i0 = (uint32_t)(qt_first + it % per_head) * C::kQT;
-    const size_t bh = (size_t)b * H + kvh * n_rep + r;
-    const auto rq = make_rsrc(Q + bh * Nq * D, q_bytes);
-    const auto rd = make_rsrc(dO + bh * Nq * D, q_bytes);
-#pragma unroll
-    for (int i = 0; i < C::kCPW; ++i) {
-      const int ch = wave * C::kCPW + i;
-      buffer_load16_lds(rq, lq + ch * 512, goff[i], i0 * C::kRowBytes);
-      buffer_load16_lds(rd, ld + ch * 512, goff[i], i0 * C::kRowBytes);
-    }
-    if (wave == 0) {  // 64 rows x 4 bytes of LSE*log2(e) and D; rows >= Nq read zero
-      const auto rl = make_rsrc(LSE2 + bh * Nq, (uint32_t)Nq * 4);
-      const auto rD = make_rsrc(Dv + bh * Nq, (uint32_t)Nq * 4);
-      buffer_load4_lds(rl, ll, lane4, i0 * 4);
-      buffer_load4_lds(rD, lD, lane4, i0 * 4);
-      if constexpr (IMASK) {  // and the rows' key intervals
-        const auto rlo = make_rsrc(kv_lo + (size_t)b * Nq, (uint32_t)Nq * 4);
-        const auto rhi = make_rsrc(kv_hi + (size_t)b * Nq, (uint32_t)Nq * 4);
-        buffer_load4_lds(rlo, lm, lane4, i0 * 4);
-        buffer_load4_lds(rhi, lm + C::kQT, lane4, i0 * 4);
-        // The tile's summary comes through LDS too: read from global memory in the
-        // loop, it would need a vmcnt wait that also drains the prefetches in flight.
-        // (The tile offset goes into the per-lane offset, which the buffer's range check
-        // always covers: lanes past the last summary read zero.)
-        const auto rs = make_rsrc(tile_sum + (size_t)b * n_qt, (uint32_t)n_qt * 16);
-        buffer_load4_lds(rs, lm + 2 * C::kQT, lane4 + (i0 / C::kQT) * 16, 0);
-      }
-    }
-  };
-  // Outstanding loads per staged tile: 2 * kCPW per wave, and wave 0 also loads LSE
-  // and D (and the two interval arrays and the tile summary).
-  constexpr int kW0 = IMASK ? 5 : 2;
-
-  // LDS read offsets (bytes in a tile), loop-invariant per lane.
-  //  row-wise (A operand of S and dP): row 32qb + l32, logical granule 2c + hi
-  uint32_t roff[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) roff[c] = l32 * C::kRowBytes + (((2 * c + hi) ^ bwd_swz<D>(l32)) * 16);
-  //  transposed (A operands of dV^T and dK^T): rows 16cq + tr_row (+8), columns
-  //  32t + tr_col .. +3 (see common.h for the lane pattern of the transpose read)
-  const int tr_row = 4 * hi + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  //  The upper half (rows +8) has swizzle bwd_swz(row) ^ 2: granule bit 1, i.e. byte
-  //  bit 5 of the in-row offset, flips.
-  uint32_t toff[D / 32], toff8[D / 32];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
-    const int col = 32 * t + tr_col;
-    toff[t] = tr_row * C::kRowBytes + (((col >> 3) ^ bwd_swz<D>(tr_row)) * 16) + (col & 7) * 2;
-    toff8[t] = (tr_row + 8) * C::kRowBytes + (((col >> 3) ^ bwd_swz<D>(tr_row + 8)) * 16) + (col & 7) * 2;
-  }
-
-  // One staged tile of 64 query rows = two 32-row blocks.  The scores and dP of
-  // both blocks are issued first; the softmax-JVP arithmetic of block 0 then
-  // overlaps the MFMAs of block 1 and the dV/dK MFMAs of block 0 overlap the
-  // arithmetic of block 1.  Everything is one basic block (masking is a
-  // compile-time variant chosen per tile) so the scheduler can interleave.
-  // Variant for 32 keys per wave: one staged tile of 64 query rows, processed as
-  // two 32-row blocks.  For each block every LDS operand is requested before the
-  // instructions that consume it, with scheduling fences in between, so that LDS
-  // latency overlaps other work of the same wave (one wave per SIMD has nothing
-  // else to hide it):
-  //   row-wise Q/dO reads + LSE/D   | S, dP MFMAs
-  //   transposed Q/dO reads         | softmax-JVP arithmetic
-  //                                 | dV, dK MFMAs
-  auto compute_tile_fenced = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
-                          const float* lD, const int* lm) __attribute__((always_inline)) {
-    constexpr int MM = decltype(mask_c)::value;  // 0 none, 1 causal, 2 intervals
-#pragma unroll
-    for (int qb = 0; qb < C::kQT / 32; ++qb) {
-      // -- operand requests for S and dP
-      u32x4 aq[D / 16], ad[D / 16];
-#pragma unroll
+    // K and V rows of this wave (B operands of S = Q K^T and dP = dO V^T).
+    vec8 kf[KB][D / 16], vf[KB][D / 16];
+  #pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint32_t rowoff = (uint32_t)(kw + 32 * kb + l32) * C::kRowBytes;
+  #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        aq[c] = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
-        ad[c] = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
-      }
-      f32x4 lse4[4], d4[4];  // rows 32qb + 8g + 4hi + 0..3 for register group g
-      i32x4 lo4[4], hi4[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        lse4[g] = *(const f32x4*)&ll[32 * qb + 8 * g + 4 * hi];
-        d4[g] = *(const f32x4*)&lD[32 * qb + 8 * g + 4 * hi];
-        if constexpr (MM == 2) {
-          lo4[g] = *(const i32x4*)&lm[32 * qb + 8 * g + 4 * hi];
-          hi4[g] = *(const i32x4*)&lm[C::kQT + 32 * qb + 8 * g + 4 * hi];
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // -- S = Q K^T, dP = dO V^T (lane = key, register r = query row 8(r/4)+4hi+r%4)
-      f32x16 s[KB], dp[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[kb][r] = 0.f;
-          dp[kb][r] = 0.f;
-        }
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          s[kb] = M::mma32(as_vec8<T>(aq[c]), kf[kb][c], s[kb]);
-          dp[kb] = M::mma32(as_vec8<T>(ad[c]), vf[kb][c], dp[kb]);
-        }
-      // -- operand requests for dV^T and dK^T (transposed reads of the same tiles)
-      vec8 adt[2][D / 32], aqt[2][D / 32];
-#pragma unroll
-      for (int cq = 0; cq < 2; ++cq) {
-        const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          adt[cq][t] = join8<T>(lds_read_tr4(db_ + rowb + toff[t]), lds_read_tr4(db_ + rowb + toff8[t]));
-          aqt[cq][t] = join8<T>(lds_read_tr4(qb_ + rowb + toff[t]), lds_read_tr4(qb_ + rowb + toff8[t]));
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // -- P = exp2(S*c - LSE*log2e) (0 where masked), dS = P * (dP - D)
-      vec8 pp[2][KB], ps[2][KB];
-#pragma unroll
-      for (int cq = 0; cq < 2; ++cq)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int key = kw + 32 * kb + l32;
-          float p8[8], d8[8];
-#pragma unroll
-          for (int g2 = 0; g2 < 2; ++g2) {
-            const int g = 2 * cq + g2;
-            const int ql = 32 * qb + 8 * g + 4 * hi;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              float pv = fast_exp2(fmaf(s[kb][r], scale_log2, -lse4[g][e]));
-              if constexpr (MM == 1) {
-                if (key > i0 + ql + e) pv = 0.f;
-              } else if constexpr (MM == 2) {
-                if (key < lo4[g][e] || key > hi4[g][e]) pv = 0.f;
-              }
-              p8[4 * g2 + e] = pv;
-              d8[4 * g2 + e] = pv * (dp[kb][r] - d4[g][e]);
-            }
-          }
-          pp[cq][kb] = pack8<T>(p8);
-          ps[cq][kb] = pack8<T>(d8);
-        }
-      // -- dV^T += dO^T P ; dK^T += Q^T dS  (reduction over the 32 query rows)
-#pragma unroll
-      for (int cq = 0; cq < 2; ++cq)
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            dv_acc[kb][t] = M::mma32(adt[cq][t], pp[cq][kb], dv_acc[kb][t]);
-            dk_acc[kb][t] = M::mma32(aqt[cq][t], ps[cq][kb], dk_acc[kb][t]);
-          }
-    }
-  };
-  auto compute_tile_wide = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
-                          const float* lD, const int* lm) __attribute__((always_inline)) {
-    constexpr int MM = decltype(mask_c)::value;  // 0 none, 1 causal, 2 intervals
-    constexpr int NQB = C::kQT / 32;
-    // S = Q K^T, dP = dO V^T (lane = key, register r = query row 8(r/4)+4hi+r%4)
-    f32x16 s[NQB][KB], dp[NQB][KB];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[qb][kb][r] = 0.f;
-          dp[qb][kb][r] = 0.f;
-        }
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const u32x4 aq = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
-        const u32x4 ad = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          s[qb][kb] = M::mma32(as_vec8<T>(aq), kf[kb][c], s[qb][kb]);
-          dp[qb][kb] = M::mma32(as_vec8<T>(ad), vf[kb][c], dp[qb][kb]);
-        }
-      }
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      // P = exp2(S*c - LSE*log2e) (0 where masked), dS = P * (dP - D)
-#pragma unroll
-      for (int cq = 0; cq < 2; ++cq) {
-        vec8 pp[KB], ps[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int key = kw + 32 * kb + l32;
-          float p8[8], d8[8];
-#pragma unroll
-          for (int g2 = 0; g2 < 2; ++g2) {
-            const int ql = 32 * qb + 16 * cq + 8 * g2 + 4 * hi;  // local row of register 8cq+4g2
-            const f32x4 lse4 = *(const f32x4*)&ll[ql];
-            const f32x4 d4 = *(const f32x4*)&lD[ql];
-            i32x4 lo4 = {}, hi4 = {};
-            if constexpr (MM == 2) {
-              lo4 = *(const i32x4*)&lm[ql];
-              hi4 = *(const i32x4*)&lm[C::kQT + ql];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 8 * cq + 4 * g2 + e;
-              float pv = fast_exp2(fmaf(s[qb][kb][r], scale_log2, -lse4[e]));
-              if constexpr (MM == 1) {
-                if (key > i0 + ql + e) pv = 0.f;
-              } else if constexpr (MM == 2) {
-                if (key < lo4[e] || key > hi4[e]) pv = 0.f;
-              }
-              p8[4 * g2 + e] = pv;
-              d8[4 * g2 + e] = pv * (dp[qb][kb][r] - d4[e]);
-            }
-          }
-          pp[kb] = pack8<T>(p8);
-          ps[kb] = pack8<T>(d8);
-        }
-        // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over these 16 query rows)
-        const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          const vec8 adt = join8<T>(lds_read_tr4(db_ + rowb + toff[t]), lds_read_tr4(db_ + rowb + toff8[t]));
-          const vec8 aqt = join8<T>(lds_read_tr4(qb_ + rowb + toff[t]), lds_read_tr4(qb_ + rowb + toff8[t]));
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            dv_acc[kb][t] = M::mma32(adt, pp[kb], dv_acc[kb][t]);
-            dk_acc[kb][t] = M::mma32(aqt, ps[kb], dk_acc[kb][t]);
-          }
-        }
+        kf[kb][c] = as_vec8<T>(buffer_load16(rk, rowoff + (16 * c + 8 * hi) * 2));
+        vf[kb][c] = as_vec8<T>(buffer_load16(rv, rowoff + (16 * c + 8 * hi) * 2));
       }
     }
-  };
-  // Software-pipelined variant for 32 keys per wave.  Per 32-row block qb the work
-  // is G1 (S and dP: 16 MFMAs), J (the softmax-JVP arithmetic: about 130 VALU
-  // instructions) and G2 (dV and dK: 16 MFMAs).  With one wave per SIMD nothing
-  // else hides J, so the tile runs
-  //   G1(0) | G1(1) with J(0) | G2(0) with J(1) | G2(1)
-  // and scheduling groups interleave the VALU work between the MFMAs of the same
-  // phase (MFMA and VALU of one wave overlap when they are independent).
-  struct RowOps {
-    u32x4 aq[D / 16], ad[D / 16];
-    f32x4 lse4[4], d4[4];  // rows 32qb + 8g + 4hi + 0..3 for register group g
-  };
-  struct TrOps {
-    vec8 adt[2][D / 32], aqt[2][D / 32];
-  };
-  auto read_rows = [&](RowOps& o, int qb, const char* qb_, const char* db_, const float* ll,
-                       const float* lD) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      o.aq[c] = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
-      o.ad[c] = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      o.lse4[g] = *(const f32x4*)&ll[32 * qb + 8 * g + 4 * hi];
-      o.d4[g] = *(const f32x4*)&lD[32 * qb + 8 * g + 4 * hi];
-    }
-  };
-  auto read_tr = [&](TrOps& o, int qb, const char* qb_, const char* db_)
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int cq = 0; cq < 2; ++cq) {
-      const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        o.adt[cq][t] = join8<T>(lds_read_tr4(db_ + rowb + toff[t]), lds_read_tr4(db_ + rowb + toff8[t]));
-        o.aqt[cq][t] = join8<T>(lds_read_tr4(qb_ + rowb + toff[t]), lds_read_tr4(qb_ + rowb + toff8[t]));
-      }
-    }
-  };
-  auto g1 = [&](const RowOps& o, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = 0.f;
-      dp[r] = 0.f;
-    }
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      s = M::mma32(as_vec8<T>(o.aq[c]), kf[0][c], s);
-      dp = M::mma32(as_vec8<T>(o.ad[c]), vf[0][c], dp);
-    }
-  };
-  auto jvp = [&](auto mask_c, int i0, int qb, const RowOps& o, const f32x16& s, const f32x16& dp,
-                 vec8 (&pp)[2], vec8 (&ps)[2], const int* lm) __attribute__((always_inline)) {
-    constexpr int MM = decltype(mask_c)::value;  // 0 none, 1 causal, 2 intervals
-    const int key = kw + l32;
-#pragma unroll
-    for (int cq = 0; cq < 2; ++cq) {
-      float p8[8], d8[8];
-#pragma unroll
-      for (int g2 = 0; g2 < 2; ++g2) {
-        const int g = 2 * cq + g2;
-        const int ql = 32 * qb + 8 * g + 4 * hi;
-        i32x4 lo4 = {}, hi4 = {};  // the rows' key intervals (interval masks only)
-        if constexpr (MM == 2) {
-          lo4 = *(const i32x4*)&lm[ql];
-          hi4 = *(const i32x4*)&lm[C::kQT + ql];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pv = fast_exp2(fmaf(s[r], scale_log2, -o.lse4[g][e]));
-          if constexpr (MM == 1) {
-            if (key > i0 + ql + e) pv = 0.f;
-          } else if constexpr (MM == 2) {
-            if (key < lo4[e] || key > hi4[e]) pv = 0.f;
-          }
-          p8[4 * g2 + e] = pv;
-          d8[4 * g2 + e] = pv * (dp[r] - o.d4[g][e]);
-        }
-      }
-      pp[cq] = pack8<T>(p8);
-      ps[cq] = pack8<T>(d8);
-    }
-  };
-  auto g2 = [&](const TrOps& o, const vec8 (&pp)[2], const vec8 (&ps)[2])
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int cq = 0; cq < 2; ++cq)
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        dv_acc[0][t] = M::mma32(o.adt[cq][t], pp[cq], dv_acc[0][t]);
-        dk_acc[0][t] = M::mma32(o.aqt[cq][t], ps[cq], dk_acc[0][t]);
-      }
-  };
-  // One phase's interleave: n_ds LDS reads and n_v0 VALU first (to cover the first
-  // MFMA's operand latency), then 16 times one MFMA, ds_per LDS reads, v_per VALU.
-  auto interleave16 = [&](auto n_ds_c, auto n_v0_c, auto ds_per_c, auto v_per_c)
-      __attribute__((always_inline)) {
-    constexpr int kVALU = 0x2 | 0x400;  // VALU including transcendental
-    __builtin_amdgcn_sched_group_barrier(0x100, decltype(n_ds_c)::value, 0);
-    __builtin_amdgcn_sched_group_barrier(kVALU, decltype(n_v0_c)::value, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, decltype(ds_per_c)::value, 0);
-      __builtin_amdgcn_sched_group_barrier(kVALU, decltype(v_per_c)::value, 0);
-    }
-  };
-  auto compute_tile_pipe = [&](auto mask_c, int i0, const char* qb_, const char* db_,
-                               const float* ll, const float* lD, const int* lm)
-      __attribute__((always_inline)) {
-    using IC0 = std::integral_constant<int, 0>;
-    RowOps r0, r1;
-    TrOps t0, t1;
-    f32x16 s0, dp0, s1, dp1;
-    vec8 pp0[2], ps0[2], pp1[2], ps1[2];
-    // G1(0)
-    read_rows(r0, 0, qb_, db_, ll, lD);
-    g1(r0, s0, dp0);
-    __builtin_amdgcn_sched_barrier(0);
-    // G1(1) with J(0); block 0's transposed operands are requested here too
-    read_rows(r1, 1, qb_, db_, ll, lD);
-    read_tr(t0, 0, qb_, db_);
-    jvp(mask_c, i0, 0, r0, s0, dp0, pp0, ps0, lm);
-    g1(r1, s1, dp1);
-    interleave16(std::integral_constant<int, OSATTN_IL1_DS0>{}, std::integral_constant<int, OSATTN_IL1_V0>{},
-                 std::integral_constant<int, OSATTN_IL1_DS>{}, std::integral_constant<int, OSATTN_IL1_V>{});
-    __builtin_amdgcn_sched_barrier(0);
-    // G2(0) with J(1); block 1's transposed operands
-    read_tr(t1, 1, qb_, db_);
-    jvp(mask_c, i0, 1, r1, s1, dp1, pp1, ps1, lm);
-    g2(t0, pp0, ps0);
-    interleave16(std::integral_constant<int, 0>{}, std::integral_constant<int, OSATTN_IL2_V0>{},
-                 std::integral_constant<int, OSATTN_IL2_DS>{}, std::integral_constant<int, OSATTN_IL2_V>{});
-    __builtin_amdgcn_sched_barrier(0);
-    // G2(1)
-    g2(t1, pp1, ps1);
-    (void)IC0{};
-  };
-  auto compute_tile = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
-                          const float* lD, const int* lm) __attribute__((always_inline)) {
-    if constexpr (KB == 1) {
-      if constexpr (OSATTN_DKDV_PIPE) compute_tile_pipe(mask_c, i0, qb_, db_, ll, lD, lm);
-      else compute_tile_fenced(mask_c, i0, qb_, db_, ll, lD, lm);
-    } else {
-      compute_tile_wide(mask_c, i0, qb_, db_, ll, lD, lm);
-    }
-  };
-  using M0 = std::integral_constant<int, 0>;
-  using M1 = std::integral_constant<int, 1>;
-  using M2 = std::integral_constant<int, 2>;
-  auto compute = [&](int it, const char* qb_, const char* db_, const float* ll, const float* lD,
-                     const int* lm) __attribute__((always_inline)) {
-    const int tq = qt_first + it % per_head;
-    const int i0 = tq * C::kQT;
-    if constexpr (IMASK) {
-      // Skip the tile if no row's interval meets this wave's keys; mask it unless every
-      // row sees all of them.
-      const i32x4 smv = *(const i32x4*)(lm + 2 * C::kQT);
-      const int sm[4] = {__builtin_amdgcn_readfirstlane(smv[0]), __builtin_amdgcn_readfirstlane(smv[1]),
-                         __builtin_amdgcn_readfirstlane(smv[2]), __builtin_amdgcn_readfirstlane(smv[3])};
-      const int kw_last = kw + 32 * KB - 1;
-      if (sm[0] > kw_last || sm[1] < kw) return;
-      if (sm[2] <= kw && sm[3] >= kw_last) compute_tile(M0{}, i0, qb_, db_, ll, lD, lm);
-      else compute_tile(M2{}, i0, qb_, db_, ll, lD, lm);
-      return;
-    }
-    if (CAUSAL && i0 + C::kQT - 1 < kw) return;  // every key of this wave is after every row
-    // Causal: only tiles whose first row precedes this wave's last key need the mask.
-    if (CAUSAL && i0 < kw + 32 * KB - 1)
-      compute_tile(M1{}, i0, qb_, db_, ll, lD, lm);
-    else
-      compute_tile(M0{}, i0, qb_, db_, ll, lD, lm);
-  };
 
-  auto stage = [&](auto sc, auto fn) __attribute__((always_inline)) {
-    constexpr int S = decltype(sc)::value;
-    // The interval arrays only exist for interval masks (elsewhere they must not be
-    // referenced at all, or the compiler stops telling the stages' LDS apart).
-    int* const m0 = IMASK ? lm0 : nullptr;
-    int* const m1 = IMASK ? lm1 : nullptr;
-    int* const m2 = IMASK ? lm2 : nullptr;
-    int* const m3 = IMASK ? lm3 : nullptr;
-    if constexpr (S == 0) fn(lq0, ld0, ll0, lD0, m0);
-    else if constexpr (S == 1) fn(lq1, ld1, ll1, lD1, m1);
-    else if constexpr (S == 2) fn(lq2, ld2, ll2, lD2, m2);
-    else fn(lq3, ld3, ll3, lD3, m3);
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  if (0 < n_iter)
-    stage(I0{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) { issue(0, a, d, l, dd, mm); });
-  if (NBUF > 2 && 1 < n_iter)
-    stage(I1{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) { issue(1, a, d, l, dd, mm); });
-  if (NBUF > 3 && 2 < n_iter)
-    stage(I2{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) { issue(2, a, d, l, dd, mm); });
-
-  auto step = [&](auto sc, int it) __attribute__((always_inline)) {
-    constexpr int S = decltype(sc)::value;
-    constexpr int SN = (S + NBUF - 1) % NBUF;  // receives tile it + NBUF - 1
-    // Tile `it` has landed once at most the loads of the tiles issued after it
-    // (up to NBUF - 2 of them) are outstanding.
-    constexpr int kPer = 2 * C::kCPW;  // loads per tile and wave (+kW0 on wave 0)
-    const int ahead = min(NBUF - 2, n_iter - 1 - it);
-    if (NBUF > 3 && ahead >= 2) {
-      if (wave == 0) wait_vmcnt<2 * (kPer + kW0)>();
-      else wait_vmcnt<2 * kPer>();
-    } else if (NBUF > 2 && ahead >= 1) {
-      if (wave == 0) wait_vmcnt<kPer + kW0>();
-      else wait_vmcnt<kPer>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    block_barrier();
-    if (it + NBUF - 1 < n_iter)
-      stage(std::integral_constant<int, SN>{},
-            [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) {
-              issue(it + NBUF - 1, a, d, l, dd, mm);
-            });
-    stage(sc, [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) {
-      compute(it, (const char*)a, (const char*)d, l, dd, mm);
-    });
-  };
-  for (int it = 0; it < n_iter; it += NBUF) {
-    step(I0{}, it);
-    if (it + 1 < n_iter) step(I1{}, it + 1);
-    if constexpr (NBUF > 2)
-      if (it + 2 < n_iter) step(I2{}, it + 2);
-    if constexpr (NBUF > 3)
-      if (it + 3 < n_iter) step(std::integral_constant<int, 3>{}, it + 3);
-  }
-
-  // Store: lane = key, register r of tile t = column 32t + 8(r/4) + 4hi + r%4.
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int key = kw + 32 * kb + l32;
-    if (key < Nk) {
-      uint16_t* dkp = dK + ((size_t)bg * Nk + key) * D;
-      uint16_t* dvp = dV + ((size_t)bg * Nk + key) * D;
-#pragma unroll
+    f32x16 dk_acc[KB][D / 32], dv_acc[KB][D / 32];
+  #pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+  #pragma unroll
       for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 wk, wv;
-          wk[0] = (uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 0] * scale) |
-                  ((uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 1] * scale) << 16);
-          wk[1] = (uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 2] * scale) |
-                  ((uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 3] * scale) << 16);
-          wv[0] = (uint32_t)to_bits<T>(dv_acc[kb][t][4 * g + 0]) |
-                  ((uint32_t)to_bits<T>(dv_acc[kb][t][4 * g + 1]) << 16);
-          wv[1] = (uint32_t)to_bits<T>(dv_acc[kb][t][4 * g + 2]) |
-                  ((uint32_t)to_bits<T>(dv_acc[kb][t][4 * g + 3]) << 16);
-          *(u32x2*)(dkp + 32 * t + 8 * g + 4 * hi) = wk;
-          *(u32x2*)(dvp + 32 * t + 8 * g + 4 * hi) = wv;
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          dk_acc[kb][t][r] = 0.f;
+          dv_acc[kb][t][r] = 0.f;
         }
+
+    // Query tiles that see these keys: all of them, or (causal) from the diagonal on,
+    // or (interval masks) the first through the last tile whose rows' intervals meet
+    // this workgroup's keys, from the per-tile summaries (min lo, max hi, max lo, min hi).
+    const int n_qt = (Nq + C::kQT - 1) / C::kQT;
+    int qt_first = CAUSAL ? (k0 / C::kQT) : 0;
+    int per_head = n_qt - qt_first;
+    if constexpr (IMASK) {
+      const int key_hi = min(Nk, k0 + C::kKeys) - 1;
+      int f = n_qt, l = -1;
+      for (int t = lane; t < n_qt; t += 64) {
+        const i32x4 sm = tile_sum[(size_t)b * n_qt + t];
+        if (sm[0] <= key_hi && sm[1] >= k0) {
+          f = min(f, t);
+          l = max(l, t);
+        }
+      }
+  #pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        f = min(f, __shfl_xor(f, off));
+        l = max(l, __shfl_xor(l, off));
+      }
+      // (Equal in every lane after the reduction; read from lane 0 so that the loop's
+      // trip count and its wait choices are scalar.)
+      qt_first = __builtin_amdgcn_readfirstlane(l >= 0 ? f : 0);
+      per_head = __builtin_amdgcn_readfirstlane(l >= 0 ? l - f + 1 : 0);
     }
+    const int n_iter = per_head * n_rep;
+
+    // LDS-DMA offsets: chunk ch of a tile holds tile row off / kRowBytes, physical
+    // granule pg, i.e. logical granule pg ^ swizzle(row).
+    uint32_t goff[C::kCPW];
+  #pragma unroll
+    for (int i = 0; i < C::kCPW; ++i) {
+      const int off = (wave * C::kCPW + i) * 1024 + lane * 16;
+      const int row = off / C::kRowBytes;
+      const int pg = (off % C::kRowBytes) / 16;
+      goff[i] = row * C::kRowBytes + ((pg ^ bwd_swz<D>(row)) * 16);
+    }
+    const uint32_t lane4 = (uint32_t)lane * 4;  // per-lane offset of the 4-byte row loads
+    auto issue = [&](int it, uint16_t* lq, uint16_t* ld, float* ll, float* lD, int* lm)
+        __attribute__((always_inline)) {
+      const int r = it / per_head;
+      const uint32_t i0 = (uint32_t)(qt_first + it % per_head) * C::kQT;
+      const size_t bh = (size_t)b * H + kvh * n_rep + r;
+      const auto rq = make_rsrc(Q + bh * Nq * D, q_bytes);
+      const auto rd = make_rsrc(dO + bh * Nq * D, q_bytes);
+  #pragma unroll
+      for (int i = 0; i < C::kCPW; ++i) {
+        const int ch = wave * C::kCPW + i;
+        buffer_load16_lds(rq, lq + ch * 512, goff[i], i0 * C::kRowBytes);
+        buffer_load16_lds(rd, ld + ch * 512, goff[i], i0 * C::kRowBytes);
+      }
+      if (wave == 0) {  // 64 rows x 4 bytes of LSE*log2(e) and D; rows >= Nq read zero
+        const auto rl = make_rsrc(LSE2 + bh * Nq, (uint32_t)Nq * 4);
+        const auto rD = make_rsrc(Dv + bh * Nq, (uint32_t)Nq * 4);
+        buffer_load4_lds(rl, ll, lane4, i0 * 4);
+        buffer_load4_lds(rD, lD, lane4, i0 * 4);
+        if constexpr (IMASK) {  // and the rows' key intervals
+          const auto rlo = make_rsrc(kv_lo + (size_t)b * Nq, (uint32_t)Nq * 4);
+          const auto rhi = make_rsrc(kv_hi + (size_t)b * Nq, (uint32_t)Nq * 4);
+          buffer_load4_lds(rlo, lm, lane4, i0 * 4);
+          buffer_load4_lds(rhi, lm + C::kQT, lane4, i0 * 4);
+          // The tile's summary comes through LDS too: read from global memory in the
+          // loop, it would need a vmcnt wait that also drains the prefetches in flight.
+          // (The tile offset goes into the per-lane offset, which the buffer's range check
+          // always covers: lanes past the last summary read zero.)
+          const auto rs = make_rsrc(tile_sum + (size_t)b * n_qt, (uint32_t)n_qt * 16);
+          buffer_load4_lds(rs, lm + 2 * C::kQT, lane4 + (i0 / C::kQT) * 16, 0);
+        }
+      }
+    };
+    // Outstanding loads per staged tile: 2 * kCPW per wave, and wave 0 also loads LSE
+    // and D (and the two interval arrays and the tile summary).
+    constexpr int kW0 = IMASK ? 5 : 2;
+
+    // LDS read offsets (bytes in a tile), loop-invariant per lane.
+    //  row-wise (A operand of S and dP): row 32qb + l32, logical granule 2c + hi
+    uint32_t roff[D / 16];
+  #pragma unroll
+    for (int c = 0; c < D / 16; ++c) roff[c] = l32 * C::kRowBytes + (((2 * c + hi) ^ bwd_swz<D>(l32)) * 16);
+    //  transposed (A operands of dV^T and dK^T): rows 16cq + tr_row (+8), columns
+    //  32t + tr_col .. +3 (see common.h for the lane pattern of the transpose read)
+    const int tr_row = 4 * hi + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    //  The upper half (rows +8) has swizzle bwd_swz(row) ^ 2: granule bit 1, i.e. byte
+    //  bit 5 of the in-row offset, flips.
+    uint32_t toff[D / 32], toff8[D / 32];
+  #pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      const int col = 32 * t + tr_col;
+      toff[t] = tr_row * C::kRowBytes + (((col >> 3) ^ bwd_swz<D>(tr_row)) * 16) + (col & 7) * 2;
+      toff8[t] = (tr_row + 8) * C::kRowBytes + (((col >> 3) ^ bwd_swz<D>(tr_row + 8)) * 16) + (col & 7) * 2;
+    }
+
+    // One staged tile of 64 query rows = two 32-row blocks.  The scores and dP of
+    // both blocks are issued first; the softmax-JVP arithmetic of block 0 then
+    // overlaps the MFMAs of block 1 and the dV/dK MFMAs of block 0 overlap the
+    // arithmetic of block 1.  Everything is one basic block (masking is a
+    // compile-time variant chosen per tile) so the scheduler can interleave.
+    // Variant for 32 keys per wave: one staged tile of 64 query rows, processed as
+    // two 32-row blocks.  For each block every LDS operand is requested before the
+    // instructions that consume it, with scheduling fences in between, so that LDS
+    // latency overlaps other work of the same wave (one wave per SIMD has nothing
+    // else to hide it):
+    //   row-wise Q/dO reads + LSE/D   | S, dP MFMAs
+    //   transposed Q/dO reads         | softmax-JVP arithmetic
+    //                                 | dV, dK MFMAs
+    auto compute_tile_fenced = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
+                            const float* lD, const int* lm) __attribute__((always_inline)) {
+      constexpr int MM = decltype(mask_c)::value;  // 0 none, 1 causal, 2 intervals
+  #pragma unroll
+      for (int qb = 0; qb < C::kQT / 32; ++qb) {
+        // -- operand requests for S and dP
+        u32x4 aq[D / 16], ad[D / 16];
+  #pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          aq[c] = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
+          ad[c] = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
+        }
+        f32x4 lse4[4], d4[4];  // rows 32qb + 8g + 4hi + 0..3 for register group g
+        i32x4 lo4[4], hi4[4];
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          lse4[g] = *(const f32x4*)&ll[32 * qb + 8 * g + 4 * hi];
+          d4[g] = *(const f32x4*)&lD[32 * qb + 8 * g + 4 * hi];
+          if constexpr (MM == 2) {
+            lo4[g] = *(const i32x4*)&lm[32 * qb + 8 * g + 4 * hi];
+            hi4[g] = *(const i32x4*)&lm[C::kQT + 32 * qb + 8 * g + 4 * hi];
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // -- S = Q K^T, dP = dO V^T (lane = key, register r = query row 8(r/4)+4hi+r%4)
+        f32x16 s[KB], dp[KB];
+  #pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[kb][r] = 0.f;
+            dp[kb][r] = 0.f;
+          }
+  #pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+  #pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            s[kb] = M::mma32(as_vec8<T>(aq[c]), kf[kb][c], s[kb]);
+            dp[kb] = M::mma32(as_vec8<T>(ad[c]), vf[kb][c], dp[kb]);
+          }
+        // -- operand requests for dV^T and dK^T (transposed reads of the same tiles)
+        vec8 adt[2][D / 32], aqt[2][D / 32];
+  #pragma unroll
+        for (int cq = 0; cq < 2; ++cq) {
+          const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
+  #pragma unroll
+          for (int t = 0; t < D / 32; ++t) {
+            adt[cq][t] = join8<T>(lds_read_tr4(db_ + rowb + toff[t]), lds_read_tr4(db_ + rowb + toff8[t]));
+            aqt[cq][t] = join8<T>(lds_read_tr4(qb_ + rowb + toff[t]), lds_read_tr4(qb_ + rowb + toff8[t]));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // -- P = exp2(S*c - LSE*log2e) (0 where masked), dS = P * (dP - D)
+        vec8 pp[2][KB], ps[2][KB];
+  #pragma unroll
+        for (int cq = 0; cq < 2; ++cq)
+  #pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const int key = kw + 32 * kb + l32;
+            float p8[8], d8[8];
+  #pragma unroll
+            for (int g2 = 0; g2 < 2; ++g2) {
+              const int g = 2 * cq + g2;
+              const int ql = 32 * qb + 8 * g + 4 * hi;
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                float pv = fast_exp2(fmaf(s[kb][r], scale_log2, -lse4[g][e]));
+                if constexpr (MM == 1) {
+                  if (key > i0 + ql + e) pv = 0.f;
+                } else if constexpr (MM == 2) {
+                  if (key < lo4[g][e] || key > hi4[g][e]) pv = 0.f;
+                }
+                p8[4 * g2 + e] = pv;
+                d8[4 * g2 + e] = pv * (dp[kb][r] - d4[g][e]);
+              }
+            }
+            pp[cq][kb] = pack8<T>(p8);
+            ps[cq][kb] = pack8<T>(d8);
+          }
+        // -- dV^T += dO^T P ; dK^T += Q^T dS  (reduction over the 32 query rows)
+  #pragma unroll
+        for (int cq = 0; cq < 2; ++cq)
+  #pragma unroll
+          for (int t = 0; t < D / 32; ++t)
+  #pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              dv_acc[kb][t] = M::mma32(adt[cq][t], pp[cq][kb], dv_acc[kb][t]);
+              dk_acc[kb][t] = M::mma32(aqt[cq][t], ps[cq][kb], dk_acc[kb][t]);
+            }
+      }
+    };
+    auto compute_tile_wide = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
+                            const float* lD, const int* lm) __attribute__((always_inline)) {
+      constexpr int MM = decltype(mask_c)::value;  // 0 none, 1 causal, 2 intervals
+      constexpr int NQB = C::kQT / 32;
+      // S = Q K^T, dP = dO V^T (lane = key, register r = query row 8(r/4)+4hi+r%4)
+      f32x16 s[NQB][KB], dp[NQB][KB];
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+  #pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[qb][kb][r] = 0.f;
+            dp[qb][kb][r] = 0.f;
+          }
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+  #pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          const u32x4 aq = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
+          const u32x4 ad = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
+  #pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            s[qb][kb] = M::mma32(as_vec8<T>(aq), kf[kb][c], s[qb][kb]);
+            dp[qb][kb] = M::mma32(as_vec8<T>(ad), vf[kb][c], dp[qb][kb]);
+          }
+        }
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        // P = exp2(S*c - LSE*log2e) (0 where masked), dS = P * (dP - D)
+  #pragma unroll
+        for (int cq = 0; cq < 2; ++cq) {
+          vec8 pp[KB], ps[KB];
+  #pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const int key = kw + 32 * kb + l32;
+            float p8[8], d8[8];
+  #pragma unroll
+            for (int g2 = 0; g2 < 2; ++g2) {
+              const int ql = 32 * qb + 16 * cq + 8 * g2 + 4 * hi;  // local row of register 8cq+4g2
+              const f32x4 lse4 = *(const f32x4*)&ll[ql];
+              const f32x4 d4 = *(const f32x4*)&lD[ql];
+              i32x4 lo4 = {}, hi4 = {};
+              if constexpr (MM == 2) {
+                lo4 = *(const i32x4*)&lm[ql];
+                hi4 = *(const i32x4*)&lm[C::kQT + ql];
+              }
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 8 * cq + 4 * g2 + e;
+                float pv = fast_exp2(fmaf(s[qb][kb][r], scale_log2, -lse4[e]));
+                if constexpr (MM == 1) {
+                  if (key > i0 + ql + e) pv = 0.f;
+                } else if constexpr (MM == 2) {
+                  if (key < lo4[e] || key > hi4[e]) pv = 0.f;
+                }
+                p8[4 * g2 + e] = pv;
+                d8[4 * g2 + e] = pv * (dp[qb][kb][r] - d4[e]);
+              }
+            }
+            pp[kb] = pack8<T>(p8);
+            ps[kb] = pack8<T>(d8);
+          }
+          // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over these 16 query rows)
+          const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
+  #pragma unroll
+          for (int t = 0; t < D / 32; ++t) {
+            const vec8 adt = join8<T>(lds_read_tr4(db_ + rowb + toff[t]), lds_read_tr4(db_ + rowb + toff8[t]));
+            const vec8 aqt = join8<T>(lds_read_tr4(qb_ + rowb + toff[t]), lds_read_tr4(qb_ + rowb + toff8[t]));
+  #pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              dv_acc[kb][t] = M::mma32(adt, pp[kb], dv_acc[kb][t]);
+              dk_acc[kb][t] = M::mma32(aqt, ps[kb], dk_acc[kb][t]);
+            }
+          }
+        }
+      }
+    };
+    // Software-pipelined variant for 32 keys per wave.  Per 32-row block qb the work
+    // is G1 (S and dP: 16 MFMAs), J (the softmax-JVP arithmetic: about 130 VALU
+    // instructions) and G2 (dV and dK: 16 MFMAs).  With one wave per SIMD nothing
+    // else hides J, so the tile runs
+    //   G1(0) | G1(1) with J(0) | G2(0) with J(1) | G2(1)
+    // and scheduling groups interleave the VALU work between the MFMAs of the same
+    // phase (MFMA and VALU of one wave overlap when they are independent).
+    struct RowOps {
+      u32x4 aq[D / 16], ad[D / 16];
+      f32x4 lse4[4], d4[4];  // rows 32qb + 8g + 4hi + 0..3 for register group g
+    };
+    struct TrOps {
+      vec8 adt[2][D / 32], aqt[2][D / 32];
+    };
+    auto read_rows = [&](RowOps& o, int qb, const char* qb_, const char* db_, const float* ll,
+                         const float* lD) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        o.aq[c] = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
+        o.ad[c] = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
+      }
+  #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        o.lse4[g] = *(const f32x4*)&ll[32 * qb + 8 * g + 4 * hi];
+        o.d4[g] = *(const f32x4*)&lD[32 * qb + 8 * g + 4 * hi];
+      }
+    };
+    auto read_tr = [&](TrOps& o, int qb, const char* qb_, const char* db_)
+        __attribute__((always_inline)) {
+  #pragma unroll
+      for (int cq = 0; cq < 2; ++cq) {
+        const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
+  #pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          o.adt[cq][t] = join8<T>(lds_read_tr4(db_ + rowb + toff[t]), lds_read_tr4(db_ + rowb + toff8[t]));
+          o.aqt[cq][t] = join8<T>(lds_read_tr4(qb_ + rowb + toff[t]), lds_read_tr4(qb_ + rowb + toff8[t]));
+        }
+      }
+    };
+    auto g1 = [&](const RowOps& o, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+  #pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        s = M::mma32(as_vec8<T>(o.aq[c]), kf[0][c], s);
+        dp = M::mma32(as_vec8<T>(o.ad[c]), vf[0][c], dp);
+      }
+    };
+    auto jvp = [&](auto mask_c, int i0, int qb, const RowOps& o, const f32x16& s, const f32x16& dp,
+                   vec8 (&pp)[2], vec8 (&ps)[2], const int* lm) __attribute__((always_inline)) {
+      constexpr int MM = decltype(mask_c)::value;  // 0 none, 1 causal, 2 intervals
+      const int key = kw + l32;
+  #pragma unroll
+      for (int cq = 0; cq < 2; ++cq) {
+        float p8[8], d8[8];
+  #pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int g = 2 * cq + g2;
+          const int ql = 32 * qb + 8 * g + 4 * hi;
+          i32x4 lo4 = {}, hi4 = {};  // the rows' key intervals (interval masks only)
+          if constexpr (MM == 2) {
+            lo4 = *(const i32x4*)&lm[ql];
+            hi4 = *(const i32x4*)&lm[C::kQT + ql];
+          }
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float pv = fast_exp2(fmaf(s[r], scale_log2, -o.lse4[g][e]));
+            if constexpr (MM == 1) {
+              if (key > i0 + ql + e) pv = 0.f;
+            } else if constexpr (MM == 2) {
+              if (key < lo4[e] || key > hi4[e]) pv = 0.f;
+            }
+            p8[4 * g2 + e] = pv;
+            d8[4 * g2 + e] = pv * (dp[r] - o.d4[g][e]);
+          }
+        }
+        pp[cq] = pack8<T>(p8);
+        ps[cq] = pack8<T>(d8);
+      }
+    };
+    auto g2 = [&](const TrOps& o, const vec8 (&pp)[2], const vec8 (&ps)[2])
+        __attribute__((always_inline)) {
+  #pragma unroll
+      for (int cq = 0; cq < 2; ++cq)
+  #pragma unroll
+        for (int t = 0; t < D / 32; ++t) {
+          dv_acc[0][t] = M::mma32(o.adt[cq][t], pp[cq], dv_acc[0][t]);
+          dk_acc[0][t] = M::mma32(o.aqt[cq][t], ps[cq], dk_acc[0][t]);
+        }
+    };
+    // One phase's interleave: n_ds LDS reads and n_v0 VALU first (to cover the first
+    // MFMA's operand latency), then 16 times one MFMA, ds_per LDS reads, v_per VALU.
+    auto interleave16 = [&](auto n_ds_c, auto n_v0_c, auto ds_per_c, auto v_per_c)
+        __attribute__((always_inline)) {
+      constexpr int kVALU = 0x2 | 0x400;  // VALU including transcendental
+      __builtin_amdgcn_sched_group_barrier(0x100, decltype(n_ds_c)::value, 0);
+      __builtin_amdgcn_sched_group_barrier(kVALU, decltype(n_v0_c)::value, 0);
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, decltype(ds_per_c)::value, 0);
+        __builtin_amdgcn_sched_group_barrier(kVALU, decltype(v_per_c)::value, 0);
+      }
+    };
+    auto compute_tile_pipe = [&](auto mask_c, int i0, const char* qb_, const char* db_,
+                                 const float* ll, const float* lD, const int* lm)
+        __attribute__((always_inline)) {
+      using IC0 = std::integral_constant<int, 0>;
+      RowOps r0, r1;
+      TrOps t0, t1;
+      f32x16 s0, dp0, s1, dp1;
+      vec8 pp0[2], ps0[2], pp1[2], ps1[2];
+      // G1(0)
+      read_rows(r0, 0, qb_, db_, ll, lD);
+      g1(r0, s0, dp0);
+      __builtin_amdgcn_sched_barrier(0);
+      // G1(1) with J(0); block 0's transposed operands are requested here too
+      read_rows(r1, 1, qb_, db_, ll, lD);
+      read_tr(t0, 0, qb_, db_);
+      jvp(mask_c, i0, 0, r0, s0, dp0, pp0, ps0, lm);
+      g1(r1, s1, dp1);
+      interleave16(std::integral_constant<int, OSATTN_IL1_DS0>{}, std::integral_constant<int, OSATTN_IL1_V0>{},
+                   std::integral_constant<int, OSATTN_IL1_DS>{}, std::integral_constant<int, OSATTN_IL1_V>{});
+      __builtin_amdgcn_sched_barrier(0);
+      // G2(0) with J(1); block 1's transposed operands
+      read_tr(t1, 1, qb_, db_);
+      jvp(mask_c, i0, 1, r1, s1, dp1, pp1, ps1, lm);
+      g2(t0, pp0, ps0);
+      interleave16(std::integral_constant<int, 0>{}, std::integral_constant<int, OSATTN_IL2_V0>{},
+                   std::integral_constant<int, OSATTN_IL2_DS>{}, std::integral_constant<int, OSATTN_IL2_V>{});
+      __builtin_amdgcn_sched_barrier(0);
+      // G2(1)
+      g2(t1, pp1, ps1);
+      (void)IC0{};
+    };
+    auto compute_tile = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
+                            const float* lD, const int* lm) __attribute__((always_inline)) {
+      if constexpr (KB == 1) {
+        if constexpr (OSATTN_DKDV_PIPE) compute_tile_pipe(mask_c, i0, qb_, db_, ll, lD, lm);
+        else compute_tile_fenced(mask_c, i0, qb_, db_, ll, lD, lm);
+      } else {
+        compute_tile_wide(mask_c, i0, qb_, db_, ll, lD, lm);
+      }
+    };
+    using M0 = std::integral_constant<int, 0>;
+    using M1 = std::integral_constant<int, 1>;
+    using M2 = std::integral_constant<int, 2>;
+    auto compute = [&](int it, const char* qb_, const char* db_, const float* ll, const float* lD,
+                       const int* lm) __attribute__((always_inline)) {
+      const int tq = qt_first + it % per_head;
+      const int i0 = tq * C::kQT;
+      if constexpr (IMASK) {
+        // Skip the tile if no row's interval meets this wave's keys; mask it unless every
+        // row sees all of them.
+        const i32x4 smv = *(const i32x4*)(lm + 2 * C::kQT);
+        const int sm[4] = {__builtin_amdgcn_readfirstlane(smv[0]), __builtin_amdgcn_readfirstlane(smv[1]),
+                           __builtin_amdgcn_readfirstlane(smv[2]), __builtin_amdgcn_readfirstlane(smv[3])};
+        const int kw_last = kw + 32 * KB - 1;
+        if (sm[0] > kw_last || sm[1] < kw) return;
+        if (sm[2] <= kw && sm[3] >= kw_last) compute_tile(M0{}, i0, qb_, db_, ll, lD, lm);
+        else compute_tile(M2{}, i0, qb_, db_, ll, lD, lm);
+        return;
+      }
+      if (CAUSAL && i0 + C::kQT - 1 < kw) return;  // every key of this wave is after every row
+      // Causal: only tiles whose first row precedes this wave's last key need the mask.
+      if (CAUSAL && i0 < kw + 32 * KB - 1)
+        compute_tile(M1{}, i0, qb_, db_, ll, lD, lm);
+      else
+        compute_tile(M0{}, i0, qb_, db_, ll, lD, lm);
+    };
+
+    auto stage = [&](auto sc, auto fn) __attribute__((always_inline)) {
+      constexpr int S = decltype(sc)::value;
+      // The interval arrays only exist for interval masks (elsewhere they must not be
+      // referenced at all, or the compiler stops telling the stages' LDS apart).
+      int* const m0 = IMASK ? lm0 : nullptr;
+      int* const m1 = IMASK ? lm1 : nullptr;
+      int* const m2 = IMASK ? lm2 : nullptr;
+      int* const m3 = IMASK ? lm3 : nullptr;
+      if constexpr (S == 0) fn(lq0, ld0, ll0, lD0, m0);
+      else if constexpr (S == 1) fn(lq1, ld1, ll1, lD1, m1);
+      else if constexpr (S == 2) fn(lq2, ld2, ll2, lD2, m2);
+      else fn(lq3, ld3, ll3, lD3, m3);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (0 < n_iter)
+      stage(I0{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) { issue(0, a, d, l, dd, mm); });
+    if (NBUF > 2 && 1 < n_iter)
+      stage(I1{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) { issue(1, a, d, l, dd, mm); });
+    if (NBUF > 3 && 2 < n_iter)
+      stage(I2{}, [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) { issue(2, a, d, l, dd, mm); });
+
+    auto step = [&](auto sc, int it) __attribute__((always_inline)) {
+      constexpr int S = decltype(sc)::value;
+      constexpr int SN = (S + NBUF - 1) % NBUF;  // receives tile it + NBUF - 1
+      // Tile `it` has landed once at most the loads of the tiles issued after it
+      // (up to NBUF - 2 of them) are outstanding.
+      constexpr int kPer = 2 * C::kCPW;  // loads per tile and wave (+kW0 on wave 0)
+      const int ahead = min(NBUF - 2, n_iter - 1 - it);
+      if (NBUF > 3 && ahead >= 2) {
+        if (wave == 0) wait_vmcnt<2 * (kPer + kW0)>();
+        else wait_vmcnt<2 * kPer>();
+      } else if (NBUF > 2 && ahead >= 1) {
+        if (wave == 0) wait_vmcnt<kPer + kW0>();
+        else wait_vmcnt<kPer>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      block_barrier();
+      if (it + NBUF - 1 < n_iter)
+        stage(std::integral_constant<int, SN>{},
+              [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) {
+                issue(it + NBUF - 1, a, d, l, dd, mm);
+              });
+      stage(sc, [&](uint16_t* a, uint16_t* d, float* l, float* dd, int* mm) {
+        compute(it, (const char*)a, (const char*)d, l, dd, mm);
+      });
+    };
+    for (int it = 0; it < n_iter; it += NBUF) {
+      step(I0{}, it);
+      if (it + 1 < n_iter) step(I1{}, it + 1);
+      if constexpr (NBUF > 2)
+        if (it + 2 < n_iter) step(I2{}, it + 2);
+      if constexpr (NBUF > 3)
+        if (it + 3 < n_iter) step(std::integral_constant<int, 3>{}, it + 3);
+    }
+
+    // Store: lane = key, register r of tile t = column 32t + 8(r/4) + 4hi + r%4.
+  #pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int key = kw + 32 * kb + l32;
+      if (key < Nk) {
+        uint16_t* dkp = dK + ((size_t)bg * Nk + key) * D;
+        uint16_t* dvp = dV + ((size_t)bg * Nk + key) * D;
+  #pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+  #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            u32x2 wk, wv;
+            wk[0] = (uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 0] * scale) |
+                    ((uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 1] * scale) << 16);
+            wk[1] = (uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 2] * scale) |
+                    ((uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 3] * scale) << 16);
+            wv[0] = (uint32_t)to_bits<T>(dv_acc[kb][t][4 * g + 0]) |
+                    ((uint32_t)to_bits<T>(dv_acc[kb][t][4 * g + 1]) << 16);
+            wv[1] = (uint32_t)to_bits<T>(dv_acc[kb][t][4 * g + 2]) |
+                    ((uint32_t)to_bits<T>(dv_acc[kb][t][4 * g + 3]) << 16);
+            store_global(dkp + 32 * t + 8 * g + 4 * hi, wk);
+            store_global(dvp + 32 * t + 8 * g + 4 * hi, wv);
+          }
+      }
+    }
+    if constexpr (!PERSIST) break;
+    __syncthreads();  // every wave is done with the staged tiles
+    L = sched.next();
   }
 }
 
@@ -1111,12 +1159,18 @@ static hipError_t bwd_t(const BwdArgs& a) {
   if (a.stages & kStageDkdv) {
     using C = DkdvCfg<D, NBK>;
     const int n_kt = (Nk + C::kKeys - 1) / C::kKeys;
-    const long long blocks = (long long)n_kt * a.B * a.Hkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NBK, CAUSAL, IMASK>), dim3((unsigned)blocks),
-                       dim3(256), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse2,
-                       a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv, a.H, a.Hkv, a.N, n_kt,
-                       a.scale, sl2, a.kv_lo, a.kv_hi, (const i32x4*)a.tile_sum, Nk);
+    const long long jobs = (long long)n_kt * a.B * a.Hkv;
+    auto kernel = bwd_dkdv_kernel<T, D, NBK, CAUSAL, IMASK>;
+    long long blocks = jobs;
+    if (OSATTN_DKDV_PERSIST && CAUSAL && !IMASK) {
+      static const int per_cu = resident_per_cu(kernel, 256);
+      blocks = persistent_grid(per_cu, jobs);
+    }
+    const DkdvKernelArgs ka{(const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                            (const uint16_t*)a.dO, a.lse2, a.dvec, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                            a.H, a.Hkv, a.N, n_kt, a.scale, sl2, a.kv_lo, a.kv_hi,
+                            (const i32x4*)a.tile_sum, Nk, (int)jobs, 0};
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)a.stream, ka);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -206,4 +206,76 @@ __device__ __forceinline__ int xcd_group_remap(int bid, int nblocks, int group_t
   return ((w / group_tiles) * 8 + r) * group_tiles + w % group_tiles;
 }
 
+// ---------------------------------------------------------------------------
+// Persistent grids.  The dispatcher hands workgroups to the 8 XCDs round-robin and in
+// launch order, so a workgroup waits for a free CU on its own XCD even when other
+// XCDs have one free.  With tiles of very different lengths (causal masks) the CUs
+// then idle between workgroups: traced per workgroup, a causal forward left 6-7 us
+// between one workgroup's end and the next one's start on a CU, against 0.2 us when
+// all tiles are equal.  A persistent grid (one workgroup per resident slot) launches
+// everything at once and walks a fixed schedule instead:
+//   - the logical tiles are cut into one contiguous block per XCD (the heads that
+//     xcd_remap gives that XCD, for its L2), and the workgroups that launch order
+//     places on that XCD share its block;
+//   - they take it in rounds, one tile each per round, in snake order (reversed
+//     every other round).  Tiles come longest first within a head, so a workgroup
+//     that gets a long tile in one round gets a short one in the next: under a causal
+//     mask each pair of rounds gives every workgroup about the same work.
+// The schedule is a fixed function of the launch index: no state in memory, nothing
+// shared between launches (streams and graph replays may overlap freely).
+struct StaticSchedule {
+  int base;   // first logical tile of this workgroup's block
+  int count;  // tiles in the block
+  int nw;     // workgroups sharing the block
+  int w;      // this workgroup's place among them
+  int round;  // rounds taken so far
+
+  __device__ StaticSchedule(int total, int bid, int grid) {
+    const int k = grid < 8 ? grid : 8;  // blocks (one per XCD)
+    const int per = (total + k - 1) / k;
+    const int x = bid % k;
+    base = x * per;
+    count = max(0, min(per, total - base));
+    nw = (grid - x + k - 1) / k;
+    w = bid / k;
+    round = 0;
+  }
+  // Next logical tile of this workgroup, or -1 when it has none left.
+  __device__ int next() {
+    const int j = round * nw + ((round & 1) ? nw - 1 - w : w);
+    ++round;
+    return j < count ? base + j : -1;
+  }
+};
+
+// Global-memory accesses through pointers the compiler cannot tell are global (ones
+// loaded from memory, such as fresh_kernel_args gives): plain dereferences of those
+// become flat instructions, which also count against the LDS wait counter.
+template <typename V>
+__device__ __forceinline__ void store_global(void* p, const V& v) {
+  *(__attribute__((address_space(1))) V*)p = v;
+}
+template <typename V>
+__device__ __forceinline__ V load_global(const void* p) {
+  return *(const __attribute__((address_space(1))) V*)p;
+}
+
+// The kernel's arguments (a struct passed as its only argument), loaded anew from the
+// kernel-argument segment: the empty asm hides that the pointer does not change, so
+// the loads are not hoisted out of the caller's loop.  A persistent grid reads them
+// once per tile: kept from one tile to the next, they would hold scalar registers
+// through the tile loop, and the compiler gives up the LDS read-ahead there to make
+// room.
+template <typename A>
+__device__ __forceinline__ A fresh_kernel_args() {
+  static_assert(sizeof(A) % 4 == 0, "argument struct of whole words");
+  auto p = (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  A a;
+  uint32_t* w = reinterpret_cast<uint32_t*>(&a);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(A) / 4); ++i) w[i] = p[i];
+  return a;
+}
+
 }  // namespace osattn

@@ -71,6 +71,33 @@ struct SplitArgs {
   void* stream;
 };
 
+// Compute units of the current device (256 on MI355X if the runtime cannot say).
+inline int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+// Workgroups of `kernel` that one CU holds at once (1 if the runtime cannot say).
+template <typename K>
+inline int resident_per_cu(K kernel, int threads) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
+  return per_cu;
+}
+
+// Workgroups of a persistent grid for `jobs` tiles: one per resident slot of the device,
+// or fewer if there are fewer tiles.
+inline long long persistent_grid(int per_cu, long long jobs) {
+  const long long slots = (long long)device_cus() * per_cu;
+  return jobs < slots ? jobs : slots;
+}
+
 // Waves per split-KV workgroup (32 query rows each) for a query group of `rows`
 // rows: one per 32 rows, up to four.
 inline int splitkv_waves(int rows) {

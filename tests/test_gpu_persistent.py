@@ -1,0 +1,67 @@
+"""Persistent grids (the causal forward and dK/dV kernels).
+
+Their workgroups walk a fixed schedule of tiles (one block of tiles per XCD, taken in
+snake-ordered rounds) instead of one tile each.  These tests check that many launches
+in a row, and launches on two streams at once, give results bit for bit equal to the
+first launch, which the oracle checks, on shapes whose tile counts do not divide
+evenly among the workgroups.
+"""
+
+import pytest
+import torch
+
+import synthetic as S
+from gpu_parity import check_full, need_gpu, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+N_LAUNCHES = 20
+
+
+def _run(inp, scale, stream=None):
+    import online_softmax_attn_amd as osa
+    q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    else:
+        stream.wait_stream(torch.cuda.current_stream())  # the inputs' copies
+    with torch.cuda.stream(stream):
+        o, lse = osa.attn_fwd(q, k, v, causal=True, scale=scale)
+        dq, dk, dv = osa.attn_bwd(q, k, v, o, lse, do, causal=True, scale=scale)
+    return o, lse, dq, dk, dv
+
+
+def _same(a, b):
+    return all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_many_launches_bitwise(d):
+    need_gpu()
+    w = S.custom("bf16", 2, 4, 2, 1100, d, True, seed_base=9100 + d)
+    inp = S.make_inputs(w)
+    check_full(inp, "bf16", True, w.scale, label=w.name)
+    first = _run(inp, w.scale)
+    torch.cuda.synchronize()
+    for i in range(N_LAUNCHES):
+        again = _run(inp, w.scale)
+        torch.cuda.synchronize()
+        assert _same(first, again), f"launch {i} differs"
+    say(f"[persistent] {w.name}: {N_LAUNCHES} launches bit-identical")
+
+
+def test_causal_two_streams_at_once():
+    need_gpu()
+    w1 = S.custom("bf16", 1, 8, 8, 2048, 128, True, seed_base=9200)
+    w2 = S.custom("fp16", 2, 4, 1, 1500, 64, True, seed_base=9300)
+    in1, in2 = S.make_inputs(w1), S.make_inputs(w2)
+    ref1, ref2 = _run(in1, w1.scale), _run(in2, w2.scale)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for i in range(8):
+        got1 = _run(in1, w1.scale, s1)
+        got2 = _run(in2, w2.scale, s2)
+        torch.cuda.synchronize()
+        assert _same(ref1, got1) and _same(ref2, got2), f"round {i} differs"
+    check_full(in1, "bf16", True, w1.scale, label=w1.name)
+    check_full(in2, "fp16", True, w2.scale, label=w2.name)
