@@ -298,7 +298,7 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
       const int key_hi = min(Nk, k0 + C::kKeys) - 1;
       int f = n_qt, l = -1;
       for (int t = lane; t < n_qt; t += 64) {
-        const i32x4 sm = tile_sum[(size_t)b * n_qt + t];
+        const i32x4 sm = load_global<i32x4>(tile_sum + (size_t)b * n_qt + t);
         if (sm[0] <= key_hi && sm[1] >= k0) {
           f = min(f, t);
           l = max(l, t);
