@@ -835,10 +835,10 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
 #define OSATTN_DQ_BC 64
 #endif
 
-template <int D, int NBUF>
+template <int D, int NBUF, int QB>
 struct DqCfg {
   static constexpr int kNW = 8;              // waves (two per SIMD)
-  static constexpr int kRows = kNW * 32;     // query rows per workgroup
+  static constexpr int kRows = kNW * 32 * QB;  // query rows per workgroup (QB 32-row blocks per wave)
   static constexpr int kBC = OSATTN_DQ_BC;   // keys per staged tile
   static constexpr int kRowBytes = D * 2;
   static constexpr int kTileElems = kBC * D;
@@ -847,7 +847,7 @@ struct DqCfg {
   static_assert(kCPW >= 1 && kChunks % kNW == 0, "tile must split evenly over the waves");
 };
 
-template <typename T, int D, int NBUF, bool CAUSAL, bool IMASK>
+template <typename T, int D, int NBUF, int QB, bool CAUSAL, bool IMASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -857,7 +857,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    float scale, float scale_log2, const int* __restrict__ kv_lo,
                    const int* __restrict__ kv_hi, int Nk_arg) {
   const int Nk = IMASK ? Nk_arg : Nq;  // keys differ from queries only under interval masks
-  using C = DqCfg<D, NBUF>;
+  using C = DqCfg<D, NBUF, QB>;
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
   static_assert(NBUF >= 2 && NBUF <= 4, "two to four stages");
@@ -887,8 +887,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int b = bh / H;
   const int kvh = h / (H / Hkv);
   const int q0 = qt * C::kRows;
-  const int wrow0 = q0 + 32 * wave;
-  const int row = wrow0 + l32;
+  const int wrow0 = q0 + 32 * QB * wave;  // the wave's rows: QB blocks of 32 from here
 
   const uint32_t q_bytes = (uint32_t)Nq * C::kRowBytes;
   const uint32_t kv_bytes = (uint32_t)Nk * C::kRowBytes;
@@ -897,47 +896,63 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const auto rk = make_rsrc(K + (size_t)(b * Hkv + kvh) * Nk * D, kv_bytes);
   const auto rv = make_rsrc(V + (size_t)(b * Hkv + kvh) * Nk * D, kv_bytes);
 
-  // Q and dO rows of this lane (B operands of S^T = K Q^T and dP^T = V dO^T).
-  vec8 qf[D / 16], df[D / 16];
-  {
+  // Q and dO rows of this lane, one per row block (B operands of S^T = K Q^T and
+  // dP^T = V dO^T), with their LSE*log2(e) and D.
+  vec8 qf[QB][D / 16], df[QB][D / 16];
+  float lse2[QB], drow[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wrow0 + 32 * qb + l32;
     const uint32_t rowoff = (uint32_t)row * C::kRowBytes;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      qf[c] = as_vec8<T>(buffer_load16(rq, rowoff + (16 * c + 8 * hi) * 2));
-      df[c] = as_vec8<T>(buffer_load16(rdo, rowoff + (16 * c + 8 * hi) * 2));
+      qf[qb][c] = as_vec8<T>(buffer_load16(rq, rowoff + (16 * c + 8 * hi) * 2));
+      df[qb][c] = as_vec8<T>(buffer_load16(rdo, rowoff + (16 * c + 8 * hi) * 2));
     }
+    lse2[qb] = row < Nq ? LSE2[(size_t)bh * Nq + row] : 0.f;
+    drow[qb] = row < Nq ? Dv[(size_t)bh * Nq + row] : 0.f;
   }
-  const float lse2 = row < Nq ? LSE2[(size_t)bh * Nq + row] : 0.f;
-  const float drow = row < Nq ? Dv[(size_t)bh * Nq + row] : 0.f;
 
-  f32x16 acc[D / 32];
+  f32x16 acc[QB][D / 32];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[qb][t][r] = 0.f;
 
   int kt0 = 0;  // first key tile of the loop
   int n_kt = (Nk + C::kBC - 1) / C::kBC;
   if (CAUSAL) n_kt = min(n_kt, (q0 + C::kRows + C::kBC - 1) / C::kBC);
 
-  // Interval masks (as in the forward): this row's keys lo .. hi (empty: lo = Nk,
+  // Interval masks (as in the forward): each row's keys lo .. hi (empty: lo = Nk,
   // hi = -1), the wave's union and intersection of its rows' intervals, and the
   // workgroup's tile range.
-  int lo_r = 0, hi_r = 0, w_lo = 0, w_hi = 0, w_maxlo = 0, w_minhi = 0;
+  int lo_r[QB], hi_r[QB];
+  int w_lo = 0, w_hi = 0, w_maxlo = 0, w_minhi = 0;
   if constexpr (IMASK) {
     __shared__ int wg_bounds[2 * C::kNW];
-    lo_r = Nk;
-    hi_r = -1;
-    if (row < Nq) {
-      lo_r = max(kv_lo[(size_t)b * Nq + row], 0);
-      hi_r = min(kv_hi[(size_t)b * Nq + row], Nk - 1);
-      if (lo_r > hi_r) {
-        lo_r = Nk;
-        hi_r = -1;
+    w_lo = w_maxlo = Nk;
+    w_hi = w_minhi = -1;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = wrow0 + 32 * qb + l32;
+      int lo = Nk, hi = -1;
+      if (row < Nq) {
+        lo = max(kv_lo[(size_t)b * Nq + row], 0);
+        hi = min(kv_hi[(size_t)b * Nq + row], Nk - 1);
+        if (lo > hi) {
+          lo = Nk;
+          hi = -1;
+        }
       }
+      lo_r[qb] = lo;
+      hi_r[qb] = hi;
+      w_lo = min(w_lo, lo);
+      w_hi = max(w_hi, hi);
+      w_maxlo = qb == 0 ? lo : max(w_maxlo, lo);
+      w_minhi = qb == 0 ? hi : min(w_minhi, hi);
     }
-    w_lo = w_maxlo = lo_r;
-    w_hi = w_minhi = hi_r;
 #pragma unroll
     for (int off = 1; off < 32; off <<= 1) {
       w_lo = min(w_lo, __shfl_xor(w_lo, off));
@@ -945,7 +960,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       w_maxlo = max(w_maxlo, __shfl_xor(w_maxlo, off));
       w_minhi = min(w_minhi, __shfl_xor(w_minhi, off));
     }
-    // Both half-waves hold the same 32 rows, so every lane now has the wave's values;
+    // Both half-waves hold the same rows, so every lane now has the wave's values;
     // read them from lane 0 so that the per-tile tests are scalar branches.
     w_lo = __builtin_amdgcn_readfirstlane(w_lo);
     w_hi = __builtin_amdgcn_readfirstlane(w_hi);
@@ -1001,25 +1016,31 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
   auto compute = [&](int kt, const char* kbase, const char* vbase) __attribute__((always_inline)) {
     const int k0 = (kt0 + kt) * C::kBC;
-    if (CAUSAL && k0 > wrow0 + 31) return;  // every key of the tile is after every row
+    if (CAUSAL && k0 > wrow0 + 32 * QB - 1) return;  // every key of the tile is after every row
     if (IMASK && (k0 > w_hi || k0 + C::kBC - 1 < w_lo)) return;  // no row of the wave sees it
     const bool need_mask = (k0 + C::kBC > Nk) || (CAUSAL && k0 + C::kBC - 1 > wrow0) ||
                            (IMASK && !(k0 >= w_maxlo && k0 + C::kBC - 1 <= w_minhi));
 #pragma unroll
     for (int kb = 0; kb < C::kBC / 32; ++kb) {
-      // S^T = K Q^T, dP^T = V dO^T (lane = query row, register = key)
-      f32x16 s, dp;
+      // S^T = K Q^T, dP^T = V dO^T (lane = query row, register = key); each K and V
+      // operand read from LDS serves every row block.
+      f32x16 s[QB], dp[QB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[qb][r] = 0.f;
+          dp[qb][r] = 0.f;
+        }
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         const u32x4 ak = *(const u32x4*)(kbase + kb * 32 * C::kRowBytes + roff[c]);
         const u32x4 av = *(const u32x4*)(vbase + kb * 32 * C::kRowBytes + roff[c]);
-        s = M::mma32(as_vec8<T>(ak), qf[c], s);
-        dp = M::mma32(as_vec8<T>(av), df[c], dp);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          s[qb] = M::mma32(as_vec8<T>(ak), qf[qb][c], s[qb]);
+          dp[qb] = M::mma32(as_vec8<T>(av), df[qb][c], dp[qb]);
+        }
       }
       // Masked scores become -inf (P = 0, so dS = 0) in a branch of their own: folded
       // into the loop below, the compiler would evaluate the key tests as selects on
@@ -1029,27 +1050,37 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         // Key of element r: base + ko with ko a compile-time constant; the limits are
         // taken relative to base once per block.
         const int base = k0 + kb * 32 + 4 * hi;
-        const int lim_hi = IMASK ? min(hi_r - base, Nk - 1 - base) : Nk - 1 - base;
-        const int lim_lo = IMASK ? lo_r - base : 0;
-        const int lim_c = row - base;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ko = 8 * (r >> 2) + (r & 3);
-          if (ko > lim_hi || (CAUSAL && ko > lim_c) || (IMASK && ko < lim_lo)) s[r] = -INFINITY;
+        for (int qb = 0; qb < QB; ++qb) {
+          const int lim_hi = IMASK ? min(hi_r[qb] - base, Nk - 1 - base) : Nk - 1 - base;
+          const int lim_lo = IMASK ? lo_r[qb] - base : 0;
+          const int lim_c = wrow0 + 32 * qb + l32 - base;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ko = 8 * (r >> 2) + (r & 3);
+            if (ko > lim_hi || (CAUSAL && ko > lim_c) || (IMASK && ko < lim_lo)) s[qb][r] = -INFINITY;
+          }
         }
       }
-      float dsv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dsv[r] = fast_exp2(fmaf(s[r], scale_log2, -lse2)) * (dp[r] - drow);
-      // dQ^T += K^T dS^T (reduction over the 32 keys of this block, 16 at a time)
+      // dQ^T += K^T dS^T (reduction over the 32 keys of this block, 16 at a time); each
+      // transposed K operand serves every row block.
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        const vec8 ps = pack8<T>(&dsv[8 * cc]);
+        vec8 ps[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float dsv[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            dsv[r] = fast_exp2(fmaf(s[qb][8 * cc + r], scale_log2, -lse2[qb])) * (dp[qb][8 * cc + r] - drow[qb]);
+          ps[qb] = pack8<T>(dsv);
+        }
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
           const int rowb = (32 * kb + 16 * cc) * C::kRowBytes;
           const vec8 a = join8<T>(lds_read_tr4(kbase + rowb + toff[t]), lds_read_tr4(kbase + rowb + toff8[t]));
-          acc[t] = M::mma32(a, ps, acc[t]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc[qb][t] = M::mma32(a, ps[qb], acc[qb][t]);
         }
       }
     }
@@ -1099,19 +1130,23 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       if (kt + 3 < n_kt) step(std::integral_constant<int, 3>{}, kt + 3);
   }
 
-  if (row < Nq) {
-    uint16_t* qp = dQ + ((size_t)bh * Nq + row) * D;
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wrow0 + 32 * qb + l32;
+    if (row < Nq) {
+      uint16_t* qp = dQ + ((size_t)bh * Nq + row) * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = (uint32_t)to_bits<T>(acc[t][4 * g + 0] * scale) |
-               ((uint32_t)to_bits<T>(acc[t][4 * g + 1] * scale) << 16);
-        w[1] = (uint32_t)to_bits<T>(acc[t][4 * g + 2] * scale) |
-               ((uint32_t)to_bits<T>(acc[t][4 * g + 3] * scale) << 16);
-        *(u32x2*)(qp + 32 * t + 8 * g + 4 * hi) = w;
-      }
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w;
+          w[0] = (uint32_t)to_bits<T>(acc[qb][t][4 * g + 0] * scale) |
+                 ((uint32_t)to_bits<T>(acc[qb][t][4 * g + 1] * scale) << 16);
+          w[1] = (uint32_t)to_bits<T>(acc[qb][t][4 * g + 2] * scale) |
+                 ((uint32_t)to_bits<T>(acc[qb][t][4 * g + 3] * scale) << 16);
+          *(u32x2*)(qp + 32 * t + 8 * g + 4 * hi) = w;
+        }
+    }
   }
 }
 
@@ -1150,6 +1185,23 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a) {
 #define OSATTN_DKDV_NBUF 4
 #endif
 
+#ifndef OSATTN_DQ64_QB
+#define OSATTN_DQ64_QB 2
+#endif
+
+template <typename T, int D, int NB, int QB, bool CAUSAL, bool IMASK>
+static hipError_t launch_dq_t(const BwdArgs& a, float sl2, int Nk) {
+  using C = DqCfg<D, NB, QB>;
+  const int n_qt = (a.N + C::kRows - 1) / C::kRows;
+  const long long blocks = (long long)n_qt * a.B * a.H;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, NB, QB, CAUSAL, IMASK>), dim3((unsigned)blocks),
+                     dim3(512), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse2,
+                     a.dvec, (uint16_t*)a.dq, a.H, a.Hkv, a.N, n_qt, a.scale, sl2,
+                     a.kv_lo, a.kv_hi, Nk);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool CAUSAL, bool IMASK>
 static hipError_t bwd_t(const BwdArgs& a) {
   constexpr int NB = OSATTN_BWD_NBUF;
@@ -1175,14 +1227,16 @@ static hipError_t bwd_t(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   if (a.stages & kStageDq) {
-    using C = DqCfg<D, NB>;
-    const int n_qt = (a.N + C::kRows - 1) / C::kRows;
-    const long long blocks = (long long)n_qt * a.B * a.H;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, NB, CAUSAL, IMASK>), dim3((unsigned)blocks),
-                       dim3(512), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO, a.lse2,
-                       a.dvec, (uint16_t*)a.dq, a.H, a.Hkv, a.N, n_qt, a.scale, sl2,
-                       a.kv_lo, a.kv_hi, Nk);
+    // d = 64 (not causal, no interval masks): two 32-row blocks per wave (512-row
+    // workgroups), so that every K and V operand read from LDS feeds two MFMAs, unless
+    // that grid would leave CUs without a workgroup.  (Under the causal mask the longer
+    // staircase of 512-row tiles costs more than the reuse gains: 0.88 -> 0.99 ms on
+    // fp16 B2 H32 N8192.)
+    constexpr int QB2 = (D == 64 && !CAUSAL && !IMASK) ? OSATTN_DQ64_QB : 1;
+    const long long wide = (long long)((a.N + DqCfg<D, NB, QB2>::kRows - 1) / DqCfg<D, NB, QB2>::kRows) *
+                           a.B * a.H;
+    if (QB2 > 1 && wide >= device_cus()) return launch_dq_t<T, D, NB, QB2, CAUSAL, IMASK>(a, sl2, Nk);
+    return launch_dq_t<T, D, NB, 1, CAUSAL, IMASK>(a, sl2, Nk);
   }
   return hipGetLastError();
 }
