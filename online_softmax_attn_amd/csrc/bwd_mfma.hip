@@ -267,10 +267,10 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
 
     // K and V rows of this wave (B operands of S = Q K^T and dP = dO V^T).
     vec8 kf[KB][D / 16], vf[KB][D / 16];
-  #pragma unroll
+#pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const uint32_t rowoff = (uint32_t)(kw + 32 * kb + l32) * C::kRowBytes;
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         kf[kb][c] = as_vec8<T>(buffer_load16(rk, rowoff + (16 * c + 8 * hi) * 2));
         vf[kb][c] = as_vec8<T>(buffer_load16(rv, rowoff + (16 * c + 8 * hi) * 2));
@@ -278,11 +278,11 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
     }
 
     f32x16 dk_acc[KB][D / 32], dv_acc[KB][D / 32];
-  #pragma unroll
+#pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < D / 32; ++t)
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 16; ++r) {
           dk_acc[kb][t][r] = 0.f;
           dv_acc[kb][t][r] = 0.f;
@@ -304,7 +304,7 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
           l = max(l, t);
         }
       }
-  #pragma unroll
+#pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         f = min(f, __shfl_xor(f, off));
         l = max(l, __shfl_xor(l, off));
@@ -319,7 +319,7 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
     // LDS-DMA offsets: chunk ch of a tile holds tile row off / kRowBytes, physical
     // granule pg, i.e. logical granule pg ^ swizzle(row).
     uint32_t goff[C::kCPW];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < C::kCPW; ++i) {
       const int off = (wave * C::kCPW + i) * 1024 + lane * 16;
       const int row = off / C::kRowBytes;
@@ -334,7 +334,7 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
       const size_t bh = (size_t)b * H + kvh * n_rep + r;
       const auto rq = make_rsrc(Q + bh * Nq * D, q_bytes);
       const auto rd = make_rsrc(dO + bh * Nq * D, q_bytes);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < C::kCPW; ++i) {
         const int ch = wave * C::kCPW + i;
         buffer_load16_lds(rq, lq + ch * 512, goff[i], i0 * C::kRowBytes);
@@ -366,7 +366,7 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
     // LDS read offsets (bytes in a tile), loop-invariant per lane.
     //  row-wise (A operand of S and dP): row 32qb + l32, logical granule 2c + hi
     uint32_t roff[D / 16];
-  #pragma unroll
+#pragma unroll
     for (int c = 0; c < D / 16; ++c) roff[c] = l32 * C::kRowBytes + (((2 * c + hi) ^ bwd_swz<D>(l32)) * 16);
     //  transposed (A operands of dV^T and dK^T): rows 16cq + tr_row (+8), columns
     //  32t + tr_col .. +3 (see common.h for the lane pattern of the transpose read)
@@ -375,7 +375,7 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
     //  The upper half (rows +8) has swizzle bwd_swz(row) ^ 2: granule bit 1, i.e. byte
     //  bit 5 of the in-row offset, flips.
     uint32_t toff[D / 32], toff8[D / 32];
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t < D / 32; ++t) {
       const int col = 32 * t + tr_col;
       toff[t] = tr_row * C::kRowBytes + (((col >> 3) ^ bwd_swz<D>(tr_row)) * 16) + (col & 7) * 2;
@@ -398,18 +398,18 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
     auto compute_tile_fenced = [&](auto mask_c, int i0, const char* qb_, const char* db_, const float* ll,
                             const float* lD, const int* lm) __attribute__((always_inline)) {
       constexpr int MM = decltype(mask_c)::value;  // 0 none, 1 causal, 2 intervals
-  #pragma unroll
+#pragma unroll
       for (int qb = 0; qb < C::kQT / 32; ++qb) {
         // -- operand requests for S and dP
         u32x4 aq[D / 16], ad[D / 16];
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < D / 16; ++c) {
           aq[c] = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
           ad[c] = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
         }
         f32x4 lse4[4], d4[4];  // rows 32qb + 8g + 4hi + 0..3 for register group g
         i32x4 lo4[4], hi4[4];
-  #pragma unroll
+#pragma unroll
         for (int g = 0; g < 4; ++g) {
           lse4[g] = *(const f32x4*)&ll[32 * qb + 8 * g + 4 * hi];
           d4[g] = *(const f32x4*)&lD[32 * qb + 8 * g + 4 * hi];
@@ -421,26 +421,26 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
         __builtin_amdgcn_sched_barrier(0);
         // -- S = Q K^T, dP = dO V^T (lane = key, register r = query row 8(r/4)+4hi+r%4)
         f32x16 s[KB], dp[KB];
-  #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 16; ++r) {
             s[kb][r] = 0.f;
             dp[kb][r] = 0.f;
           }
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < D / 16; ++c)
-  #pragma unroll
+#pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
             s[kb] = M::mma32(as_vec8<T>(aq[c]), kf[kb][c], s[kb]);
             dp[kb] = M::mma32(as_vec8<T>(ad[c]), vf[kb][c], dp[kb]);
           }
         // -- operand requests for dV^T and dK^T (transposed reads of the same tiles)
         vec8 adt[2][D / 32], aqt[2][D / 32];
-  #pragma unroll
+#pragma unroll
         for (int cq = 0; cq < 2; ++cq) {
           const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < D / 32; ++t) {
             adt[cq][t] = join8<T>(lds_read_tr4(db_ + rowb + toff[t]), lds_read_tr4(db_ + rowb + toff8[t]));
             aqt[cq][t] = join8<T>(lds_read_tr4(qb_ + rowb + toff[t]), lds_read_tr4(qb_ + rowb + toff8[t]));
@@ -449,17 +449,17 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
         __builtin_amdgcn_sched_barrier(0);
         // -- P = exp2(S*c - LSE*log2e) (0 where masked), dS = P * (dP - D)
         vec8 pp[2][KB], ps[2][KB];
-  #pragma unroll
+#pragma unroll
         for (int cq = 0; cq < 2; ++cq)
-  #pragma unroll
+#pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
             const int key = kw + 32 * kb + l32;
             float p8[8], d8[8];
-  #pragma unroll
+#pragma unroll
             for (int g2 = 0; g2 < 2; ++g2) {
               const int g = 2 * cq + g2;
               const int ql = 32 * qb + 8 * g + 4 * hi;
-  #pragma unroll
+#pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g + e;
                 float pv = fast_exp2(fmaf(s[kb][r], scale_log2, -lse4[g][e]));
@@ -476,11 +476,11 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
             ps[cq][kb] = pack8<T>(d8);
           }
         // -- dV^T += dO^T P ; dK^T += Q^T dS  (reduction over the 32 query rows)
-  #pragma unroll
+#pragma unroll
         for (int cq = 0; cq < 2; ++cq)
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < D / 32; ++t)
-  #pragma unroll
+#pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
               dv_acc[kb][t] = M::mma32(adt[cq][t], pp[cq][kb], dv_acc[kb][t]);
               dk_acc[kb][t] = M::mma32(aqt[cq][t], ps[cq][kb], dk_acc[kb][t]);
@@ -493,38 +493,38 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
       constexpr int NQB = C::kQT / 32;
       // S = Q K^T, dP = dO V^T (lane = key, register r = query row 8(r/4)+4hi+r%4)
       f32x16 s[NQB][KB], dp[NQB][KB];
-  #pragma unroll
+#pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
-  #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 16; ++r) {
             s[qb][kb][r] = 0.f;
             dp[qb][kb][r] = 0.f;
           }
-  #pragma unroll
+#pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < D / 16; ++c) {
           const u32x4 aq = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
           const u32x4 ad = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
-  #pragma unroll
+#pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
             s[qb][kb] = M::mma32(as_vec8<T>(aq), kf[kb][c], s[qb][kb]);
             dp[qb][kb] = M::mma32(as_vec8<T>(ad), vf[kb][c], dp[qb][kb]);
           }
         }
-  #pragma unroll
+#pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         // P = exp2(S*c - LSE*log2e) (0 where masked), dS = P * (dP - D)
-  #pragma unroll
+#pragma unroll
         for (int cq = 0; cq < 2; ++cq) {
           vec8 pp[KB], ps[KB];
-  #pragma unroll
+#pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
             const int key = kw + 32 * kb + l32;
             float p8[8], d8[8];
-  #pragma unroll
+#pragma unroll
             for (int g2 = 0; g2 < 2; ++g2) {
               const int ql = 32 * qb + 16 * cq + 8 * g2 + 4 * hi;  // local row of register 8cq+4g2
               const f32x4 lse4 = *(const f32x4*)&ll[ql];
@@ -534,7 +534,7 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
                 lo4 = *(const i32x4*)&lm[ql];
                 hi4 = *(const i32x4*)&lm[C::kQT + ql];
               }
-  #pragma unroll
+#pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = 8 * cq + 4 * g2 + e;
                 float pv = fast_exp2(fmaf(s[qb][kb][r], scale_log2, -lse4[e]));
@@ -552,11 +552,11 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
           }
           // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over these 16 query rows)
           const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < D / 32; ++t) {
             const vec8 adt = join8<T>(lds_read_tr4(db_ + rowb + toff[t]), lds_read_tr4(db_ + rowb + toff8[t]));
             const vec8 aqt = join8<T>(lds_read_tr4(qb_ + rowb + toff[t]), lds_read_tr4(qb_ + rowb + toff8[t]));
-  #pragma unroll
+#pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
               dv_acc[kb][t] = M::mma32(adt, pp[kb], dv_acc[kb][t]);
               dk_acc[kb][t] = M::mma32(aqt, ps[kb], dk_acc[kb][t]);
@@ -581,12 +581,12 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
     };
     auto read_rows = [&](RowOps& o, int qb, const char* qb_, const char* db_, const float* ll,
                          const float* lD) __attribute__((always_inline)) {
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         o.aq[c] = *(const u32x4*)(qb_ + 32 * qb * C::kRowBytes + roff[c]);
         o.ad[c] = *(const u32x4*)(db_ + 32 * qb * C::kRowBytes + roff[c]);
       }
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < 4; ++g) {
         o.lse4[g] = *(const f32x4*)&ll[32 * qb + 8 * g + 4 * hi];
         o.d4[g] = *(const f32x4*)&lD[32 * qb + 8 * g + 4 * hi];
@@ -594,10 +594,10 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
     };
     auto read_tr = [&](TrOps& o, int qb, const char* qb_, const char* db_)
         __attribute__((always_inline)) {
-  #pragma unroll
+#pragma unroll
       for (int cq = 0; cq < 2; ++cq) {
         const int rowb = (32 * qb + 16 * cq) * C::kRowBytes;
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < D / 32; ++t) {
           o.adt[cq][t] = join8<T>(lds_read_tr4(db_ + rowb + toff[t]), lds_read_tr4(db_ + rowb + toff8[t]));
           o.aqt[cq][t] = join8<T>(lds_read_tr4(qb_ + rowb + toff[t]), lds_read_tr4(qb_ + rowb + toff8[t]));
@@ -605,12 +605,12 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
       }
     };
     auto g1 = [&](const RowOps& o, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
-  #pragma unroll
+#pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[r] = 0.f;
         dp[r] = 0.f;
       }
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         s = M::mma32(as_vec8<T>(o.aq[c]), kf[0][c], s);
         dp = M::mma32(as_vec8<T>(o.ad[c]), vf[0][c], dp);
@@ -620,10 +620,10 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
                    vec8 (&pp)[2], vec8 (&ps)[2], const int* lm) __attribute__((always_inline)) {
       constexpr int MM = decltype(mask_c)::value;  // 0 none, 1 causal, 2 intervals
       const int key = kw + l32;
-  #pragma unroll
+#pragma unroll
       for (int cq = 0; cq < 2; ++cq) {
         float p8[8], d8[8];
-  #pragma unroll
+#pragma unroll
         for (int g2 = 0; g2 < 2; ++g2) {
           const int g = 2 * cq + g2;
           const int ql = 32 * qb + 8 * g + 4 * hi;
@@ -632,7 +632,7 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
             lo4 = *(const i32x4*)&lm[ql];
             hi4 = *(const i32x4*)&lm[C::kQT + ql];
           }
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
             float pv = fast_exp2(fmaf(s[r], scale_log2, -o.lse4[g][e]));
@@ -651,9 +651,9 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
     };
     auto g2 = [&](const TrOps& o, const vec8 (&pp)[2], const vec8 (&ps)[2])
         __attribute__((always_inline)) {
-  #pragma unroll
+#pragma unroll
       for (int cq = 0; cq < 2; ++cq)
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < D / 32; ++t) {
           dv_acc[0][t] = M::mma32(o.adt[cq][t], pp[cq], dv_acc[0][t]);
           dk_acc[0][t] = M::mma32(o.aqt[cq][t], ps[cq], dk_acc[0][t]);
@@ -666,7 +666,7 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
       constexpr int kVALU = 0x2 | 0x400;  // VALU including transcendental
       __builtin_amdgcn_sched_group_barrier(0x100, decltype(n_ds_c)::value, 0);
       __builtin_amdgcn_sched_group_barrier(kVALU, decltype(n_v0_c)::value, 0);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, decltype(ds_per_c)::value, 0);
@@ -799,15 +799,15 @@ void bwd_dkdv_kernel(const DkdvKernelArgs args) {
     }
 
     // Store: lane = key, register r of tile t = column 32t + 8(r/4) + 4hi + r%4.
-  #pragma unroll
+#pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int key = kw + 32 * kb + l32;
       if (key < Nk) {
         uint16_t* dkp = dK + ((size_t)bg * Nk + key) * D;
         uint16_t* dvp = dV + ((size_t)bg * Nk + key) * D;
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < D / 32; ++t)
-  #pragma unroll
+#pragma unroll
           for (int g = 0; g < 4; ++g) {
             u32x2 wk, wv;
             wk[0] = (uint32_t)to_bits<T>(dk_acc[kb][t][4 * g + 0] * scale) |

@@ -155,10 +155,10 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
     // Query fragments (B operand of S^T = K Q^T): lane holds row l32 of each block,
     // columns 16c + 8*hi .. +7 for every 16-column chunk c.  Rows >= N read zero.
     vec8 qf[QB][D / 16];
-  #pragma unroll
+#pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const uint32_t rowoff = (uint32_t)(wrow0 + 32 * qb + l32) * C::kRowBytes;
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < D / 16; ++c) qf[qb][c] = as_vec8<T>(buffer_load16(rq, rowoff + (16 * c + 8 * hi) * 2));
     }
 
@@ -178,7 +178,7 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
       w_hi = -1;
       w_maxlo = 0;
       w_minhi = Nk - 1;
-  #pragma unroll
+#pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int row = wrow0 + 32 * qb + l32;
         int lo = Nk, hi = -1;
@@ -197,7 +197,7 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
         w_maxlo = max(w_maxlo, lo);
         w_minhi = min(w_minhi, hi);
       }
-  #pragma unroll
+#pragma unroll
       for (int off = 1; off < 32; off <<= 1) {  // over the 32 rows (both lane halves agree)
         w_lo = min(w_lo, __shfl_xor(w_lo, off));
         w_hi = max(w_hi, __shfl_xor(w_hi, off));
@@ -210,7 +210,7 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
       }
       __syncthreads();
       int g_lo = Nk, g_hi = -1;
-  #pragma unroll
+#pragma unroll
       for (int w = 0; w < NW; ++w) {
         g_lo = min(g_lo, wg_bounds[2 * w]);
         g_hi = max(g_hi, wg_bounds[2 * w + 1]);
@@ -223,7 +223,7 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
     // covers LDS bytes [ch*1024, +1024) of the tile, i.e. tile row off / kRowBytes,
     // physical granule pg; the data there is logical granule pg ^ swizzle(row).
     uint32_t goff_k[C::kCPW], goff_v[C::kCPW];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < C::kCPW; ++i) {
       const int off = (wave * C::kCPW + i) * 1024 + lane * 16;
       const int row = off / C::kRowBytes;
@@ -233,7 +233,7 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
     }
     auto issue = [&](int kt, uint16_t* lk, uint16_t* lv) __attribute__((always_inline)) {
       const uint32_t base = (uint32_t)(kt0 + kt) * C::kBC * C::kRowBytes;
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < C::kCPW; ++i) {
         const int ch = wave * C::kCPW + i;
         // Tile base in the scalar offset, loop-invariant lane offsets: no vector
@@ -246,7 +246,7 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
     // LDS read offsets (bytes within a tile), loop-invariant per lane.
     //  K (A operand of S^T): row kb*32 + l32, logical granule 2c + hi.
     uint32_t koff[D / 16];
-  #pragma unroll
+#pragma unroll
     for (int c = 0; c < D / 16; ++c) koff[c] = l32 * C::kRowBytes + (((2 * c + hi) ^ Swz::k(l32)) * 16);
     //  V (transposed reads, see common.h): group g = lane / 16 and index i = lane % 16
     //  read row 4*hi + i/4 (+8 for the upper half) of a 16-key chunk and columns
@@ -254,23 +254,23 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
     const int tr_row = 4 * hi + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     uint32_t voff[D / 32];
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t < D / 32; ++t) {
       const int col = 32 * t + tr_col;
       voff[t] = tr_row * C::kRowBytes + (((col >> 3) ^ Swz::v(tr_row)) * 16) + (col & 7) * 2;
     }
 
     f32x16 acc[QB][D / 32];
-  #pragma unroll
+#pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < D / 32; ++t)
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 16; ++r) acc[qb][t][r] = 0.f;
     // Running statistics per query row, in log2 units of the scaled scores.  The
     // finite sentinel keeps exp2(m_old - m_new) free of inf - inf.
     float m_run[QB], l_run[QB];
-  #pragma unroll
+#pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       m_run[qb] = -1e30f;
       l_run[qb] = 0.f;
@@ -285,18 +285,18 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
       // ---- step 1: S^T = K_j Q_i^T -------------------------------------------------
       constexpr int KB = BC / 32;  // 32-key blocks per tile
       f32x16 s[QB][KB];
-  #pragma unroll
+#pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-  #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-  #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const u32x4 a = *(const u32x4*)(kbase + kb * 32 * C::kRowBytes + koff[c]);
-  #pragma unroll
+#pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[qb][kb] = M::mma32(as_vec8<T>(a), qf[qb][c], s[qb][kb]);
         }
       }
@@ -304,7 +304,7 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
          // scheduler issues two and waits for them before every pair of MFMAs).
         constexpr int nR = D / 16 * KB, AH = 8;
         __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < nR - AH; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x8, QB, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -319,14 +319,14 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
         // each test compares that constant with a limit taken once per tile.
         const int base = k0 + 4 * hi;
         const int lim_n = Nk - base;
-  #pragma unroll
+#pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const int lim_c = wrow0 + 32 * qb + l32 - base;
           const int lim_lo = MASK ? lo_r[qb] - base : 0;
           const int lim_hi = MASK ? min(hi_r[qb] - base, lim_n - 1) : lim_n - 1;
-  #pragma unroll
+#pragma unroll
           for (int kb = 0; kb < KB; ++kb)
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int ko = kb * 32 + 8 * (r >> 2) + (r & 3);
               if ((CAUSAL && ko > lim_c) || (MASK && ko < lim_lo) || ko > lim_hi)
@@ -343,14 +343,14 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
       vec8 pf[QB][2 * KB];
       float part[QB];
       auto probs = [&]() __attribute__((always_inline)) {
-  #pragma unroll
+#pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const float neg_m = -m_run[qb];
           part[qb] = 0.f;
-  #pragma unroll
+#pragma unroll
           for (int c4 = 0; c4 < 2 * KB; ++c4) {
             float pv[8];
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(s[qb][c4 >> 1][8 * (c4 & 1) + j], scale_log2, neg_m));
             pf[qb][c4] = pack8<T>(pv);
             part[qb] = sum8<T>(pf[qb][c4], part[qb]);
@@ -358,50 +358,50 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
         }
       };
       auto move_reference = [&]() __attribute__((always_inline)) {
-  #pragma unroll
+#pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
-  #pragma unroll
+#pragma unroll
           for (int kb = 0; kb < KB; ++kb)
-  #pragma unroll
+#pragma unroll
             for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
           const float mn = fmaxf(m_run[qb], wave_xor32_max(mx) * scale_log2);
           const float alpha = fast_exp2(m_run[qb] - mn);
           m_run[qb] = mn;
           l_run[qb] *= alpha;
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < D / 32; ++t)
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r) acc[qb][t][r] *= alpha;
         }
       };
       if (!MASK && kt == 0) move_reference();  // masked rows may start later: left to the range check
       probs();
       bool unsafe = false;
-  #pragma unroll
+#pragma unroll
       // 2^30 per tile keeps l below 2^44 for any N <= 2^24, far from fp32 overflow.
       for (int qb = 0; qb < QB; ++qb) unsafe |= !(part[qb] <= 1073741824.0f);  // also catches NaN
       if (__any(unsafe)) {
         move_reference();
         probs();
       }
-  #pragma unroll
+#pragma unroll
       for (int qb = 0; qb < QB; ++qb) l_run[qb] += part[qb];
       // ---- step 5: O^T += V_j^T P^T ---------------------------------------------------
-  #pragma unroll
+#pragma unroll
       for (int c4 = 0; c4 < 2 * KB; ++c4) {
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < D / 32; ++t) {
           const char* vb = vbase + 16 * c4 * C::kRowBytes + voff[t];
           const vec8 a = join8<T>(lds_read_tr4(vb), lds_read_tr4(vb + 8 * C::kRowBytes));
-  #pragma unroll
+#pragma unroll
           for (int qb = 0; qb < QB; ++qb) acc[qb][t] = M::mma32(a, pf[qb][c4], acc[qb][t]);
         }
       }
       {  // the same for the transposed V reads: 4 MFMA operands (8 reads) ahead
         constexpr int nA = 2 * KB * (D / 32), AH = 4;
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < nA - AH; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x8, QB, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -458,7 +458,7 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
     }
 
     // ---- final normalisation: O = Ot / l, LSE = ln(2) * (m + log2 l) ---------------
-  #pragma unroll
+#pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int row = wrow0 + 32 * qb + l32;
       const float l = wave_xor32_sum(l_run[qb]);
@@ -466,9 +466,9 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
       const float inv = empty ? 0.f : 1.0f / l;
       if (row < Nq) {
         uint16_t* op = O + ((size_t)bh * Nq + row) * D;
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < D / 32; ++t)
-  #pragma unroll
+#pragma unroll
           for (int g = 0; g < 4; ++g) {
             u32x2 w;
             w[0] = (uint32_t)to_bits<T>(acc[qb][t][4 * g + 0] * inv) |
