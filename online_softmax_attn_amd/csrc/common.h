@@ -230,18 +230,19 @@ struct StaticSchedule {
   int w;      // this workgroup's place among them
   int round;  // rounds taken so far
 
-  __device__ StaticSchedule(int total, int bid, int grid) {
+  __host__ __device__ StaticSchedule(int total, int bid, int grid) {
     const int k = grid < 8 ? grid : 8;  // blocks (one per XCD)
     const int per = (total + k - 1) / k;
     const int x = bid % k;
     base = x * per;
-    count = max(0, min(per, total - base));
+    count = total - base < per ? total - base : per;
+    if (count < 0) count = 0;
     nw = (grid - x + k - 1) / k;
     w = bid / k;
     round = 0;
   }
   // Next logical tile of this workgroup, or -1 when it has none left.
-  __device__ int next() {
+  __host__ __device__ int next() {
     const int j = round * nw + ((round & 1) ? nw - 1 - w : w);
     ++round;
     return j < count ? base + j : -1;
