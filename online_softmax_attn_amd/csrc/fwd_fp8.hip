@@ -126,13 +126,29 @@ __device__ __forceinline__ i32x8 lds_read32(const char* p0, const char* p1) {
   return r;
 }
 
+// Kernel arguments.
+struct Fp8KernelArgs {
+  const uint8_t* Q;
+  const uint8_t* K;
+  const uint8_t* Vt;
+  uint16_t* O;
+  float* LSE;
+  int H, Hkv, N, Np, n_qtiles;
+  float c_log2, dv;
+  int n_jobs;  // logical tiles (query tiles x heads)
+};
+
+// Persistent grid (StaticSchedule in common.h) for the causal fp8 forward, whose query
+// tiles differ in length.
+#ifndef OSATTN_FP8_PERSIST
+#define OSATTN_FP8_PERSIST 1
+#endif
+
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64)))
 __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
-                    const uint8_t* __restrict__ Vt, uint16_t* __restrict__ O,
-                    float* __restrict__ LSE, int H, int Hkv, int N, int Np, int n_qtiles,
-                    float c_log2, float dv) {
+void fwd_fp8_kernel(const Fp8KernelArgs args) {
+  constexpr bool PERSIST = OSATTN_FP8_PERSIST && CAUSAL;
   using C = Fp8Cfg<D>;
   constexpr int kD = D;
   constexpr int kRowK = C::kRowK;
@@ -149,196 +165,214 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  int qt = L % n_qtiles;
-  const int bh = L / n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
-  const int h = bh % H;
-  const int b = bh / H;
-  const int kvh = h / (H / Hkv);
-  const int q0 = qt * kBR;
-  const int wrow0 = q0 + wave * 32;
-  const size_t g = (size_t)b * Hkv + kvh;
+  // Logical tile L: query tile L % n_qtiles of head L / n_qtiles.  A persistent grid
+  // (causal) walks its schedule, longest first within each head as below; otherwise
+  // each workgroup runs one tile.
+  StaticSchedule sched(args.n_jobs, blockIdx.x, gridDim.x);
+  int L = PERSIST ? sched.next() : xcd_remap(blockIdx.x, gridDim.x);
+  while (L >= 0) {
+    // Arguments read afresh for each tile of a persistent grid (see fresh_kernel_args).
+    const Fp8KernelArgs a = PERSIST ? fresh_kernel_args<Fp8KernelArgs>() : args;
+    const uint8_t* __restrict__ Q = a.Q;
+    const uint8_t* __restrict__ K = a.K;
+    const uint8_t* __restrict__ Vt = a.Vt;
+    uint16_t* __restrict__ O = a.O;
+    float* __restrict__ LSE = a.LSE;
+    const int H = a.H, Hkv = a.Hkv, N = a.N, Np = a.Np, n_qtiles = a.n_qtiles;
+    const float c_log2 = a.c_log2, dv = a.dv;
+    int qt = L % n_qtiles;
+    const int bh = L / n_qtiles;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
+    const int h = bh % H;
+    const int b = bh / H;
+    const int kvh = h / (H / Hkv);
+    const int q0 = qt * kBR;
+    const int wrow0 = q0 + wave * 32;
+    const size_t g = (size_t)b * Hkv + kvh;
 
-  const auto rq = make_rsrc(Q + (size_t)bh * N * kD, (uint32_t)N * kD);
-  const auto rk = make_rsrc(K + g * N * kD, (uint32_t)N * kD);
-  const auto rv = make_rsrc(Vt + g * kD * Np, (uint32_t)kD * Np);
+    const auto rq = make_rsrc(Q + (size_t)bh * N * kD, (uint32_t)N * kD);
+    const auto rk = make_rsrc(K + g * N * kD, (uint32_t)N * kD);
+    const auto rv = make_rsrc(Vt + g * kD * Np, (uint32_t)kD * Np);
 
-  // Q fragments (B operand of S^T = K Q^T): row l32, dims 64c + 32hi .. +31.
-  i32x8 qf[kNC];
+    // Q fragments (B operand of S^T = K Q^T): row l32, dims 64c + 32hi .. +31.
+    i32x8 qf[kNC];
 #pragma unroll
-  for (int c = 0; c < kNC; ++c) {
-    const uint32_t off = (uint32_t)(wrow0 + l32) * kD + 64 * c + 32 * hi;
-    const u32x4 a = buffer_load16(rq, off), bb = buffer_load16(rq, off + 16);
+    for (int c = 0; c < kNC; ++c) {
+      const uint32_t off = (uint32_t)(wrow0 + l32) * kD + 64 * c + 32 * hi;
+      const u32x4 a = buffer_load16(rq, off), bb = buffer_load16(rq, off + 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qf[c][i] = (int)a[i];
-      qf[c][4 + i] = (int)bb[i];
+      for (int i = 0; i < 4; ++i) {
+        qf[c][i] = (int)a[i];
+        qf[c][4 + i] = (int)bb[i];
+      }
     }
-  }
 
-  int n_kt = (N + kBC - 1) / kBC;
-  if (CAUSAL) n_kt = min(n_kt, (q0 + kBR + kBC - 1) / kBC);
+    int n_kt = (N + kBC - 1) / kBC;
+    if (CAUSAL) n_kt = min(n_kt, (q0 + kBR + kBC - 1) / kBC);
 
-  // LDS-DMA: chunk ch of a tile is LDS bytes [ch * 1024, +1024); the lane's 16 bytes
-  // are physical granule pg of its row, logical pg ^ swz(row).
-  uint32_t goff_k[kCPW], goff_v[kCPW];
-#pragma unroll
-  for (int i = 0; i < kCPW; ++i) {
-    const int off = (wave * kCPW + i) * 1024 + lane * 16;
-    const int rk_ = off / kRowK;  // key row of the K tile
-    goff_k[i] = rk_ * kRowK + (((off % kRowK) / 16) ^ swz<kRowK>(rk_)) * 16;  // + k0 * D (scalar)
-    const int rv_ = off / kRowV;  // dim row of the V^T tile
-    goff_v[i] = rv_ * Np + (((off % kRowV) / 16) ^ swz<kRowV>(rv_)) * 16;     // + k0 (scalar)
-  }
-  auto issue = [&](int kt, uint8_t* lk, uint8_t* lv) __attribute__((always_inline)) {
-    const uint32_t k0 = (uint32_t)kt * kBC;
+    // LDS-DMA: chunk ch of a tile is LDS bytes [ch * 1024, +1024); the lane's 16 bytes
+    // are physical granule pg of its row, logical pg ^ swz(row).
+    uint32_t goff_k[kCPW], goff_v[kCPW];
 #pragma unroll
     for (int i = 0; i < kCPW; ++i) {
-      const int ch = wave * kCPW + i;
-      buffer_load16_lds(rk, lk + ch * 1024, goff_k[i], k0 * kRowK);
-      buffer_load16_lds(rv, lv + ch * 1024, goff_v[i], k0);
+      const int off = (wave * kCPW + i) * 1024 + lane * 16;
+      const int rk_ = off / kRowK;  // key row of the K tile
+      goff_k[i] = rk_ * kRowK + (((off % kRowK) / 16) ^ swz<kRowK>(rk_)) * 16;  // + k0 * D (scalar)
+      const int rv_ = off / kRowV;  // dim row of the V^T tile
+      goff_v[i] = rv_ * Np + (((off % kRowV) / 16) ^ swz<kRowV>(rv_)) * 16;     // + k0 (scalar)
     }
-  };
-
-  // LDS read offsets: row l32 of a 32-row block, logical granules 4c + 2hi, +1 (K:
-  // dims 64c + 32hi .. +31; V^T: keys 64m + 32hi .. +31).
-  uint32_t koff[kNC][2], voff[2][2];
+    auto issue = [&](int kt, uint8_t* lk, uint8_t* lv) __attribute__((always_inline)) {
+      const uint32_t k0 = (uint32_t)kt * kBC;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int c = 0; c < kNC; ++c)
-      koff[c][j] = l32 * kRowK + 16 * ((4 * c + 2 * hi + j) ^ swz<kRowK>(l32));
-#pragma unroll
-    for (int m = 0; m < 2; ++m) voff[m][j] = l32 * kRowV + 16 * ((4 * m + 2 * hi + j) ^ swz<kRowV>(l32));
-  }
-
-  f32x16 acc[kD / 32], lacc;
-#pragma unroll
-  for (int t = 0; t < kD / 32; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
-  float m_run = -1e30f;  // finite: exp2(m_old - m_new) never sees inf - inf
-  i32x8 ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;  // e4m3 1.0 in every byte
-
-  // How far a tile's max may exceed the reference before it moves (log2 units):
-  // 2^0.8 * 256 = 445.7 <= 448.
-  constexpr float kSlack = 0.8f;
-  auto compute = [&](int kt, const char* kbase, const char* vbase) __attribute__((always_inline)) {
-    const int k0 = kt * kBC;
-    if (CAUSAL && k0 > wrow0 + 31) return;  // every key after every row of the wave
-    f32x16 s[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-    for (int c = 0; c < kNC; ++c)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const char* base = kbase + kb * 32 * kRowK;
-        s[kb] = mma8(lds_read32(base + koff[c][0], base + koff[c][1]), qf[c], s[kb]);
+      for (int i = 0; i < kCPW; ++i) {
+        const int ch = wave * kCPW + i;
+        buffer_load16_lds(rk, lk + ch * 1024, goff_k[i], k0 * kRowK);
+        buffer_load16_lds(rv, lv + ch * 1024, goff_v[i], k0);
       }
-    const bool need_mask = (k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > wrow0);
-    if (need_mask) {
-      asm volatile("");  // keep this a branch
-      // Key of element r of block kb: base + ko with ko a compile-time constant.
-      const int base = k0 + 4 * hi;
-      const int lim_n = N - 1 - base, lim_c = wrow0 + l32 - base;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ko = kb * 32 + 8 * (r >> 2) + (r & 3);
-          if (ko > lim_n || (CAUSAL && ko > lim_c)) s[kb][r] = -INFINITY;
-        }
-    }
-    // The tile's row max (log2 units of the scaled scores) against the reference.
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    const float m_tile = wave_xor32_max(mx) * c_log2;
-    if (__any(m_tile > m_run + kSlack)) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = fast_exp2(m_run - m_new);
-#pragma unroll
-      for (int t = 0; t < kD / 32; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
-      m_run = m_new;
-    }
-    // P * 256 in e4m3, bytes in vt_key order: pf[m] covers keys 64m .. 64m+63.
-    const float bias = 8.0f - m_run;  // exp2(s*c - m + 8) = 256 * P
-    i32x8 pf[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const f32x16& sb = s[2 * m + j / 4];
-        const int r0 = 4 * (j % 4);
-        const float p0 = fast_exp2(fmaf(sb[r0 + 0], c_log2, bias));
-        const float p1 = fast_exp2(fmaf(sb[r0 + 1], c_log2, bias));
-        const float p2 = fast_exp2(fmaf(sb[r0 + 2], c_log2, bias));
-        const float p3 = fast_exp2(fmaf(sb[r0 + 3], c_log2, bias));
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
-        pf[m][j] = w;
-      }
-    // O^T += V^T P^T (dims 32t .. 32t+31), and l += sum of the same 8-bit P.
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-#pragma unroll
-      for (int t = 0; t < kD / 32; ++t) {
-        const char* base = vbase + t * 32 * kRowV;
-        acc[t] = mma8(lds_read32(base + voff[m][0], base + voff[m][1]), pf[m], acc[t]);
-      }
-      lacc = mma8(ones, pf[m], lacc);
-    }
-  };
+    };
 
-  if (0 < n_kt) issue(0, lk0, lv0);
-  auto step = [&](auto sc, int kt) __attribute__((always_inline)) {
-    constexpr int S = decltype(sc)::value;
-    uint8_t* lk = S == 0 ? lk0 : lk1;
-    uint8_t* lv = S == 0 ? lv0 : lv1;
-    uint8_t* nk = S == 0 ? lk1 : lk0;
-    uint8_t* nv = S == 0 ? lv1 : lv0;
-    wait_vmcnt<0>();
-    block_barrier();  // tile kt is in LDS; the other stage is free
-    if (kt + 1 < n_kt) issue(kt + 1, nk, nv);
-    compute(kt, (const char*)lk, (const char*)lv);
-  };
-  for (int kt = 0; kt < n_kt; kt += 2) {
-    step(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < n_kt) step(std::integral_constant<int, 1>{}, kt + 1);
-  }
+    // LDS read offsets: row l32 of a 32-row block, logical granules 4c + 2hi, +1 (K:
+    // dims 64c + 32hi .. +31; V^T: keys 64m + 32hi .. +31).
+    uint32_t koff[kNC][2], voff[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int c = 0; c < kNC; ++c)
+        koff[c][j] = l32 * kRowK + 16 * ((4 * c + 2 * hi + j) ^ swz<kRowK>(l32));
+#pragma unroll
+      for (int m = 0; m < 2; ++m) voff[m][j] = l32 * kRowV + 16 * ((4 * m + 2 * hi + j) ^ swz<kRowV>(l32));
+    }
 
-  // O = Ot * dv / l; LSE = ln 2 * (m + log2 l - 8).
-  const int row = wrow0 + l32;
-  const float l = lacc[0];
-  const float inv = dv / l;
-  if (row < N) {
-    uint16_t* op = O + ((size_t)bh * N + row) * kD;
+    f32x16 acc[kD / 32], lacc;
 #pragma unroll
     for (int t = 0; t < kD / 32; ++t)
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        u32x2 w;
-        w[0] = (uint32_t)to_bits<__bf16>(acc[t][4 * gg + 0] * inv) |
-               ((uint32_t)to_bits<__bf16>(acc[t][4 * gg + 1] * inv) << 16);
-        w[1] = (uint32_t)to_bits<__bf16>(acc[t][4 * gg + 2] * inv) |
-               ((uint32_t)to_bits<__bf16>(acc[t][4 * gg + 3] * inv) << 16);
-        *(u32x2*)(op + 32 * t + 8 * gg + 4 * hi) = w;
+      for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
+    float m_run = -1e30f;  // finite: exp2(m_old - m_new) never sees inf - inf
+    i32x8 ones;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;  // e4m3 1.0 in every byte
+
+    // How far a tile's max may exceed the reference before it moves (log2 units):
+    // 2^0.8 * 256 = 445.7 <= 448.
+    constexpr float kSlack = 0.8f;
+    auto compute = [&](int kt, const char* kbase, const char* vbase) __attribute__((always_inline)) {
+      const int k0 = kt * kBC;
+      if (CAUSAL && k0 > wrow0 + 31) return;  // every key after every row of the wave
+      f32x16 s[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < kNC; ++c)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const char* base = kbase + kb * 32 * kRowK;
+          s[kb] = mma8(lds_read32(base + koff[c][0], base + koff[c][1]), qf[c], s[kb]);
+        }
+      const bool need_mask = (k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > wrow0);
+      if (need_mask) {
+        asm volatile("");  // keep this a branch
+        // Key of element r of block kb: base + ko with ko a compile-time constant.
+        const int base = k0 + 4 * hi;
+        const int lim_n = N - 1 - base, lim_c = wrow0 + l32 - base;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ko = kb * 32 + 8 * (r >> 2) + (r & 3);
+            if (ko > lim_n || (CAUSAL && ko > lim_c)) s[kb][r] = -INFINITY;
+          }
       }
-    if (hi == 0) LSE[(size_t)bh * N + row] = (m_run + __log2f(l) - 8.0f) * kLn2;
+      // The tile's row max (log2 units of the scaled scores) against the reference.
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      const float m_tile = wave_xor32_max(mx) * c_log2;
+      if (__any(m_tile > m_run + kSlack)) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+        for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[t][r] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
+        m_run = m_new;
+      }
+      // P * 256 in e4m3, bytes in vt_key order: pf[m] covers keys 64m .. 64m+63.
+      const float bias = 8.0f - m_run;  // exp2(s*c - m + 8) = 256 * P
+      i32x8 pf[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const f32x16& sb = s[2 * m + j / 4];
+          const int r0 = 4 * (j % 4);
+          const float p0 = fast_exp2(fmaf(sb[r0 + 0], c_log2, bias));
+          const float p1 = fast_exp2(fmaf(sb[r0 + 1], c_log2, bias));
+          const float p2 = fast_exp2(fmaf(sb[r0 + 2], c_log2, bias));
+          const float p3 = fast_exp2(fmaf(sb[r0 + 3], c_log2, bias));
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+          pf[m][j] = w;
+        }
+      // O^T += V^T P^T (dims 32t .. 32t+31), and l += sum of the same 8-bit P.
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int t = 0; t < kD / 32; ++t) {
+          const char* base = vbase + t * 32 * kRowV;
+          acc[t] = mma8(lds_read32(base + voff[m][0], base + voff[m][1]), pf[m], acc[t]);
+        }
+        lacc = mma8(ones, pf[m], lacc);
+      }
+    };
+
+    if (0 < n_kt) issue(0, lk0, lv0);
+    auto step = [&](auto sc, int kt) __attribute__((always_inline)) {
+      constexpr int S = decltype(sc)::value;
+      uint8_t* lk = S == 0 ? lk0 : lk1;
+      uint8_t* lv = S == 0 ? lv0 : lv1;
+      uint8_t* nk = S == 0 ? lk1 : lk0;
+      uint8_t* nv = S == 0 ? lv1 : lv0;
+      wait_vmcnt<0>();
+      block_barrier();  // tile kt is in LDS; the other stage is free
+      if (kt + 1 < n_kt) issue(kt + 1, nk, nv);
+      compute(kt, (const char*)lk, (const char*)lv);
+    };
+    for (int kt = 0; kt < n_kt; kt += 2) {
+      step(std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < n_kt) step(std::integral_constant<int, 1>{}, kt + 1);
+    }
+
+    // O = Ot * dv / l; LSE = ln 2 * (m + log2 l - 8).
+    const int row = wrow0 + l32;
+    const float l = lacc[0];
+    const float inv = dv / l;
+    if (row < N) {
+      uint16_t* op = O + ((size_t)bh * N + row) * kD;
+#pragma unroll
+      for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          u32x2 w;
+          w[0] = (uint32_t)to_bits<__bf16>(acc[t][4 * gg + 0] * inv) |
+                 ((uint32_t)to_bits<__bf16>(acc[t][4 * gg + 1] * inv) << 16);
+          w[1] = (uint32_t)to_bits<__bf16>(acc[t][4 * gg + 2] * inv) |
+                 ((uint32_t)to_bits<__bf16>(acc[t][4 * gg + 3] * inv) << 16);
+          store_global(op + 32 * t + 8 * gg + 4 * hi, w);
+        }
+      if (hi == 0) store_global(LSE + (size_t)bh * N + row, (m_run + __log2f(l) - 8.0f) * kLn2);
+    }
+    if constexpr (!PERSIST) break;
+    __syncthreads();  // every wave is done with the staged tiles
+    L = sched.next();
   }
 }
 
@@ -359,18 +393,23 @@ hipError_t launch_fp8_d(const Fp8Args& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qtiles = (a.N + kBR - 1) / kBR;
-  const long long blocks = (long long)n_qtiles * a.B * a.H;
+  const long long jobs = (long long)n_qtiles * a.B * a.H;
   const float c_log2 = a.scale * a.descale_q * a.descale_k * kLog2e;
-  if (a.causal)
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, true>), dim3((unsigned)blocks), dim3(kNW * 64), 0,
-                       (hipStream_t)a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k,
-                       (const uint8_t*)a.workspace, (uint16_t*)a.o, a.lse, a.H, a.Hkv, a.N, np,
-                       n_qtiles, c_log2, a.descale_v);
-  else
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, false>), dim3((unsigned)blocks), dim3(kNW * 64), 0,
-                       (hipStream_t)a.stream, (const uint8_t*)a.q, (const uint8_t*)a.k,
-                       (const uint8_t*)a.workspace, (uint16_t*)a.o, a.lse, a.H, a.Hkv, a.N, np,
-                       n_qtiles, c_log2, a.descale_v);
+  const Fp8KernelArgs ka{(const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.workspace,
+                         (uint16_t*)a.o, a.lse, a.H, a.Hkv, a.N, np, n_qtiles, c_log2,
+                         a.descale_v, (int)jobs};
+  if (a.causal) {
+    auto kernel = fwd_fp8_kernel<D, true>;
+    long long blocks = jobs;
+    if (OSATTN_FP8_PERSIST) {
+      static const int per_cu = resident_per_cu(kernel, kNW * 64);
+      blocks = persistent_grid(per_cu, jobs);
+    }
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kNW * 64), 0, (hipStream_t)a.stream, ka);
+  } else {
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, false>), dim3((unsigned)jobs), dim3(kNW * 64), 0,
+                       (hipStream_t)a.stream, ka);
+  }
   return hipGetLastError();
 }
 
