@@ -56,8 +56,10 @@ struct FwdCfg {
   static_assert(kCPW >= 1 && kChunks % NW == 0, "tile must split evenly over the waves");
 };
 
-// Persistent grid (StaticSchedule) for the causal forward, whose query tiles differ in
-// length.
+// Persistent grid (StaticSchedule) for every forward without an interval mask: the
+// causal query tiles differ in length, and with equal tiles it still saves the gap
+// between one workgroup's end and the next one's dispatch on each CU (about 1.5% at
+// B4 H16 N8192 d128).
 #ifndef OSATTN_FWD_PERSIST
 #define OSATTN_FWD_PERSIST 1
 #endif
@@ -85,7 +87,7 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
   using M = Mfma<T>;
   using vec8 = typename M::vec8;
   using Swz = FwdSwizzle<D>;
-  constexpr bool PERSIST = OSATTN_FWD_PERSIST && CAUSAL && !MASK;
+  constexpr bool PERSIST = OSATTN_FWD_PERSIST && !MASK;
   // One array per pipeline stage: with the stage known at compile time, the
   // compiler can tell that reads of one stage do not alias the DMA writes still in
   // flight into the others, and inserts no wait for them.
@@ -102,8 +104,8 @@ void fwd_mfma_kernel(const FwdKernelArgs args) {
   const int tid0 = threadIdx.x;
 
   // Logical tile L: query tile L % n_qtiles of head L / n_qtiles.  A persistent grid
-  // (causal) walks its schedule (see StaticSchedule), longest first within each head as
-  // below; otherwise each workgroup runs one tile.
+  // (no interval mask) walks its schedule (see StaticSchedule), longest first within each
+  // head when causal, as below; otherwise each workgroup runs one tile.
   StaticSchedule sched(args.n_jobs, blockIdx.x, gridDim.x);
   int L;
   if constexpr (PERSIST) {
@@ -494,7 +496,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a) {
   const long long jobs = (long long)n_qtiles * a.B * a.H;
   auto kernel = fwd_mfma_kernel<T, D, NW, QB, NBUF, BC, CAUSAL, MASK>;
   long long blocks = jobs;
-  if (OSATTN_FWD_PERSIST && CAUSAL && !MASK) {
+  if (OSATTN_FWD_PERSIST && !MASK) {
     static const int per_cu = resident_per_cu(kernel, NW * 64);
     blocks = persistent_grid(per_cu, jobs);
   }

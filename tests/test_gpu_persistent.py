@@ -1,4 +1,4 @@
-"""Persistent grids (the causal forward and dK/dV kernels).
+"""Persistent grids (the forward without an interval mask, the causal dK/dV kernel).
 
 Their workgroups walk a fixed schedule of tiles (one block of tiles per XCD, taken in
 snake-ordered rounds) instead of one tile each.  These tests check that many launches
@@ -11,14 +11,14 @@ import pytest
 import torch
 
 import synthetic as S
-from gpu_parity import check_full, need_gpu, say, to_dev
+from gpu_parity import check_full, check_sampled_fwd, need_gpu, run_fwd, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
 N_LAUNCHES = 20
 
 
-def _run(inp, scale, stream=None):
+def _run(inp, scale, stream=None, causal=True):
     import online_softmax_attn_amd as osa
     q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
     if stream is None:
@@ -26,8 +26,8 @@ def _run(inp, scale, stream=None):
     else:
         stream.wait_stream(torch.cuda.current_stream())  # the inputs' copies
     with torch.cuda.stream(stream):
-        o, lse = osa.attn_fwd(q, k, v, causal=True, scale=scale)
-        dq, dk, dv = osa.attn_bwd(q, k, v, o, lse, do, causal=True, scale=scale)
+        o, lse = osa.attn_fwd(q, k, v, causal=causal, scale=scale)
+        dq, dk, dv = osa.attn_bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
     return o, lse, dq, dk, dv
 
 
@@ -35,19 +35,31 @@ def _same(a, b):
     return all(torch.equal(x, y) for x, y in zip(a, b))
 
 
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("d", [64, 128])
-def test_causal_many_launches_bitwise(d):
+def test_many_launches_bitwise(d, causal):
     need_gpu()
-    w = S.custom("bf16", 2, 4, 2, 1100, d, True, seed_base=9100 + d)
+    w = S.custom("bf16", 2, 4, 2, 1100, d, causal, seed_base=9100 + d + 7 * causal)
     inp = S.make_inputs(w)
-    check_full(inp, "bf16", True, w.scale, label=w.name)
-    first = _run(inp, w.scale)
+    check_full(inp, "bf16", causal, w.scale, label=w.name)
+    first = _run(inp, w.scale, causal=causal)
     torch.cuda.synchronize()
     for i in range(N_LAUNCHES):
-        again = _run(inp, w.scale)
+        again = _run(inp, w.scale, causal=causal)
         torch.cuda.synchronize()
         assert _same(first, again), f"launch {i} differs"
     say(f"[persistent] {w.name}: {N_LAUNCHES} launches bit-identical")
+
+
+@pytest.mark.parametrize("d,H", [(128, 48), (64, 96)])
+def test_many_tiles_per_workgroup(d, H):
+    """Non-causal forwards with several query tiles per workgroup (672 and 768 tiles) and
+    a ragged last tile per head: sampled rows of every head against the oracle."""
+    need_gpu()
+    w = S.custom("fp16", 2, H, 8, 1700, d, False, seed_base=9400 + d)
+    inp = S.make_inputs(w)
+    o, lse = run_fwd(inp, False, w.scale)
+    check_sampled_fwd(inp, o, lse, "fp16", False, w.scale, per_head=4, label=w.name)
 
 
 def test_causal_two_streams_at_once():
