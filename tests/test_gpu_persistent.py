@@ -62,18 +62,19 @@ def test_many_tiles_per_workgroup(d, H):
     check_sampled_fwd(inp, o, lse, "fp16", False, w.scale, per_head=4, label=w.name)
 
 
-def test_causal_two_streams_at_once():
+@pytest.mark.parametrize("causal", [True, False])
+def test_two_streams_at_once(causal):
     need_gpu()
-    w1 = S.custom("bf16", 1, 8, 8, 2048, 128, True, seed_base=9200)
-    w2 = S.custom("fp16", 2, 4, 1, 1500, 64, True, seed_base=9300)
+    w1 = S.custom("bf16", 1, 8, 8, 2048, 128, causal, seed_base=9200 + 7 * causal)
+    w2 = S.custom("fp16", 2, 4, 1, 1500, 64, causal, seed_base=9300 + 7 * causal)
     in1, in2 = S.make_inputs(w1), S.make_inputs(w2)
-    ref1, ref2 = _run(in1, w1.scale), _run(in2, w2.scale)
+    ref1, ref2 = _run(in1, w1.scale, causal=causal), _run(in2, w2.scale, causal=causal)
     torch.cuda.synchronize()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     for i in range(8):
-        got1 = _run(in1, w1.scale, s1)
-        got2 = _run(in2, w2.scale, s2)
+        got1 = _run(in1, w1.scale, s1, causal=causal)
+        got2 = _run(in2, w2.scale, s2, causal=causal)
         torch.cuda.synchronize()
         assert _same(ref1, got1) and _same(ref2, got2), f"round {i} differs"
-    check_full(in1, "bf16", True, w1.scale, label=w1.name)
-    check_full(in2, "fp16", True, w2.scale, label=w2.name)
+    check_full(in1, "bf16", causal, w1.scale, label=w1.name)
+    check_full(in2, "fp16", causal, w2.scale, label=w2.name)
