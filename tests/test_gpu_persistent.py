@@ -51,12 +51,14 @@ def test_many_launches_bitwise(d, causal):
     say(f"[persistent] {w.name}: {N_LAUNCHES} launches bit-identical")
 
 
-@pytest.mark.parametrize("d,H", [(128, 48), (64, 96)])
-def test_many_tiles_per_workgroup(d, H):
-    """Non-causal forwards with several query tiles per workgroup (672 and 768 tiles) and
-    a ragged last tile per head: sampled rows of every head against the oracle."""
+@pytest.mark.parametrize("d,B,H,Hkv,N", [(128, 2, 48, 8, 1700), (64, 2, 96, 8, 1700),
+                                           (128, 1, 35, 7, 2100), (64, 1, 35, 5, 2100)])
+def test_many_tiles_per_workgroup(d, B, H, Hkv, N):
+    """Non-causal forwards with several query tiles per workgroup and a ragged last tile
+    per head: 672 and 768 tiles, and 315 (256-row tiles at both head dims; 315 is not a
+    multiple of the 8 XCD blocks).  Sampled rows of every head against the oracle."""
     need_gpu()
-    w = S.custom("fp16", 2, H, 8, 1700, d, False, seed_base=9400 + d)
+    w = S.custom("fp16", B, H, Hkv, N, d, False, seed_base=9400 + d + N)
     inp = S.make_inputs(w)
     o, lse = run_fwd(inp, False, w.scale)
     check_sampled_fwd(inp, o, lse, "fp16", False, w.scale, per_head=4, label=w.name)
